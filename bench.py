@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of a quantised-halo GCN layer (forward + backward) on MI355X.
+
+A step is one pass of the whole hot path over the 300k-inner + 150k-halo, d = 128 partition
+(power-law in-degree, mean 25; halo widths 4 bits, 8 bits for the top 10% by degree):
+quantise the send set, fused dequantise + aggregate, project + ReLU, project backward (dA, dW),
+transposed aggregate over the halo columns, quantise the halo gradients, transposed aggregate over
+the inner columns, dequantise + add the received gradients.
+
+Prints one JSON line.  value = algorithmic bytes of the quantise and aggregate calls of a step
+divided by the whole step's wall time (the dense projections are inside the timed step too).
+Per-kernel times come from HIP events recorded on the launch stream inside the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quant+aggregate GB/s (% HBM peak) and G edge·feat/s per layer at d=128"
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+# ------------------------------------------------------------------------------------------------
+# algorithmic bytes (what each call must move with no reuse assumed)
+# ------------------------------------------------------------------------------------------------
+
+def row_words(d, bits):
+    bits = np.asarray(bits, dtype=np.int64)
+    return np.where(bits == 32, d, (d * bits + 31) // 32)
+
+
+def quantize_bytes(n_rows, d, bits, gathered):
+    w = row_words(d, bits)
+    per_row = 4 * d + 1 + 4 + 8 + (4 if gathered else 0)
+    return int(n_rows * per_row + 4 * w.sum())
+
+
+def gather_bytes(rowptr, colidx, n_inner, d, halo_words, beta, rows_weighted=True, cols_weighted=True):
+    """Per-edge gather model: every edge reads its index, its column weight and a whole feature row
+    (inner) or packed code row + metadata (halo); every row reads its bounds and weight, writes d floats
+    (and reads them first when beta = 1)."""
+    n_rows = rowptr.size - 1
+    e = colidx.size
+    halo = colidx >= n_inner
+    n_halo_e = int(halo.sum())
+    edge = e * (4 + (4 if cols_weighted else 0)) + (e - n_halo_e) * 4 * d
+    if n_halo_e:
+        k = colidx[halo] - n_inner
+        edge += int(4 * halo_words[k].sum()) + n_halo_e * (8 + 1 + 4)
+    rows = n_rows * (4 + (4 if rows_weighted else 0) + 4 * d * (2 if beta else 1))
+    return int(edge + rows)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="synthetic partition index (2 = 300k-node d=128)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU runs are not part of "
+              "this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    from quantized_halo_aggregation_amd import synth
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    part = synth.make_partition(wl)
+    gen_s = time.time() - t0
+    print(f"[bench] generated {wl.describe()} in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    gp = GpuPartition(part, chunk=args.chunk or B.DEFAULT_CHUNK)
+    st = LayerStack(gp, part.weights, part.x, part.grad_top)
+    torch.cuda.synchronize()
+    print("[bench] device set-up done", file=sys.stderr, flush=True)
+
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    hw = row_words(d, part.bits)
+    nw = gp.h_colptr
+    # algorithmic bytes per call of one layer
+    b_q_fwd = quantize_bytes(n_h, d, part.bits, gathered=True)
+    b_q_bwd = quantize_bytes(n_h, d, part.bits, gathered=False)
+    sage = wl.model == "sage"
+    b_agg_fwd = gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0, cols_weighted=not sage)
+    b_bwd_halo = gather_bytes(nw[n_in:], gp.h_rowidx[nw[n_in]:], 1 << 62, d, hw, beta=0, rows_weighted=not sage)
+    b_bwd_inner = gather_bytes(nw[:n_in + 1], gp.h_rowidx[:nw[n_in]], 1 << 62, d, hw, beta=1 if sage else 0,
+                               rows_weighted=not sage)
+    m_ptr = np.diff(B.csr_transpose(np.arange(n_h + 1, dtype=np.int32), part.mirror, n_in)[0])
+    n_targets = int((m_ptr > 0).sum())
+    b_add = n_targets * (4 + 8 * d) + n_h * (4 + 8 + 1 + 4) + int(4 * hw.sum())
+    bytes_by_stage = {"quantize_fwd": b_q_fwd, "aggregate_fwd": b_agg_fwd, "aggregate_bwd_halo": b_bwd_halo,
+                      "quantize_bwd": b_q_bwd, "aggregate_bwd_inner": b_bwd_inner, "add_received": b_add}
+    k_in = 2 * d if sage else d
+    flops_by_stage = {"dense_fwd": 2 * n_in * k_in * d, "dense_bwd": 4 * n_in * k_in * d}
+    qa_bytes_step = wl.layers * sum(bytes_by_stage.values())
+    edges_fwd = int(gp.h_idx.size)
+
+    # ---- timing ------------------------------------------------------------------------------
+    stream = torch.cuda.current_stream()
+    stages = ["quantize_fwd", "aggregate_fwd", "dense_fwd", "dense_bwd", "aggregate_bwd_halo", "quantize_bwd",
+              "aggregate_bwd_inner", "add_received"]
+    events = []
+
+    def hook(name, layer):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        events.append((name, ev))
+
+    for w in range(args.warmup):
+        st.step(epoch=w)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.warmup} warm-up steps done", file=sys.stderr, flush=True)
+
+    per_stage = {s: [] for s in stages}
+    records = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        events.clear()
+        first = torch.cuda.Event(enable_timing=True)
+        first.record(stream)
+        st.step(epoch=args.warmup + s, hook=hook)
+        prev = first
+        for name, ev in events:
+            records.append((name, prev, ev))
+            prev = ev
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for name, a, b in records:
+        per_stage[name].append(a.elapsed_time(b))
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms_step = sum(sum(v) for v in per_stage.values()) / args.steps
+    print(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step in "
+          "kernels (events)", file=sys.stderr, flush=True)
+
+    # per-kernel averages (a stage appears once per layer per step)
+    avg_ms = {s: float(np.mean(v)) for s, v in per_stage.items() if v}
+    kernels = {}
+    for s, ms in avg_ms.items():
+        rec = {"avg_ms": round(ms, 5)}
+        if s in bytes_by_stage:
+            gbs = bytes_by_stage[s] / (ms * 1e-3) / 1e9
+            rec.update(bytes=bytes_by_stage[s], gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        if s in flops_by_stage:
+            tf = flops_by_stage[s] / (ms * 1e-3) / 1e12
+            rec.update(flops=flops_by_stage[s], tflops=round(tf, 2), frac_mfma=round(tf / FP32_MFMA_PEAK_TFLOPS, 4))
+        kernels[s] = rec
+    qa_ms = sum(avg_ms[s] for s in bytes_by_stage) * wl.layers
+    value = qa_bytes_step / (ms_per_step * 1e-3) / 1e9
+    kernel_qa_gbs = qa_bytes_step / (qa_ms * 1e-3) / 1e9
+    gef_agg = edges_fwd * d / (avg_ms["aggregate_fwd"] * 1e-3) / 1e9
+    gef_layer = edges_fwd * d * wl.layers / (ms_per_step * 1e-3) / 1e9
+
+    # dominant single-kernel stage (dense_bwd is two GEMM launches, so it is split in half)
+    single = {s: (avg_ms[s] / 2 if s == "dense_bwd" else avg_ms[s]) for s in avg_ms}
+    dom = max(single, key=single.get)
+    if dom in bytes_by_stage:
+        ach = bytes_by_stage[dom] / (avg_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        fl = flops_by_stage[dom] / (2 if dom == "dense_bwd" else 1)
+        ach = fl / (single[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(part, gp, bytes_by_stage)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "n_inner": n_in, "n_halo": n_h, "edges_with_self_loops": edges_fwd,
+                   "d": d, "layers": wl.layers, "model": wl.model,
+                   "halo_bits": {str(k): v for k, v in part.stats()["bits_hist"].items()},
+                   "parallelism": "single-gpu"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "gpu_ms_per_step_events": round(gpu_ms_step, 4),
+        "kernel_quant_aggregate_gbs": round(kernel_qa_gbs, 1),
+        "g_edge_feat_per_s": {"aggregate_fwd": round(gef_agg, 2), "full_layer": round(gef_layer, 2)},
+        "quant_aggregate_bytes_per_step": qa_bytes_step,
+        "message_bytes": {"main": int(4 * hw.sum()), "scales": 8 * n_h},
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(part, gp, bytes_by_stage):
+    """The oracle, as it is, on the host cores: quantise the send set and aggregate forward over a
+    bounded sample of rows; reported in the same GB/s units (bytes of the sampled work / time)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import aggregate as OA
+    from oracle import layer as OL
+    from quantized_halo_aggregation_amd import synth
+
+    n_in, d = part.n_in, part.d
+    rng = np.random.default_rng(0)
+    n_rows_q = min(part.n_h, 50_000)
+    rows_q = np.sort(rng.choice(part.n_h, size=n_rows_q, replace=False))
+    n_rows_a = min(n_in, 100_000)
+    rows_a = np.sort(rng.choice(n_in, size=n_rows_a, replace=False))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        msg = OL.send_halo(part.x[part.mirror[rows_q]], part.bits[rows_q], synth.QUANT_SEED, 0, 0, n_in)
+        tq = time.perf_counter() - t0
+        x_cols = np.concatenate([part.x, np.zeros((part.n_h, d), np.float32)])
+        x_cols[n_in + rows_q] = msg["received"]
+        t0 = time.perf_counter()
+        OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, x_cols, rows=rows_a)
+        ta = time.perf_counter() - t0
+    frac_q = n_rows_q / part.n_h
+    frac_a = n_rows_a / n_in
+    byts = bytes_by_stage["quantize_fwd"] * frac_q + bytes_by_stage["aggregate_fwd"] * frac_a
+    secs = tq + ta
+    return {"value": round(byts / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle quantise of {n_rows_q} of {part.n_h} halo rows + float64 GCN aggregation of "
+                      f"{n_rows_a} of {n_in} inner rows (same bytes model, {secs:.1f} s, one thread)"}
+
+
+if __name__ == "__main__":
+    main()

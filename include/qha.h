@@ -1,0 +1,209 @@
+/*
+ * qha.h -- C ABI of libqha: one GPU's share of a layer of distributed full-graph GNN training
+ * with stochastically quantised halo (boundary-node) messages, for AMD MI355X (gfx950).
+ *
+ * The method is SYLVIE's per-layer data path (page "SYLVIE: 3D-adaptive and Universal System for
+ * Large-scale Graph Neural Network Training", sections 5, 6 and 11, called "the guide" below):
+ * each boundary vector is quantised at its node's bit width, sent with its (min, scale), restored
+ * to float32 by the receiver and aggregated with the local rows; the backward pass does the same
+ * with embedding gradients.  This library holds the device work of that path:
+ *
+ *   qha_quantize_pack         per-vector stochastic integer quantisation + bit packing
+ *   qha_dequant_aggregate_fwd dequantisation fused into the normalised neighbour gather (SpMM)
+ *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
+ *   qha_dense_project         the dense projection (fp32 MFMA) with ReLU, and its gradients
+ *
+ * plus small set-up helpers.  Conventions shared by every entry point:
+ *   - Array arguments are caller-owned.  Pointers documented as "device" must be HIP device
+ *     memory (or host memory the device can access); "host" pointers are read on the CPU.
+ *   - The library allocates no memory and keeps no state between calls.  Device calls enqueue
+ *     asynchronously on `stream` (a hipStream_t; NULL is the default stream) and return once
+ *     the work is queued.
+ *   - Every scalar and pointer argument is checked on the host before anything is enqueued; a
+ *     failed check returns a status != QHA_OK and enqueues nothing.  Device data (index ranges,
+ *     bits matching offsets, finite values) is a precondition: qha_validate_csr checks index
+ *     arrays on the host, and kernels never read or write outside the ranges those arrays imply.
+ *   - Feature rows are float32, row-major, `d` contiguous features per row, leading dimension
+ *     (row stride, in elements) >= d and a multiple of 4; base pointers 16-byte aligned.
+ *   - Supported widths d: 16, 32, 64, 128, 256, 512.  Index arrays are int32 (nnz < 2^31).
+ *   - No exception crosses the ABI.  qha_last_error() gives a readable reason for the last
+ *     failure on the calling thread.
+ */
+#ifndef QHA_H
+#define QHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QHA_ABI_VERSION 1
+
+/* status codes */
+#define QHA_OK 0
+#define QHA_ERR_INVALID_ARG 1   /* a pointer, size, stride, alignment or enum is out of contract */
+#define QHA_ERR_UNSUPPORTED 2   /* well-formed but not implemented here (e.g. a width d not listed) */
+#define QHA_ERR_HIP 3           /* the HIP runtime reported an error while enqueueing */
+#define QHA_ERR_WORKSPACE 4     /* workspace missing or smaller than the matching *_workspace query */
+
+/* degree normalisations for qha_degree_norm */
+#define QHA_NORM_GCN 0          /* 1 / sqrt(deg + 1) */
+#define QHA_NORM_MEAN 1         /* deg > 0 ? 1 / deg : 0 */
+
+/* dense_project prologue / epilogue */
+#define QHA_PRO_NONE 0
+#define QHA_PRO_RELU_MASK 1     /* use a where aux > 0, else +0 (backward through ReLU) */
+#define QHA_EPI_NONE 0
+#define QHA_EPI_RELU 1          /* c = c > 0 ? c : +0 */
+
+/* largest number of edges one wavefront walks for one row in an aggregation plan */
+#define QHA_DEFAULT_CHUNK 512
+
+int qha_abi_version(void);
+const char* qha_status_string(int status);
+/* Reason for the most recent non-OK status returned on this thread ("" if none). */
+const char* qha_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Host-side set-up helpers (plain host memory, no device work)
+ * ---------------------------------------------------------------------------------------- */
+
+/* Packed-message layout (guide section 6: a b-bit integer vector per boundary node; section 9:
+ * the send buffer may be grouped by width, which is only a row order).  Row r of a packed
+ * buffer holds ceil(d*bits[r]/32) uint32 words (d words when bits[r] == 32, raw float32), code j
+ * at bit j*bits[r], least-significant bit first.  Writes word_offset[0..n_rows] (host, exclusive
+ * prefix sum, word_offset[0] = 0) and *total_words (host).  Errors: INVALID_ARG for null pointers,
+ * n_rows < 0, a width not in {1,2,4,8,32}, or a total beyond 2^32-1 words; UNSUPPORTED for d. */
+int qha_pack_layout(const uint8_t* bits, int64_t n_rows, int32_t d,
+                    uint32_t* word_offset, uint64_t* total_words);
+
+/* Checks a CSR on the host: rowptr[0] == 0, non-decreasing, rowptr[n_rows] == nnz, every
+ * column in [0, n_cols), and (if require_sorted) strictly ascending columns within a row.
+ * Returns QHA_OK or INVALID_ARG with the first offending row in qha_last_error(). */
+int qha_validate_csr(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, const int32_t* colidx,
+                     int32_t require_sorted);
+
+/* Transposes a CSR [n_rows x n_cols] into a CSR of its transpose [n_cols x n_rows] (the CSC of
+ * the original): the backward pass walks the same dependencies in reverse (guide sections 3 and
+ * 11), as a gather over destinations, with no atomics.  Entries of an output row come in
+ * ascending original-row order.  All arrays host: colptr[n_cols+1], rowidx[nnz]. */
+int qha_csr_transpose(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, const int32_t* colidx,
+                      int32_t* colptr, int32_t* rowidx);
+
+/* Work plan of an aggregation over a CSR (host construction, device use).  One work item is one
+ * wavefront walking at most `chunk` edges of one row, so a heavy row of a power-law graph is
+ * spread over several wavefronts; items of split rows come first (they write partial sums to the
+ * workspace, combined afterwards in chunk order, which keeps results deterministic), then one
+ * item per remaining row.  If skip_empty is set, rows with no edges get no item: valid only
+ * with beta = 1, where such rows are left as they are.
+ * qha_agg_plan_size fills the counts; the caller then allocates the four device arrays, calls
+ * qha_agg_plan_fill with host staging buffers of the same sizes, and copies them to the device. */
+typedef struct qha_agg_plan {
+  int64_t n_rows;          /* rows of the CSR the plan was built for */
+  int32_t chunk;           /* edge budget of one item */
+  int32_t skip_empty;      /* 1 if rows without edges have no item */
+  int64_t n_items;         /* items in item_row */
+  int64_t n_split_items;   /* leading items that belong to split rows (= partial-sum slots) */
+  int64_t n_split_rows;    /* rows split into more than one item */
+  const int32_t* item_row;    /* device [n_items]: CSR row of each item */
+  const int32_t* item_chunk;  /* device [n_split_items]: chunk index of each split item */
+  const int32_t* split_row;   /* device [n_split_rows]: the split rows */
+  const int32_t* split_ptr;   /* device [n_split_rows + 1]: item range of each split row */
+} qha_agg_plan;
+
+int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int32_t skip_empty,
+                      qha_agg_plan* plan);
+int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* item_row,
+                      int32_t* item_chunk, int32_t* split_row, int32_t* split_ptr);
+/* Bytes of workspace an aggregation with this plan and width needs (0 without split rows). */
+size_t qha_agg_workspace_bytes(const qha_agg_plan* plan, int32_t d);
+
+/* ------------------------------------------------------------------------------------------
+ * Device entry points
+ * ---------------------------------------------------------------------------------------- */
+
+/* Degree normalisation of the GCN aggregation (guide section 2: each term is divided by
+ * sqrt(d_v d_u)).  deg (device int32[n]) is a node's global degree without the self-loop
+ * (section 7 asks for global, not partition-local, degree); out (device float32[n]):
+ *   QHA_NORM_GCN:  1 / sqrt(deg + 1)   -- degree of A + I, so the edge weight is out[v] * out[u]
+ *   QHA_NORM_MEAN: deg > 0 ? 1 / deg : 0  (the GraphSAGE neighbour mean of one row)
+ * Both computed with correctly rounded sqrt and division. */
+int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, void* stream);
+
+/* Stochastic integer quantisation and packing of message rows (guide section 6):
+ *   scale = (max h - min h) / (2^b - 1), q = stochastic_round((h - min h) / scale), and the
+ *   zero-point min h travels with scale; b = bits[r] in {1,2,4,8}, or 32 for a raw float32 row.
+ * Row r reads x[(row_index ? row_index[r] : r) * ldx + j], j < d (device).  Its stochastic
+ * rounding draws come from Philox4x32-10 with counter (node_base + r, j / 8, epoch, stream_id)
+ * and key `seed`, so a call is reproducible from its arguments alone.  Writes the packed row at
+ * codes[word_offset[r] ...] (layout of qha_pack_layout), scale[r] and zero_point[r] (device).
+ * Floating-point steps (all float32, round-to-nearest, no contraction): mn/mx exact; zero_point
+ * = mn + 0; range = mx - mn; inv = L / range; range == 0 or inv infinite -> scale 0 and codes 0;
+ * else scale = range / L, y = (x - mn) * inv, q = min(floor(y) + (u16 < frac(y) * 65536), L)
+ * with u16 the element's 16-bit draw.  For b = 32, codes hold the raw bits and scale = zp = 0.
+ * A row whose bits[r] is not in {1,2,4,8,32} is skipped (nothing written).
+ * Errors: INVALID_ARG (nulls, n_rows < 0, ldx < d or not a multiple of 4, misalignment),
+ * UNSUPPORTED (d), HIP.  n_rows == 0 is a no-op. */
+int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int64_t n_rows,
+                      int32_t d, const uint8_t* bits, const uint32_t* word_offset,
+                      uint64_t seed, uint32_t epoch, uint32_t stream_id, uint32_t node_base,
+                      uint32_t* codes, float* scale, float* zero_point, void* stream);
+
+/* Dequantisation fused into the normalised neighbour aggregation (guide sections 2 and 6, the
+ * receiver's "dequantize, then aggregate(local_h, remote_h)" of section 11).  For each CSR row
+ * v < n_rows (device rowptr[n_rows+1], colidx[nnz]):
+ *   out[v] = (beta ? out[v] : 0) + sum over e in row v of (r[v] * c[u]) * x~_u,  u = colidx[e]
+ *   x~_u = x_inner[u * ldx + j]                         if u < n_inner
+ *        = scale[k] * q_k[j] + zero_point[k]  (fp32)     if u = n_inner + k, k < n_halo
+ * (raw float when bits[k] == 32).  r (device float[n_rows]) and c (device float[n_inner+n_halo])
+ * may be NULL for 1.0.  codes/word_offset/bits/scale/zero_point are the received halo messages
+ * in qha_quantize_pack's layout (device; may be NULL when n_halo == 0).  plan may be NULL (one
+ * wavefront per row); otherwise it must have been built for this rowptr, and a plan with
+ * skip_empty requires beta == 1.  workspace (device) must hold qha_agg_workspace_bytes(plan, d)
+ * bytes.  beta is 0 or 1.  Summation is in float32 along each row's edges in order (chunks of a
+ * split row are summed separately, then added in chunk order); results are deterministic.
+ * Errors: INVALID_ARG, UNSUPPORTED (d), WORKSPACE, HIP. */
+int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
+                              const qha_agg_plan* plan, const float* r, const float* c,
+                              const float* x_inner, int64_t ldx, int64_t n_inner,
+                              const uint32_t* codes, const uint32_t* word_offset,
+                              const uint8_t* bits, const float* scale, const float* zero_point,
+                              int64_t n_halo, int32_t d, int32_t beta, float* out, int64_t ldo,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Transposed aggregation for embedding gradients (guide sections 3 and 11: gradients flow back
+ * along the same cross-partition dependencies).  Given the transpose of the forward CSR
+ * (qha_csr_transpose: row u lists the forward rows v that gather u), for u < n_rows:
+ *   grad_in[u] = (beta ? grad_in[u] : 0) + sum over e in row u of (r[u] * c[v]) * grad_out[v]
+ * with v = rowidx[e] < n_grad_rows.  With r and c the forward's c and r this is the adjoint of
+ * qha_dequant_aggregate_fwd.  Same plan / workspace / beta / determinism rules.  Pass a row
+ * range [u0, u1) by offsetting colptr, r and grad_in. */
+int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx,
+                      const qha_agg_plan* plan, const float* r, const float* c,
+                      const float* grad_out, int64_t ldg, int64_t n_grad_rows,
+                      int32_t d, int32_t beta, float* grad_in, int64_t ldi,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dense projection and its gradients (guide section 2: z_v = W a_v, h_v = sigma(z_v); section 7:
+ * dL/dW = sum_v (dL/dh_v * sigma'(z_v)) a_v^T) on fp32 matrix cores (MFMA):
+ *   C[m x n] = (beta ? C : 0) + op(A)[m x k] * op(B)[k x n]
+ * op(X) = X (row-major, leading dimension ld) or X^T when trans_x = 1.  The forward is
+ * trans_b = 1 with B = W [d_out x d_in] and epilogue RELU; the backward's dA is dZ * W and its
+ * dW is dZ^T * A (trans_a = 1), both with prologue RELU_MASK and aux = the forward output H, so
+ * that dZ = dH * [H > 0] is formed while A is loaded (aux has op(A)'s storage layout).
+ * When m*n is small and k large the reduction is split over k into the workspace (device,
+ * qha_dense_project_workspace bytes) and summed in a fixed order in float64; results are
+ * deterministic.  beta is 0 or 1.  Errors: INVALID_ARG, WORKSPACE, HIP. */
+int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k,
+                      const float* a, int64_t lda, const float* b, int64_t ldb,
+                      int32_t beta, float* c, int64_t ldc,
+                      int32_t prologue, const float* aux, int64_t ld_aux, int32_t epilogue,
+                      void* workspace, size_t workspace_bytes, void* stream);
+size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QHA_H */

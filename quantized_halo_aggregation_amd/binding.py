@@ -1,0 +1,294 @@
+"""Thin ctypes binding of libqha (include/qha.h): argument marshalling only.
+
+Each function takes torch tensors that live on the GPU (or numpy arrays for the host helpers),
+checks dtype / device / layout, passes raw pointers to the C entry point of the same name and
+raises on a non-OK status.  All arithmetic happens in the HIP kernels behind the C ABI; there is
+no fallback path -- importing this module fails loudly if libqha.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqha.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_halo_aggregation_amd.build` "
+                      "(or __graft_entry__.build()); there is no CPU fallback")
+
+_lib = C.CDLL(LIB_PATH)
+
+QHA_OK, QHA_ERR_INVALID_ARG, QHA_ERR_UNSUPPORTED, QHA_ERR_HIP, QHA_ERR_WORKSPACE = range(5)
+NORM_GCN, NORM_MEAN = 0, 1
+PRO_NONE, PRO_RELU_MASK = 0, 1
+EPI_NONE, EPI_RELU = 0, 1
+DEFAULT_CHUNK = 512
+
+_i32, _i64, _u32, _u64, _sz, _vp = C.c_int32, C.c_int64, C.c_uint32, C.c_uint64, C.c_size_t, C.c_void_p
+
+
+class AggPlanStruct(C.Structure):
+    _fields_ = [("n_rows", _i64), ("chunk", _i32), ("skip_empty", _i32), ("n_items", _i64),
+                ("n_split_items", _i64), ("n_split_rows", _i64), ("item_row", _vp), ("item_chunk", _vp),
+                ("split_row", _vp), ("split_ptr", _vp)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_P = C.POINTER
+_abi_version = _sig("qha_abi_version", _i32)
+_status_string = _sig("qha_status_string", C.c_char_p, _i32)
+_last_error = _sig("qha_last_error", C.c_char_p)
+_pack_layout = _sig("qha_pack_layout", _i32, _vp, _i64, _i32, _vp, _P(_u64))
+_validate_csr = _sig("qha_validate_csr", _i32, _i64, _i64, _vp, _vp, _i32)
+_csr_transpose = _sig("qha_csr_transpose", _i32, _i64, _i64, _vp, _vp, _vp, _vp)
+_plan_size = _sig("qha_agg_plan_size", _i32, _i64, _vp, _i32, _i32, _P(AggPlanStruct))
+_plan_fill = _sig("qha_agg_plan_fill", _i32, _vp, _P(AggPlanStruct), _vp, _vp, _vp, _vp)
+_plan_ws = _sig("qha_agg_workspace_bytes", _sz, _P(AggPlanStruct), _i32)
+_degree_norm = _sig("qha_degree_norm", _i32, _vp, _i64, _i32, _vp, _vp)
+_quantize_pack = _sig("qha_quantize_pack", _i32, _vp, _i64, _vp, _i64, _i32, _vp, _vp, _u64, _u32, _u32, _u32,
+                      _vp, _vp, _vp, _vp)
+_dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp, _P(AggPlanStruct), _vp, _vp,
+                              _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
+_aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _P(AggPlanStruct), _vp, _vp, _vp, _i64, _i64,
+                      _i32, _i32, _vp, _i64, _vp, _sz, _vp)
+_dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
+                      _i64, _i32, _vp, _i64, _i32, _vp, _sz, _vp)
+_dense_ws = _sig("qha_dense_project_workspace", _sz, _i32, _i32, _i64, _i64, _i64)
+
+EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_layout", "qha_validate_csr",
+            "qha_csr_transpose", "qha_agg_plan_size", "qha_agg_plan_fill", "qha_agg_workspace_bytes",
+            "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_aggregate_bwd",
+            "qha_dense_project", "qha_dense_project_workspace"]
+
+
+class QhaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_status_string(status).decode()} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != QHA_OK:
+        if status in (QHA_ERR_INVALID_ARG, QHA_ERR_UNSUPPORTED, QHA_ERR_WORKSPACE):
+            raise ValueError(str(QhaError(status, where)))
+        raise QhaError(status, where)
+
+
+def abi_version() -> int:
+    return int(_abi_version())
+
+
+# ------------------------------------------------------------------------------------------------
+# pointer helpers
+# ------------------------------------------------------------------------------------------------
+
+def _dev(t, dtype, name, allow_none=False):
+    """Device pointer of a torch tensor after dtype / device checks (None -> NULL if allowed)."""
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} must not be None")
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    return t.data_ptr()
+
+
+def _dev32(t, name):
+    """Pointer of a 32-bit word array (int32 or uint32 tensor, reinterpreted as uint32)."""
+    import torch
+    if t is None or t.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError(f"{name} must be an int32/uint32 tensor")
+    return _dev(t, t.dtype, name)
+
+
+def _rows(t, name):
+    """(pointer, leading dimension) of a float32 matrix whose rows may be strided."""
+    import torch
+    if t is None:
+        return None, 0
+    _dev(t, torch.float32, name)
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    return t.data_ptr(), t.stride(0)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(stream)
+
+
+def _host(a, dtype, name):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+# ------------------------------------------------------------------------------------------------
+# host-side set-up helpers
+# ------------------------------------------------------------------------------------------------
+
+def pack_layout(bits, d: int):
+    """Word offsets (uint32 [n+1]) and total words of a packed message buffer."""
+    bits, pb = _host(bits, np.uint8, "bits")
+    off = np.empty(bits.size + 1, dtype=np.uint32)
+    total = _u64(0)
+    _check(_pack_layout(pb, bits.size, int(d), off.ctypes.data, C.byref(total)), "qha_pack_layout")
+    return off, int(total.value)
+
+
+def validate_csr(rowptr, colidx, n_cols: int, require_sorted: bool = True):
+    rowptr, pr = _host(rowptr, np.int32, "rowptr")
+    colidx, pc = _host(colidx, np.int32, "colidx")
+    _check(_validate_csr(rowptr.size - 1, int(n_cols), pr, pc, int(require_sorted)), "qha_validate_csr")
+
+
+def csr_transpose(rowptr, colidx, n_cols: int):
+    rowptr, pr = _host(rowptr, np.int32, "rowptr")
+    colidx, pc = _host(colidx, np.int32, "colidx")
+    colptr = np.empty(int(n_cols) + 1, dtype=np.int32)
+    rowidx = np.empty(colidx.size, dtype=np.int32)
+    _check(_csr_transpose(rowptr.size - 1, int(n_cols), pr, pc, colptr.ctypes.data, rowidx.ctypes.data),
+           "qha_csr_transpose")
+    return colptr, rowidx
+
+
+class AggPlan:
+    """A work plan for one CSR (host arrays built by the library, kept on the device)."""
+
+    def __init__(self, rowptr, chunk: int = DEFAULT_CHUNK, skip_empty: bool = False, device="cuda"):
+        import torch
+        rowptr, pr = _host(rowptr, np.int32, "rowptr")
+        st = AggPlanStruct()
+        _check(_plan_size(rowptr.size - 1, pr, int(chunk), int(skip_empty), C.byref(st)), "qha_agg_plan_size")
+        item_row = np.empty(max(st.n_items, 1), np.int32)
+        item_chunk = np.empty(max(st.n_split_items, 1), np.int32)
+        split_row = np.empty(max(st.n_split_rows, 1), np.int32)
+        split_ptr = np.empty(st.n_split_rows + 1, np.int32)
+        _check(_plan_fill(pr, C.byref(st), item_row.ctypes.data, item_chunk.ctypes.data, split_row.ctypes.data,
+                          split_ptr.ctypes.data), "qha_agg_plan_fill")
+        self.host = {"item_row": item_row[:st.n_items], "item_chunk": item_chunk[:st.n_split_items],
+                     "split_row": split_row[:st.n_split_rows], "split_ptr": split_ptr}
+        self.dev = {k: torch.from_numpy(np.ascontiguousarray(v if v.size else np.zeros(1, np.int32))).to(device)
+                    for k, v in self.host.items()}
+        st.item_row = self.dev["item_row"].data_ptr()
+        st.item_chunk = self.dev["item_chunk"].data_ptr()
+        st.split_row = self.dev["split_row"].data_ptr()
+        st.split_ptr = self.dev["split_ptr"].data_ptr()
+        self.struct = st
+
+    @property
+    def n_items(self):
+        return int(self.struct.n_items)
+
+    @property
+    def n_split_rows(self):
+        return int(self.struct.n_split_rows)
+
+    def workspace_bytes(self, d: int) -> int:
+        return int(_plan_ws(C.byref(self.struct), int(d)))
+
+
+def _plan_ref(plan):
+    return None if plan is None else C.byref(plan.struct)
+
+
+def dense_project_workspace(trans_a: int, trans_b: int, m: int, n: int, k: int) -> int:
+    return int(_dense_ws(int(trans_a), int(trans_b), int(m), int(n), int(k)))
+
+
+# ------------------------------------------------------------------------------------------------
+# device entry points
+# ------------------------------------------------------------------------------------------------
+
+def degree_norm(deg, kind: int, out, stream=None):
+    import torch
+    _check(_degree_norm(_dev(deg, torch.int32, "deg"), deg.numel(), int(kind), _dev(out, torch.float32, "out"),
+                        _stream(stream)), "qha_degree_norm")
+
+
+def quantize_pack(x, row_index, n_rows: int, bits, word_offset, seed: int, epoch: int, stream_id: int,
+                  node_base: int, codes, scale, zero_point, stream=None):
+    import torch
+    px, ldx = _rows(x, "x")
+    d = x.shape[1]
+    _check(_quantize_pack(px, ldx, _dev(row_index, torch.int32, "row_index", allow_none=True), int(n_rows), int(d),
+                          _dev(bits, torch.uint8, "bits"), _dev32(word_offset, "word_offset"),
+                          int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch), int(stream_id), int(node_base),
+                          _dev32(codes, "codes"), _dev(scale, torch.float32, "scale"),
+                          _dev(zero_point, torch.float32, "zero_point"), _stream(stream)), "qha_quantize_pack")
+
+
+def dequant_aggregate_fwd(rowptr, colidx, plan, r, c, x_inner, n_inner: int, codes, word_offset, bits, scale,
+                          zero_point, n_halo: int, beta: int, out, workspace=None, n_rows=None, stream=None):
+    import torch
+    n_rows = rowptr.numel() - 1 if n_rows is None else int(n_rows)
+    px, ldx = _rows(x_inner, "x_inner")
+    po, ldo = _rows(out, "out")
+    d = out.shape[1]
+    halo = n_halo > 0
+    ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_dequant_aggregate_fwd(
+        n_rows, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"), _plan_ref(plan),
+        _dev(r, torch.float32, "r", allow_none=True), _dev(c, torch.float32, "c", allow_none=True),
+        px, ldx, int(n_inner),
+        _dev32(codes, "codes") if halo else None,
+        _dev32(word_offset, "word_offset") if halo else None,
+        _dev(bits, torch.uint8, "bits") if halo else None,
+        _dev(scale, torch.float32, "scale") if halo else None,
+        _dev(zero_point, torch.float32, "zero_point") if halo else None,
+        int(n_halo), int(d), int(beta), po, ldo, ws_ptr, ws_bytes, _stream(stream)), "qha_dequant_aggregate_fwd")
+
+
+def aggregate_bwd(colptr, rowidx, plan, r, c, grad_out, n_grad_rows: int, beta: int, grad_in, workspace=None,
+                  n_rows=None, stream=None):
+    import torch
+    n_rows = colptr.numel() - 1 if n_rows is None else int(n_rows)
+    pg, ldg = _rows(grad_out, "grad_out")
+    pi, ldi = _rows(grad_in, "grad_in")
+    d = grad_in.shape[1]
+    ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_aggregate_bwd(n_rows, _dev(colptr, torch.int32, "colptr"), _dev(rowidx, torch.int32, "rowidx"),
+                          _plan_ref(plan), _dev(r, torch.float32, "r", allow_none=True),
+                          _dev(c, torch.float32, "c", allow_none=True), pg, ldg, int(n_grad_rows), int(d), int(beta),
+                          pi, ldi, ws_ptr, ws_bytes, _stream(stream)), "qha_aggregate_bwd")
+
+
+def dense_project(trans_a: int, trans_b: int, a, b, beta: int, c, prologue: int = PRO_NONE, aux=None,
+                  epilogue: int = EPI_NONE, workspace=None, stream=None):
+    """C = (beta ? C : 0) + op(A) op(B); shapes are read from the tensors."""
+    pa, lda = _rows(a, "a")
+    pb, ldb = _rows(b, "b")
+    pc, ldc = _rows(c, "c")
+    m = a.shape[1] if trans_a else a.shape[0]
+    k = a.shape[0] if trans_a else a.shape[1]
+    kb = b.shape[1] if trans_b else b.shape[0]
+    n = b.shape[0] if trans_b else b.shape[1]
+    if kb != k or tuple(c.shape) != (m, n):
+        raise ValueError(f"shape mismatch: op(A) {m}x{k}, op(B) {kb}x{n}, C {tuple(c.shape)}")
+    paux, ldaux = (None, 0)
+    if prologue == PRO_RELU_MASK:
+        if aux is None or tuple(aux.shape) != tuple(a.shape):
+            raise ValueError("aux must have A's shape")
+        paux, ldaux = _rows(aux, "aux")
+    ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_dense_project(int(trans_a), int(trans_b), m, n, k, pa, lda, pb, ldb, int(beta), pc, ldc, int(prologue),
+                          paux, ldaux, int(epilogue), ws_ptr, ws_bytes, _stream(stream)), "qha_dense_project")

@@ -1,0 +1,411 @@
+// C ABI of libqha: host-side argument checks, set-up helpers and kernel launches.
+// Every check runs before anything is enqueued, so bad arguments never reach the GPU.
+#include "../../include/qha.h"
+#include "qha_internal.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return QHA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool width_supported(int32_t d) {
+  return d == 16 || d == 32 || d == 64 || d == 128 || d == 256 || d == 512;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t kMaxIndex = 2147483647LL;
+
+int check_rows(const char* name, const float* p, int64_t ld, int32_t d) {
+  if (!p) return fail(QHA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (ld < d || (ld & 3) != 0) return fail(QHA_ERR_INVALID_ARG, "%s: leading dimension %lld must be >= d=%d and a multiple of 4", name, (long long)ld, d);
+  if (!aligned16(p)) return fail(QHA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return QHA_OK;
+}
+
+int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d, const void* ws, size_t ws_bytes) {
+  if (!plan) return QHA_OK;
+  if (plan->n_rows != n_rows) return fail(QHA_ERR_INVALID_ARG, "plan was built for %lld rows, call has %lld", (long long)plan->n_rows, (long long)n_rows);
+  if (plan->chunk <= 0) return fail(QHA_ERR_INVALID_ARG, "plan chunk must be positive");
+  if (plan->n_items < 0 || plan->n_split_items < 0 || plan->n_split_rows < 0 || plan->n_split_items > plan->n_items)
+    return fail(QHA_ERR_INVALID_ARG, "plan counts are inconsistent");
+  if (plan->n_items > 0 && !plan->item_row) return fail(QHA_ERR_INVALID_ARG, "plan item_row is NULL");
+  if (plan->n_split_items > 0 && (!plan->item_chunk || !plan->split_row || !plan->split_ptr))
+    return fail(QHA_ERR_INVALID_ARG, "plan split arrays are NULL");
+  if (plan->skip_empty && beta != 1) return fail(QHA_ERR_INVALID_ARG, "a plan that skips empty rows needs beta = 1");
+  const size_t need = qha_agg_workspace_bytes(plan, d);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(QHA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  }
+  return QHA_OK;
+}
+
+void fill_plan_args(qha::GatherArgs& g, const qha_agg_plan* plan, int64_t n_rows, void* ws) {
+  if (plan) {
+    g.n_items = plan->n_items;
+    g.n_split_items = plan->n_split_items;
+    g.chunk = plan->chunk;
+    g.item_row = plan->item_row;
+    g.item_chunk = plan->item_chunk;
+    g.n_split_rows = plan->n_split_rows;
+    g.split_row = plan->split_row;
+    g.split_ptr = plan->split_ptr;
+  } else {
+    g.n_items = n_rows;
+    g.n_split_items = 0;
+    g.chunk = 0;
+    g.item_row = nullptr;
+    g.item_chunk = nullptr;
+    g.n_split_rows = 0;
+    g.split_row = nullptr;
+    g.split_ptr = nullptr;
+  }
+  g.partial = static_cast<float*>(ws);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qha_abi_version(void) { return QHA_ABI_VERSION; }
+
+const char* qha_status_string(int status) {
+  switch (status) {
+    case QHA_OK: return "ok";
+    case QHA_ERR_INVALID_ARG: return "invalid argument";
+    case QHA_ERR_UNSUPPORTED: return "unsupported";
+    case QHA_ERR_HIP: return "HIP runtime error";
+    case QHA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* qha_last_error(void) { return g_err; }
+
+int qha_pack_layout(const uint8_t* bits, int64_t n_rows, int32_t d, uint32_t* word_offset, uint64_t* total_words) {
+  if (n_rows < 0) return fail(QHA_ERR_INVALID_ARG, "n_rows < 0");
+  if (!word_offset || !total_words || (n_rows > 0 && !bits)) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  uint64_t acc = 0;
+  word_offset[0] = 0;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const uint32_t b = bits[r];
+    uint64_t w;
+    if (b == 32) w = static_cast<uint64_t>(d);
+    else if (b == 1 || b == 2 || b == 4 || b == 8) w = (static_cast<uint64_t>(d) * b + 31) / 32;
+    else return fail(QHA_ERR_INVALID_ARG, "bits[%lld] = %u is not in {1,2,4,8,32}", (long long)r, b);
+    acc += w;
+    if (acc > 0xFFFFFFFFull) return fail(QHA_ERR_INVALID_ARG, "packed buffer exceeds 2^32-1 words");
+    word_offset[r + 1] = static_cast<uint32_t>(acc);
+  }
+  *total_words = acc;
+  return ok();
+}
+
+int qha_validate_csr(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, const int32_t* colidx, int32_t require_sorted) {
+  if (n_rows < 0 || n_cols < 0 || n_rows > kMaxIndex || n_cols > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if (!rowptr) return fail(QHA_ERR_INVALID_ARG, "rowptr is NULL");
+  if (rowptr[0] != 0) return fail(QHA_ERR_INVALID_ARG, "rowptr[0] != 0");
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int32_t b = rowptr[r], e = rowptr[r + 1];
+    if (e < b) return fail(QHA_ERR_INVALID_ARG, "rowptr decreases at row %lld", (long long)r);
+    if (e > b && !colidx) return fail(QHA_ERR_INVALID_ARG, "colidx is NULL");
+    for (int32_t i = b; i < e; ++i) {
+      if (colidx[i] < 0 || colidx[i] >= n_cols) return fail(QHA_ERR_INVALID_ARG, "row %lld has column %d outside [0, %lld)", (long long)r, colidx[i], (long long)n_cols);
+      if (require_sorted && i > b && colidx[i] <= colidx[i - 1]) return fail(QHA_ERR_INVALID_ARG, "row %lld is not strictly ascending", (long long)r);
+    }
+  }
+  return ok();
+}
+
+int qha_csr_transpose(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, const int32_t* colidx, int32_t* colptr, int32_t* rowidx) {
+  if (n_rows < 0 || n_cols < 0 || n_rows > kMaxIndex || n_cols > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if (!rowptr || !colptr) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  const int64_t nnz = rowptr[n_rows];
+  if (nnz > 0 && (!colidx || !rowidx)) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  std::vector<int64_t> cnt(static_cast<size_t>(n_cols) + 1, 0);
+  for (int64_t e = 0; e < nnz; ++e) {
+    const int32_t c = colidx[e];
+    if (c < 0 || c >= n_cols) return fail(QHA_ERR_INVALID_ARG, "column %d outside [0, %lld)", c, (long long)n_cols);
+    ++cnt[static_cast<size_t>(c) + 1];
+  }
+  for (int64_t c = 0; c < n_cols; ++c) cnt[c + 1] += cnt[c];
+  for (int64_t c = 0; c <= n_cols; ++c) colptr[c] = static_cast<int32_t>(cnt[c]);
+  for (int64_t r = 0; r < n_rows; ++r)
+    for (int32_t e = rowptr[r]; e < rowptr[r + 1]; ++e) rowidx[cnt[colidx[e]]++] = static_cast<int32_t>(r);
+  return ok();
+}
+
+int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int32_t skip_empty, qha_agg_plan* plan) {
+  if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
+  if (!rowptr || !plan) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (chunk <= 0) return fail(QHA_ERR_INVALID_ARG, "chunk must be positive");
+  int64_t items = 0, split_items = 0, split_rows = 0;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
+    if (len < 0) return fail(QHA_ERR_INVALID_ARG, "rowptr decreases at row %lld", (long long)r);
+    if (len == 0) {
+      if (!skip_empty) ++items;
+      continue;
+    }
+    const int64_t c = (len + chunk - 1) / chunk;
+    items += c;
+    if (c > 1) {
+      split_items += c;
+      ++split_rows;
+    }
+  }
+  if (items > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "too many work items");
+  std::memset(plan, 0, sizeof(*plan));
+  plan->n_rows = n_rows;
+  plan->chunk = chunk;
+  plan->skip_empty = skip_empty ? 1 : 0;
+  plan->n_items = items;
+  plan->n_split_items = split_items;
+  plan->n_split_rows = split_rows;
+  return ok();
+}
+
+int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* item_row, int32_t* item_chunk,
+                      int32_t* split_row, int32_t* split_ptr) {
+  if (!rowptr || !plan) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if ((plan->n_items > 0 && !item_row) || (plan->n_split_items > 0 && (!item_chunk || !split_row || !split_ptr)))
+    return fail(QHA_ERR_INVALID_ARG, "NULL output array");
+  const int32_t chunk = plan->chunk;
+  // split rows first (heaviest work starts first), then every other row in order
+  int64_t it = 0, sr = 0;
+  if (plan->n_split_rows > 0) split_ptr[0] = 0;
+  for (int64_t r = 0; r < plan->n_rows; ++r) {
+    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
+    const int64_t c = (len + chunk - 1) / chunk;
+    if (c > 1) {
+      for (int64_t j = 0; j < c; ++j) {
+        item_row[it] = static_cast<int32_t>(r);
+        item_chunk[it] = static_cast<int32_t>(j);
+        ++it;
+      }
+      split_row[sr] = static_cast<int32_t>(r);
+      split_ptr[++sr] = static_cast<int32_t>(it);
+    }
+  }
+  if (it != plan->n_split_items || sr != plan->n_split_rows) return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr");
+  for (int64_t r = 0; r < plan->n_rows; ++r) {
+    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
+    if (len > chunk) continue;
+    if (len == 0 && plan->skip_empty) continue;
+    item_row[it++] = static_cast<int32_t>(r);
+  }
+  if (it != plan->n_items) return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr");
+  return ok();
+}
+
+size_t qha_agg_workspace_bytes(const qha_agg_plan* plan, int32_t d) {
+  if (!plan || d <= 0) return 0;
+  return static_cast<size_t>(plan->n_split_items) * static_cast<size_t>(d) * sizeof(float);
+}
+
+int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, void* stream) {
+  if (n < 0) return fail(QHA_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && (!deg || !out)) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (kind != QHA_NORM_GCN && kind != QHA_NORM_MEAN) return fail(QHA_ERR_INVALID_ARG, "unknown normalisation %d", kind);
+  return hip_status(qha::launch_degree_norm(deg, n, kind, out, static_cast<hipStream_t>(stream)), "degree_norm");
+}
+
+int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int64_t n_rows, int32_t d,
+                      const uint8_t* bits, const uint32_t* word_offset, uint64_t seed, uint32_t epoch,
+                      uint32_t stream_id, uint32_t node_base, uint32_t* codes, float* scale, float* zero_point,
+                      void* stream) {
+  if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
+  if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  if (n_rows == 0) return ok();
+  int st = check_rows("x", x, ldx, d);
+  if (st) return st;
+  if (!bits || !word_offset || !codes || !scale || !zero_point) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned4(codes) || !aligned4(scale) || !aligned4(zero_point) || !aligned4(word_offset) ||
+      (row_index && !aligned4(row_index)))
+    return fail(QHA_ERR_INVALID_ARG, "misaligned array");
+  if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_rows) - 1 > 0xFFFFFFFFull)
+    return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
+  qha::QuantArgs a;
+  a.x = x;
+  a.ldx = ldx;
+  a.row_index = row_index;
+  a.n_rows = n_rows;
+  a.bits = bits;
+  a.word_offset = word_offset;
+  a.seed_lo = static_cast<uint32_t>(seed);
+  a.seed_hi = static_cast<uint32_t>(seed >> 32);
+  a.epoch = epoch;
+  a.stream_id = stream_id;
+  a.node_base = node_base;
+  a.codes = codes;
+  a.scale = scale;
+  a.zero_point = zero_point;
+  return hip_status(qha::launch_quantize(a, d, static_cast<hipStream_t>(stream)), "quantize_pack");
+}
+
+int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const qha_agg_plan* plan,
+                              const float* r, const float* c, const float* x_inner, int64_t ldx, int64_t n_inner,
+                              const uint32_t* codes, const uint32_t* word_offset, const uint8_t* bits,
+                              const float* scale, const float* zero_point, int64_t n_halo, int32_t d, int32_t beta,
+                              float* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > kMaxIndex || n_inner < 0 || n_halo < 0 || n_inner + n_halo > kMaxIndex)
+    return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  if (beta != 0 && beta != 1) return fail(QHA_ERR_INVALID_ARG, "beta must be 0 or 1");
+  if (n_rows == 0) return ok();
+  if (!rowptr || !colidx) return fail(QHA_ERR_INVALID_ARG, "rowptr/colidx is NULL");
+  int st = check_rows("out", out, ldo, d);
+  if (st) return st;
+  if (n_inner > 0) {
+    st = check_rows("x_inner", x_inner, ldx, d);
+    if (st) return st;
+  }
+  if (n_halo > 0 && (!codes || !word_offset || !bits || !scale || !zero_point))
+    return fail(QHA_ERR_INVALID_ARG, "halo message arrays are NULL");
+  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
+  if (st) return st;
+  qha::GatherArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.n_rows = n_rows;
+  g.rowptr = rowptr;
+  g.colidx = colidx;
+  fill_plan_args(g, plan, n_rows, workspace);
+  g.rs = r;
+  g.cs = c;
+  g.x = x_inner;
+  g.ldx = ldx;
+  g.n_inner = n_inner;
+  g.codes = codes;
+  g.word_offset = word_offset;
+  g.bits = bits;
+  g.scale = scale;
+  g.zero_point = zero_point;
+  g.n_halo = n_halo;
+  g.beta = beta;
+  g.out = out;
+  g.ldo = ldo;
+  return hip_status(qha::launch_gather(g, d, n_halo > 0, static_cast<hipStream_t>(stream)), "dequant_aggregate_fwd");
+}
+
+int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const qha_agg_plan* plan,
+                      const float* r, const float* c, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
+                      int32_t d, int32_t beta, float* grad_in, int64_t ldi, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (n_rows < 0 || n_rows > kMaxIndex || n_grad_rows < 0 || n_grad_rows > kMaxIndex)
+    return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  if (beta != 0 && beta != 1) return fail(QHA_ERR_INVALID_ARG, "beta must be 0 or 1");
+  if (n_rows == 0) return ok();
+  if (!colptr || !rowidx) return fail(QHA_ERR_INVALID_ARG, "colptr/rowidx is NULL");
+  int st = check_rows("grad_in", grad_in, ldi, d);
+  if (st) return st;
+  if (n_grad_rows > 0) {
+    st = check_rows("grad_out", grad_out, ldg, d);
+    if (st) return st;
+  }
+  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
+  if (st) return st;
+  qha::GatherArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.n_rows = n_rows;
+  g.rowptr = colptr;
+  g.colidx = rowidx;
+  fill_plan_args(g, plan, n_rows, workspace);
+  g.rs = r;
+  g.cs = c;
+  g.x = grad_out;
+  g.ldx = ldg;
+  g.n_inner = n_grad_rows;
+  g.beta = beta;
+  g.out = grad_in;
+  g.ldo = ldi;
+  return hip_status(qha::launch_gather(g, d, false, static_cast<hipStream_t>(stream)), "aggregate_bwd");
+}
+
+size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k) {
+  (void)trans_a;
+  (void)trans_b;
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  int32_t s;
+  int64_t kps;
+  qha::gemm_split_rule(m, n, k, &s, &kps);
+  return s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(m) * static_cast<size_t>(n) * sizeof(float) : 0;
+}
+
+int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, const float* a, int64_t lda,
+                      const float* b, int64_t ldb, int32_t beta, float* c, int64_t ldc, int32_t prologue,
+                      const float* aux, int64_t ld_aux, int32_t epilogue, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (m < 0 || n < 0 || k < 0 || m > kMaxIndex || n > kMaxIndex || k > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return fail(QHA_ERR_INVALID_ARG, "trans flags must be 0 or 1");
+  if (beta != 0 && beta != 1) return fail(QHA_ERR_INVALID_ARG, "beta must be 0 or 1");
+  if (prologue != QHA_PRO_NONE && prologue != QHA_PRO_RELU_MASK) return fail(QHA_ERR_INVALID_ARG, "unknown prologue");
+  if (epilogue != QHA_EPI_NONE && epilogue != QHA_EPI_RELU) return fail(QHA_ERR_INVALID_ARG, "unknown epilogue");
+  if (m == 0 || n == 0) return ok();
+  // storage shapes: A is [m x k] or [k x m]; B is [k x n] or [n x k]; the contiguous extent of each
+  // must be a multiple of 4 (16-byte loads)
+  const int64_t a_cols = trans_a ? m : k, b_cols = trans_b ? k : n;
+  if (k > 0) {
+    if (!a || !b) return fail(QHA_ERR_INVALID_ARG, "A or B is NULL");
+    if ((a_cols & 3) || (b_cols & 3)) return fail(QHA_ERR_INVALID_ARG, "the contiguous extent of A (%lld) and B (%lld) must be multiples of 4", (long long)a_cols, (long long)b_cols);
+    if (lda < a_cols || (lda & 3) || !aligned16(a)) return fail(QHA_ERR_INVALID_ARG, "lda / A alignment out of contract");
+    if (ldb < b_cols || (ldb & 3) || !aligned16(b)) return fail(QHA_ERR_INVALID_ARG, "ldb / B alignment out of contract");
+    if (prologue == QHA_PRO_RELU_MASK && (!aux || ld_aux < a_cols || (ld_aux & 3) || !aligned16(aux)))
+      return fail(QHA_ERR_INVALID_ARG, "aux out of contract");
+  }
+  if (!c || ldc < n || !aligned4(c)) return fail(QHA_ERR_INVALID_ARG, "C / ldc out of contract");
+  qha::GemmArgs g;
+  g.ta = trans_a;
+  g.tb = trans_b;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.a = a;
+  g.lda = lda;
+  g.b = b;
+  g.ldb = ldb;
+  g.beta = beta;
+  g.c = c;
+  g.ldc = ldc;
+  g.pro = prologue;
+  g.aux = aux;
+  g.ld_aux = ld_aux;
+  g.epi = epilogue;
+  qha::gemm_split_rule(m, n, k, &g.splits, &g.k_per_split);
+  g.ws = static_cast<float*>(workspace);
+  if (g.splits > 1) {
+    const size_t need = qha_dense_project_workspace(trans_a, trans_b, m, n, k);
+    if (!workspace || workspace_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+    if (!aligned4(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
+  }
+  return hip_status(qha::launch_gemm(g, static_cast<hipStream_t>(stream)), "dense_project");
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal launch interface between the C ABI (abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace qha {
+
+struct QuantArgs {
+  const float* x;
+  int64_t ldx;
+  const int32_t* row_index;
+  int64_t n_rows;
+  const uint8_t* bits;
+  const uint32_t* word_offset;
+  uint32_t seed_lo, seed_hi, epoch, stream_id, node_base;
+  uint32_t* codes;
+  float* scale;
+  float* zero_point;
+};
+
+// One gather over a CSR: out[row] (+)= sum_e rs[row] * cs[col_e] * value(col_e).  value() is a
+// float32 row of x for col < n_inner and a dequantised halo message for col >= n_inner.
+struct GatherArgs {
+  int64_t n_rows;
+  const int32_t* rowptr;
+  const int32_t* colidx;
+  // work plan (item_row == nullptr: item i is row i, no splitting)
+  int64_t n_items;
+  int64_t n_split_items;
+  int32_t chunk;
+  const int32_t* item_row;
+  const int32_t* item_chunk;
+  int64_t n_split_rows;
+  const int32_t* split_row;
+  const int32_t* split_ptr;
+  // weights
+  const float* rs;
+  const float* cs;
+  // values
+  const float* x;
+  int64_t ldx;
+  int64_t n_inner;
+  const uint32_t* codes;
+  const uint32_t* word_offset;
+  const uint8_t* bits;
+  const float* scale;
+  const float* zero_point;
+  int64_t n_halo;
+  // output
+  int32_t beta;
+  float* out;
+  int64_t ldo;
+  float* partial;  // [n_split_items, d] partial sums of split rows
+};
+
+struct GemmArgs {
+  int32_t ta, tb;
+  int64_t m, n, k;
+  const float* a;
+  int64_t lda;
+  const float* b;
+  int64_t ldb;
+  int32_t beta;
+  float* c;
+  int64_t ldc;
+  int32_t pro;
+  const float* aux;
+  int64_t ld_aux;
+  int32_t epi;
+  float* ws;           // split-k partials [splits, m, n]
+  int32_t splits;
+  int64_t k_per_split;
+};
+
+// Split-k rule shared by the workspace query and the launcher.
+void gemm_split_rule(int64_t m, int64_t n, int64_t k, int32_t* splits, int64_t* k_per_split);
+
+hipError_t launch_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs& a, int32_t d, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace qha

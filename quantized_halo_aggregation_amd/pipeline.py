@@ -1,0 +1,218 @@
+"""One GPU's share of a partition's GNN layers, driven through the C ABI.
+
+The per-layer data path of the SYLVIE guide (sections 5 and 11) on one GPU:
+
+  forward   quantize_pack(send set) -> [exchange] -> dequant_aggregate_fwd -> dense_project(+ReLU)
+  backward  dense_project(dA, dW; ReLU mask) -> aggregate_bwd(halo columns) -> quantize_pack
+            -> [exchange] -> aggregate_bwd(inner columns) -> dequant_aggregate_fwd(received, add)
+
+The exchange is the identity under the mirror model (halo k is the remote copy of inner node
+mirror[k]): the codes sent are the codes received.  Everything numeric runs in libqha's kernels;
+this module only lays out device buffers and issues the calls in order on one stream.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synth
+
+QUANT_SEED = synth.QUANT_SEED
+
+
+@dataclasses.dataclass
+class Messages:
+    """One packed message buffer: the codes and per-row (min, scale) of the halo rows."""
+    codes: torch.Tensor        # int32 words (uint32 bit patterns)
+    scale: torch.Tensor
+    zero_point: torch.Tensor
+
+
+class GpuPartition:
+    """Device-resident CSR / CSC / norms / widths / plans of one partition (set-up, untimed)."""
+
+    def __init__(self, part: synth.Partition, device: str = "cuda", chunk: int = B.DEFAULT_CHUNK,
+                 bits=None):
+        self.part = part
+        self.device = device
+        n_in, n_h, d = part.n_in, part.n_h, part.d
+        self.n_in, self.n_h, self.d = n_in, n_h, d
+        self.n_cols = n_in + n_h
+        self.model = part.wl.model
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+        if self.model == "gcn":
+            ptr, idx = synth.with_self_loops(part.nbr_ptr, part.nbr_idx)
+        else:
+            ptr, idx = part.nbr_ptr, part.nbr_idx
+        self.h_ptr, self.h_idx = ptr, idx
+        colptr, rowidx = B.csr_transpose(ptr, idx, self.n_cols)
+        self.h_colptr, self.h_rowidx = colptr, rowidx
+        self.rowptr, self.colidx = dev(ptr), dev(idx)
+        self.colptr, self.rowidx = dev(colptr), dev(rowidx)
+
+        # mirror map as a CSR over inner rows listing the halo rows that copy them
+        m_ptr, m_idx = B.csr_transpose(np.arange(n_h + 1, dtype=np.int32), part.mirror, n_in)
+        self.mirror = dev(part.mirror)
+        self.m_ptr, self.m_idx = dev(m_ptr), dev(m_idx)
+
+        self.set_bits(part.bits if bits is None else bits)
+
+        self.deg = dev(part.deg)
+        if self.model == "gcn":
+            self.norm = torch.empty(self.n_cols, dtype=torch.float32, device=device)
+            B.degree_norm(self.deg, B.NORM_GCN, self.norm)
+            self.r_fwd, self.c_fwd = self.norm[:n_in], self.norm
+        else:
+            row_len = dev(np.diff(part.nbr_ptr).astype(np.int32))
+            self.mean_r = torch.empty(n_in, dtype=torch.float32, device=device)
+            B.degree_norm(row_len, B.NORM_MEAN, self.mean_r)
+            self.r_fwd, self.c_fwd = self.mean_r, None
+
+        self.plan_fwd = B.AggPlan(ptr, chunk, device=device)
+        self.plan_bwd_halo = B.AggPlan(colptr[n_in:], chunk, device=device)
+        self.plan_bwd_inner = B.AggPlan(colptr[:n_in + 1], chunk, device=device)
+        self.plan_mirror = B.AggPlan(m_ptr, chunk, skip_empty=True, device=device)
+        ws = max(p.workspace_bytes(d) for p in (self.plan_fwd, self.plan_bwd_halo, self.plan_bwd_inner,
+                                                 self.plan_mirror))
+        self.agg_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
+        self.dense_ws = None
+
+    def set_bits(self, bits):
+        bits = np.ascontiguousarray(bits, dtype=np.uint8)
+        self.h_bits = bits
+        off, total = B.pack_layout(bits, self.d)
+        self.h_word_offset = off
+        self.total_words = total
+        self.bits = torch.from_numpy(bits).to(self.device)
+        self.word_offset = torch.from_numpy(off.view(np.int32)).to(self.device)
+
+    def new_messages(self) -> Messages:
+        return Messages(torch.empty(max(self.total_words, 1), dtype=torch.int32, device=self.device),
+                        torch.empty(self.n_h, dtype=torch.float32, device=self.device),
+                        torch.empty(self.n_h, dtype=torch.float32, device=self.device))
+
+    def dense_workspace(self, *shapes):
+        need = max(B.dense_project_workspace(*s) for s in shapes)
+        if need and (self.dense_ws is None or self.dense_ws.numel() * 4 < need):
+            self.dense_ws = torch.empty(need // 4 + 4, dtype=torch.float32, device=self.device)
+        return self.dense_ws
+
+    # -------------------------------------------------------------------------------------
+    # the calls of one layer
+    # -------------------------------------------------------------------------------------
+
+    def quantize_send(self, x, row_index, msg: Messages, epoch, stream_id, seed=QUANT_SEED):
+        """a1 / a7: quantise the n_h outgoing boundary rows (x[row_index] or x itself)."""
+        B.quantize_pack(x, row_index, self.n_h, self.bits, self.word_offset, seed, epoch, stream_id, self.n_in,
+                        msg.codes, msg.scale, msg.zero_point)
+
+    def aggregate_fwd(self, x_inner, msg: Messages, out):
+        """a3: out = sum over N(v) and v of w_vu * x~_u, halo rows dequantised from msg."""
+        B.dequant_aggregate_fwd(self.rowptr, self.colidx, self.plan_fwd, self.r_fwd, self.c_fwd, x_inner, self.n_in,
+                                msg.codes, self.word_offset, self.bits, msg.scale, msg.zero_point, self.n_h, 0, out,
+                                workspace=self.agg_ws)
+
+    def aggregate_bwd_halo(self, grad_out, dx_halo):
+        """a6 (halo range): gradients of the halo columns."""
+        n_in = self.n_in
+        if self.model == "gcn":
+            r, c = self.norm[n_in:], self.norm[:n_in]
+        else:
+            r, c = None, self.mean_r
+        B.aggregate_bwd(self.colptr[n_in:], self.rowidx, self.plan_bwd_halo, r, c, grad_out, n_in, 0, dx_halo,
+                        workspace=self.agg_ws)
+
+    def aggregate_bwd_inner(self, grad_out, dx_inner, beta):
+        """a6 (inner range): gradients of the inner columns (beta = 1 adds to dx_inner)."""
+        n_in = self.n_in
+        if self.model == "gcn":
+            r, c = self.norm[:n_in], self.norm[:n_in]
+        else:
+            r, c = None, self.mean_r
+        B.aggregate_bwd(self.colptr[:n_in + 1], self.rowidx, self.plan_bwd_inner, r, c, grad_out, n_in, beta,
+                        dx_inner, workspace=self.agg_ws)
+
+    def add_received(self, msg: Messages, dx_inner):
+        """a8: dx_inner[mirror[k]] += dequantised gradient message k."""
+        B.dequant_aggregate_fwd(self.m_ptr, self.m_idx, self.plan_mirror, None, None, None, 0, msg.codes,
+                                self.word_offset, self.bits, msg.scale, msg.zero_point, self.n_h, 1, dx_inner,
+                                workspace=self.agg_ws)
+
+
+class LayerStack:
+    """Buffers and call order of a stack of GCN or GraphSAGE-mean layers on one partition."""
+
+    def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED):
+        self.gp = gp
+        self.seed = seed
+        dev = gp.device
+        n_in, d = gp.n_in, gp.d
+        self.L = len(weights)
+        self.W = [torch.from_numpy(w).to(dev) for w in weights]
+        self.dW = [torch.empty_like(w) for w in self.W]
+        sage = gp.model == "sage"
+        self.sage = sage
+        k_in = 2 * d if sage else d
+        # activations: A_l is layer l's aggregated input ([n, 2d] for SAGE with the self half
+        # first), H_l its output.  For SAGE, H_{l-1} is the left half of A_l.
+        if sage:
+            self.A = [torch.empty(n_in, k_in, dtype=torch.float32, device=dev) for _ in range(self.L)]
+            self.A[0][:, :d].copy_(torch.from_numpy(x).to(dev))
+            self.H = [self.A[l + 1][:, :d] for l in range(self.L - 1)] + \
+                     [torch.empty(n_in, d, dtype=torch.float32, device=dev)]
+            self.X = [self.A[0][:, :d]] + self.H[:-1]
+        else:
+            self.A = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
+            self.H = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
+            self.X = [torch.from_numpy(x).to(dev)] + self.H[:-1]
+        self.grad_top = torch.from_numpy(grad_top).to(dev)
+        self.dA = [torch.empty(n_in, k_in, dtype=torch.float32, device=dev) for _ in range(self.L)]
+        if sage:
+            # dL/dh of layer l's input rows = the self half of dA, plus the transposed mean (added
+            # in place), plus the received halo gradients
+            self.dX = [self.dA[l][:, :d] for l in range(self.L)]
+        else:
+            self.dX = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
+        self.dX_halo = torch.empty(gp.n_h, d, dtype=torch.float32, device=dev)
+        self.msg_f = [gp.new_messages() for _ in range(self.L)]
+        self.msg_b = [gp.new_messages() for _ in range(self.L)]
+        self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), (0, 0, n_in, k_in, d), (1, 0, d, k_in, n_in))
+
+    def forward_layer(self, l, epoch, hook=None):
+        gp, d = self.gp, self.gp.d
+        x = self.X[l]
+        gp.quantize_send(x, gp.mirror, self.msg_f[l], epoch, 2 * l, self.seed)
+        if hook: hook("quantize_fwd", l)
+        agg_out = self.A[l][:, d:] if self.sage else self.A[l]
+        gp.aggregate_fwd(x, self.msg_f[l], agg_out)
+        if hook: hook("aggregate_fwd", l)
+        B.dense_project(0, 1, self.A[l], self.W[l], 0, self.H[l], epilogue=B.EPI_RELU, workspace=self.dense_ws)
+        if hook: hook("dense_fwd", l)
+
+    def backward_layer(self, l, epoch, hook=None):
+        gp, d = self.gp, self.gp.d
+        dH = self.grad_top if l == self.L - 1 else self.dX[l + 1]
+        B.dense_project(0, 0, dH, self.W[l], 0, self.dA[l], prologue=B.PRO_RELU_MASK, aux=self.H[l],
+                        workspace=self.dense_ws)
+        B.dense_project(1, 0, dH, self.A[l], 0, self.dW[l], prologue=B.PRO_RELU_MASK, aux=self.H[l],
+                        workspace=self.dense_ws)
+        if hook: hook("dense_bwd", l)
+        g = self.dA[l][:, d:] if self.sage else self.dA[l]
+        gp.aggregate_bwd_halo(g, self.dX_halo)
+        if hook: hook("aggregate_bwd_halo", l)
+        gp.quantize_send(self.dX_halo, None, self.msg_b[l], epoch, 2 * l + 1, self.seed)
+        if hook: hook("quantize_bwd", l)
+        gp.aggregate_bwd_inner(g, self.dX[l], 1 if self.sage else 0)
+        if hook: hook("aggregate_bwd_inner", l)
+        gp.add_received(self.msg_b[l], self.dX[l])
+        if hook: hook("add_received", l)
+
+    def step(self, epoch=0, hook=None):
+        for l in range(self.L):
+            self.forward_layer(l, epoch, hook)
+        for l in reversed(range(self.L)):
+            self.backward_layer(l, epoch, hook)

@@ -1,0 +1,159 @@
+"""The C ABI without a GPU: the library loads, exports every entry point of include/qha.h, its host
+helpers compute the documented layouts, and bad arguments are rejected before any HIP call.
+
+Argument-error cases pass fake (never dereferenced) device addresses: the checks must fire first.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_halo_aggregation_amd import binding as B
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qha.h")
+FAKE = 0x10000          # 16-byte aligned, never dereferenced by a call that fails its checks
+
+
+def test_header_symbols_are_exported():
+    text = open(HDR).read()
+    declared = set(re.findall(r"\b(qha_[a-z0-9_]+)\s*\(", text))
+    assert declared, "no declarations found"
+    lib = C.CDLL(B.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in qha.h but not exported"
+    assert declared == set(B.EXPORTED)
+    assert B.abi_version() == 1
+
+
+def test_status_strings():
+    assert B._status_string(0) == b"ok"
+    assert B._status_string(2) == b"unsupported"
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256, 512])
+def test_pack_layout(d):
+    bits = np.array([1, 2, 4, 8, 32, 4, 1], np.uint8)
+    off, total = B.pack_layout(bits, d)
+    sizes = [d if b == 32 else (d * int(b) + 31) // 32 for b in bits]
+    assert list(off) == [0] + list(np.cumsum(sizes))
+    assert total == sum(sizes)
+
+
+def test_pack_layout_rejects_bad_width_and_d():
+    with pytest.raises(ValueError, match="not in"):
+        B.pack_layout(np.array([4, 3], np.uint8), 128)
+    with pytest.raises(ValueError, match="not supported"):
+        B.pack_layout(np.array([4], np.uint8), 24)
+
+
+def test_csr_transpose_and_validate():
+    rng = np.random.default_rng(0)
+    n_rows, n_cols = 50, 70
+    dense = rng.random((n_rows, n_cols)) < 0.1
+    ptr = np.concatenate([[0], np.cumsum(dense.sum(1))]).astype(np.int32)
+    idx = np.nonzero(dense)[1].astype(np.int32)
+    B.validate_csr(ptr, idx, n_cols)
+    cptr, ridx = B.csr_transpose(ptr, idx, n_cols)
+    dt = dense.T
+    assert np.array_equal(cptr, np.concatenate([[0], np.cumsum(dt.sum(1))]))
+    assert np.array_equal(ridx, np.nonzero(dt)[1])
+    bad = idx.copy()
+    bad[3] = n_cols
+    with pytest.raises(ValueError, match="outside"):
+        B.validate_csr(ptr, bad, n_cols)
+    unsorted = idx.copy()
+    r = int(np.argmax(np.diff(ptr) >= 2))
+    unsorted[ptr[r]], unsorted[ptr[r] + 1] = unsorted[ptr[r] + 1], unsorted[ptr[r]]
+    with pytest.raises(ValueError, match="ascending"):
+        B.validate_csr(ptr, unsorted, n_cols)
+
+
+def _plan_host(ptr, chunk, skip_empty):
+    st = B.AggPlanStruct()
+    B._check(B._plan_size(ptr.size - 1, ptr.ctypes.data, chunk, int(skip_empty), C.byref(st)), "size")
+    arrs = [np.zeros(max(n, 1), np.int32) for n in (st.n_items, st.n_split_items, st.n_split_rows)]
+    sp = np.zeros(st.n_split_rows + 1, np.int32)
+    B._check(B._plan_fill(ptr.ctypes.data, C.byref(st), arrs[0].ctypes.data, arrs[1].ctypes.data,
+                          arrs[2].ctypes.data, sp.ctypes.data), "fill")
+    return st, arrs[0][:st.n_items], arrs[1][:st.n_split_items], arrs[2][:st.n_split_rows], sp
+
+
+@pytest.mark.parametrize("skip_empty", [False, True])
+def test_agg_plan_covers_every_edge_once(skip_empty):
+    lens = np.array([0, 3, 1200, 5, 0, 512, 513, 2000, 1], np.int32)
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    chunk = 512
+    st, item_row, item_chunk, split_row, split_ptr = _plan_host(ptr, chunk, skip_empty)
+    covered = np.zeros(ptr[-1], np.int32)
+    for it, row in enumerate(item_row):
+        e0, e1 = ptr[row], ptr[row + 1]
+        if it < st.n_split_items:
+            e0 = e0 + item_chunk[it] * chunk
+            e1 = min(e1, e0 + chunk)
+        covered[e0:e1] += 1
+    assert (covered == 1).all()
+    assert list(split_row) == [2, 6, 7]
+    assert list(split_ptr) == [0, 3, 5, 9]
+    rows_with_items = set(item_row.tolist())
+    assert (0 in rows_with_items) == (not skip_empty)
+    assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 4
+
+
+def test_device_calls_reject_bad_arguments_before_any_hip_call():
+    q = B._quantize_pack
+    # unsupported width
+    assert q(FAKE, 24, None, 10, 24, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, FAKE, None) == B.QHA_ERR_UNSUPPORTED
+    # leading dimension below d
+    assert q(FAKE, 64, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # misaligned rows
+    assert q(FAKE + 4, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # null outputs
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, None, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # node ids overflow 32 bits
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0xFFFFFFFF, FAKE, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # nothing to do is OK without touching the device
+    assert q(None, 0, None, 0, 128, None, None, 1, 0, 0, 0, None, None, None, None) == B.QHA_OK
+
+    f = B._dequant_aggregate_fwd
+    args = dict(n_rows=10, rowptr=FAKE, colidx=FAKE, plan=None, r=None, c=None, x=FAKE, ldx=128, n_inner=5,
+                codes=FAKE, wo=FAKE, bits=FAKE, sc=FAKE, zp=FAKE, n_halo=5, d=128, beta=0, out=FAKE, ldo=128,
+                ws=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+    assert call(beta=2) == B.QHA_ERR_INVALID_ARG
+    assert call(d=100) == B.QHA_ERR_UNSUPPORTED
+    assert call(ldo=130) == B.QHA_ERR_INVALID_ARG
+    assert call(codes=None) == B.QHA_ERR_INVALID_ARG
+    assert call(rowptr=None) == B.QHA_ERR_INVALID_ARG
+    assert call(n_inner=-1) == B.QHA_ERR_INVALID_ARG
+    # a plan that skips empty rows cannot be combined with beta = 0
+    lens = np.array([0, 600, 3], np.int32)
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    st, *_ = _plan_host(ptr, 512, True)
+    st.item_row = st.item_chunk = st.split_row = st.split_ptr = FAKE
+    assert call(n_rows=3, plan=C.byref(st)) == B.QHA_ERR_INVALID_ARG
+    st2, *_ = _plan_host(ptr, 512, False)
+    st2.item_row = st2.item_chunk = st2.split_row = st2.split_ptr = FAKE
+    # split rows need a workspace
+    assert call(n_rows=3, plan=C.byref(st2)) == B.QHA_ERR_WORKSPACE
+    # plan built for another row count
+    assert call(n_rows=4, plan=C.byref(st2)) == B.QHA_ERR_INVALID_ARG
+
+    g = B._aggregate_bwd
+    assert g(10, FAKE, FAKE, None, None, None, FAKE, 128, 10, 128, 3, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
+    assert g(10, FAKE, FAKE, None, None, None, FAKE, 96, 10, 128, 0, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
+
+    p = B._dense_project
+    # contiguous extent of A not a multiple of 4
+    assert p(0, 1, 100, 128, 126, FAKE, 128, FAKE, 128, 0, FAKE, 128, 0, None, 0, 1, None, 0, None) == B.QHA_ERR_INVALID_ARG
+    # mask prologue without aux
+    assert p(0, 0, 100, 128, 128, FAKE, 128, FAKE, 128, 0, FAKE, 128, 1, None, 0, 0, None, 0, None) == B.QHA_ERR_INVALID_ARG
+    # split-k reduction without workspace
+    assert B.dense_project_workspace(1, 0, 128, 128, 300000) > 0
+    assert p(1, 0, 128, 128, 300000, FAKE, 128, FAKE, 128, 0, FAKE, 128, 0, None, 0, 0, None, 0, None) == B.QHA_ERR_WORKSPACE
+    assert B._last_error().decode().startswith("workspace")
+    assert B._degree_norm(FAKE, 10, 7, FAKE, None) == B.QHA_ERR_INVALID_ARG

@@ -1,0 +1,162 @@
+"""Fused dequantise + aggregate (forward), transposed aggregate (backward) and the received-gradient add
+on the GPU against the oracle, on the same seeded inputs (messages quantised by the oracle)."""
+import numpy as np
+import pytest
+
+import gpu_helpers as H
+from oracle import aggregate as OA
+from quantized_halo_aggregation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = synth.QUANT_SEED
+
+# (n_in, n_h, nnz, d, bits recipe, model, chunk): several tiles, ragged sizes, heavy rows split
+CASES = [
+    (301, 97, 3000, 16, ("uniform", (1, 2, 4, 8, 32)), "gcn", 512),
+    (517, 713, 20000, 32, ("uniform", (1, 2, 4, 8)), "gcn", 32),
+    (777, 300, 12000, 64, ("uniform", (1, 2, 4, 8, 32)), "gcn", 64),
+    (1003, 301, 30000, 128, ("top", 4, 8, 0.10), "gcn", 64),
+    (1003, 301, 30000, 128, ("uniform", (1, 2, 4, 8, 32)), "gcn", 512),
+    (401, 203, 8000, 256, ("top", 2, 4, 0.20), "gcn", 100),
+    (203, 101, 2000, 512, ("uniform", (1, 2, 4, 8, 32)), "gcn", 16),
+    (999, 333, 9000, 128, ("const", 1), "sage", 48),
+    (513, 257, 5000, 256, ("const", 1), "sage", 512),
+]
+
+
+def _case_id(c):
+    return f"{c[5]}-n{c[0]}-h{c[1]}-d{c[3]}-c{c[6]}"
+
+
+def _setup(case):
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition
+    n_in, n_h, nnz, d, bits, model, chunk = case
+    wl = synth.small_workload(n_in, n_h, nnz, d, bits=bits, model=model, index=100 + CASES.index(case))
+    part = synth.make_partition(wl)
+    gp = GpuPartition(part, chunk=chunk)
+    return part, gp
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_forward_aggregation(case):
+    H.require_gpu()
+    import torch
+    part, gp = _setup(case)
+    n_in, d = part.n_in, part.d
+    msg = H.oracle_messages(part.x[part.mirror], part.bits, SEED, 0, 0, n_in)
+    x_cols = np.concatenate([part.x, msg["received"]])
+    if part.wl.model == "gcn":
+        ref = OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, x_cols)
+        H.note(f"aggregate_fwd {_case_id(case)}")
+        out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+        gp.aggregate_fwd(H.dev(part.x), H.upload_messages(gp, msg), out)
+        H.assert_close(H.host(out), ref, what="aggregate_fwd")
+    else:
+        ref = OA.mean_aggregate(part.nbr_ptr, part.nbr_idx, x_cols)
+        H.note(f"aggregate_fwd sage {_case_id(case)}")
+        acat = torch.full((n_in, 2 * d), np.nan, dtype=torch.float32, device="cuda")
+        acat[:, :d] = H.dev(part.x)
+        gp.aggregate_fwd(acat[:, :d], H.upload_messages(gp, msg), acat[:, d:])
+        got = H.host(acat)
+        H.assert_close(got[:, d:], ref, what="mean aggregate (strided output)")
+        H.assert_bits_equal(got[:, :d], part.x, "self half untouched")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_backward_aggregation_and_received_add(case):
+    H.require_gpu()
+    import torch
+    part, gp = _setup(case)
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal((n_in, d)).astype(np.float32)
+    if part.wl.model == "gcn":
+        ref = OA.gcn_aggregate_t(part.nbr_ptr, part.nbr_idx, part.deg, g)
+    else:
+        ref = OA.mean_aggregate_t(part.nbr_ptr, part.nbr_idx, g, n_in + n_h)
+    H.note(f"aggregate_bwd {_case_id(case)}")
+    g_dev = H.dev(g)
+    dxh = torch.full((n_h, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_halo(g_dev, dxh)
+    H.assert_close(H.host(dxh), ref[n_in:], what="aggregate_bwd halo")
+    base = rng.standard_normal((n_in, d)).astype(np.float32)
+    dxi = H.dev(base)
+    gp.aggregate_bwd_inner(g_dev, dxi, 1)
+    H.assert_close(H.host(dxi), ref[:n_in] + base.astype(np.float64), what="aggregate_bwd inner (beta=1)")
+    dxi0 = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_inner(g_dev, dxi0, 0)
+    H.assert_close(H.host(dxi0), ref[:n_in], what="aggregate_bwd inner (beta=0)")
+
+    # received halo gradients: quantised by the oracle, dequantised and added on the GPU
+    halo_grad = ref[n_in:].astype(np.float32)
+    msg = H.oracle_messages(halo_grad, part.bits, SEED, 0, 1, n_in)
+    want = OA.add_received(H.host(dxi0).astype(np.float64), part.mirror, msg["received"])
+    start = H.host(dxi0)
+    gp.add_received(H.upload_messages(gp, msg), dxi0)
+    got = H.host(dxi0)
+    H.assert_close(got, want, what="received add")
+    untouched = np.setdiff1d(np.arange(n_in), part.mirror)
+    H.assert_bits_equal(got[untouched], start[untouched], "rows without a halo copy")
+
+
+def test_deterministic_repeats():
+    H.require_gpu()
+    import torch
+    part, gp = _setup(CASES[3])
+    msg = H.upload_messages(gp, H.oracle_messages(part.x[part.mirror], part.bits, SEED, 0, 0, part.n_in))
+    x = H.dev(part.x)
+    outs = []
+    H.note("aggregate determinism")
+    for _ in range(3):
+        out = torch.empty(part.n_in, part.d, dtype=torch.float32, device="cuda")
+        gp.aggregate_fwd(x, msg, out)
+        outs.append(H.host(out))
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+
+
+def test_plain_rows_and_degenerate_inputs():
+    """No plan (one wavefront per row), rows without edges, all-halo rows, empty calls, b = 32 halos."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(9)
+    d, n_inner, n_halo = 128, 40, 30
+    lens = rng.integers(0, 9, size=25)
+    lens[[0, 7, 24]] = 0
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    idx = np.concatenate([np.sort(rng.choice(n_inner + n_halo, size=l, replace=False)) for l in lens]).astype(np.int32)
+    B.validate_csr(ptr, idx, n_inner + n_halo)
+    x = rng.standard_normal((n_inner, d)).astype(np.float32)
+    hx = rng.standard_normal((n_halo, d)).astype(np.float32)
+    bits = rng.choice(np.array([1, 2, 4, 8, 32], np.uint8), size=n_halo)
+    msg = H.oracle_messages(hx, bits, 11, 0, 0, n_inner)
+    off, _ = B.pack_layout(bits, d)
+    r = rng.random(25).astype(np.float32)
+    c = rng.random(n_inner + n_halo).astype(np.float32)
+    x_cols = np.concatenate([x, msg["received"]]).astype(np.float64)
+    rows = np.repeat(np.arange(25), lens)
+    ref = np.zeros((25, d))
+    np.add.at(ref, rows, (r[rows].astype(np.float64) * c[idx])[:, None] * x_cols[idx])
+    H.note("aggregate plain rows")
+    out = torch.full((25, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dequant_aggregate_fwd(H.dev(ptr), H.dev(idx), None, H.dev(r), H.dev(c), H.dev(x), n_inner,
+                            H.dev(msg["words"].view(np.int32)), H.dev(off.view(np.int32)), H.dev(bits),
+                            H.dev(msg["scale"]), H.dev(msg["zero_point"]), n_halo, 0, out)
+    got = H.host(out)
+    H.assert_close(got, ref, what="plain rows")
+    assert not got[[0, 7, 24]].any()
+    # zero rows: nothing happens
+    B.dequant_aggregate_fwd(H.dev(ptr[:1]), H.dev(idx), None, None, None, H.dev(x), n_inner, None, None, None, None,
+                            None, 0, 0, out, n_rows=0)
+    # no halo at all: only inner columns may appear
+    inner_only = ptr.copy()
+    keep = idx < n_inner
+    cnt = np.bincount(rows[keep], minlength=25)
+    inner_only = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    out2 = torch.full((25, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dequant_aggregate_fwd(H.dev(inner_only), H.dev(idx[keep]), None, None, None, H.dev(x), n_inner, None, None,
+                            None, None, None, 0, 0, out2)
+    ref2 = np.zeros((25, d))
+    np.add.at(ref2, rows[keep], x[idx[keep]].astype(np.float64))
+    H.assert_close(H.host(out2), ref2, what="inner-only rows, unit weights")

@@ -1,0 +1,85 @@
+"""qha_dense_project (fp32 MFMA) against the oracle's float64 projection and gradients."""
+import numpy as np
+import pytest
+
+import gpu_helpers as H
+from oracle import dense as OD
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("m,d_in,d_out", [(1, 16, 16), (1001, 16, 16), (777, 64, 64), (3001, 128, 128),
+                                          (1000, 256, 256), (513, 512, 256), (130, 32, 48)])
+def test_forward_projection_relu(m, d_in, d_out):
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(m + d_in)
+    a = rng.standard_normal((m, d_in)).astype(np.float32)
+    w = (rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).astype(np.float32)
+    ref = OD.project(a, w)
+    H.note(f"dense fwd m={m} {d_in}->{d_out}")
+    c = torch.full((m, d_out), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, H.dev(a), H.dev(w), 0, c, epilogue=B.EPI_RELU)
+    H.assert_close(H.host(c), ref, what="relu(A W^T)")
+    # no epilogue, accumulate into C
+    c0 = rng.standard_normal((m, d_out)).astype(np.float32)
+    c = H.dev(c0)
+    B.dense_project(0, 1, H.dev(a), H.dev(w), 1, c)
+    H.assert_close(H.host(c), a.astype(np.float64) @ w.T.astype(np.float64) + c0, what="C + A W^T")
+
+
+@pytest.mark.parametrize("m,d_in,d_out", [(1001, 16, 16), (3001, 128, 128), (20000, 128, 128),
+                                          (4099, 512, 256), (70000, 256, 256)])
+def test_backward_projection(m, d_in, d_out):
+    """dA = (dH * [H > 0]) W and dW = (dH * [H > 0])^T A; large m exercises the split-k reduction."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(m * 3 + d_out)
+    a = rng.standard_normal((m, d_in)).astype(np.float32)
+    w = (rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).astype(np.float32)
+    h = OD.project(a, w).astype(np.float32)
+    dh = rng.standard_normal((m, d_out)).astype(np.float32)
+    da_ref, dw_ref = OD.project_backward(a, w, h, dh)
+    ws_bytes = max(B.dense_project_workspace(0, 0, m, d_in, d_out), B.dense_project_workspace(1, 0, d_out, d_in, m))
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    H.note(f"dense bwd m={m} {d_in}->{d_out} ws={ws_bytes}")
+    dh_d, h_d, a_d, w_d = H.dev(dh), H.dev(h), H.dev(a), H.dev(w)
+    da = torch.full((m, d_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 0, dh_d, w_d, 0, da, prologue=B.PRO_RELU_MASK, aux=h_d, workspace=ws)
+    H.assert_close(H.host(da), da_ref, what="dA")
+    dw = torch.full((d_out, d_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(1, 0, dh_d, a_d, 0, dw, prologue=B.PRO_RELU_MASK, aux=h_d, workspace=ws)
+    got = H.host(dw)
+    H.assert_close_normwise(got, dw_ref, what="dW")
+    # deterministic: the split-k partials are summed in a fixed order
+    dw2 = torch.empty_like(dw)
+    B.dense_project(1, 0, dh_d, a_d, 0, dw2, prologue=B.PRO_RELU_MASK, aux=h_d, workspace=ws)
+    assert np.array_equal(H.host(dw2).view(np.uint32), got.view(np.uint32))
+
+
+def test_strided_operands_and_empty_reduction():
+    """Operands that are column slices of wider buffers (the GraphSAGE concat layout), and k = 0."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(3)
+    m, d = 999, 128
+    acat = rng.standard_normal((m, 2 * d)).astype(np.float32)
+    w = (rng.standard_normal((d, 2 * d)) / 16).astype(np.float32)
+    big = torch.full((m, 3 * d), np.nan, dtype=torch.float32, device="cuda")
+    out = big[:, d:2 * d]
+    H.note("dense strided")
+    B.dense_project(0, 1, H.dev(acat), H.dev(w), 0, out, epilogue=B.EPI_RELU)
+    got = H.host(big)
+    H.assert_close(got[:, d:2 * d], OD.project(acat, w), what="strided C")
+    assert np.isnan(got[:, :d]).all() and np.isnan(got[:, 2 * d:]).all()
+    a_d = H.dev(acat)
+    c = torch.full((m, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, a_d[:, :d], H.dev(np.ascontiguousarray(w[:, d:])), 0, c)
+    H.assert_close(H.host(c), acat[:, :d].astype(np.float64) @ w[:, d:].T.astype(np.float64), what="strided A")
+    # an empty reduction writes zeros (then the epilogue)
+    z = torch.full((m, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, a_d[:, :0], torch.empty((d, 0), dtype=torch.float32, device="cuda"), 0, z)
+    assert not H.host(z).any()
