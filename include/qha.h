@@ -117,7 +117,8 @@ int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int3
                       qha_agg_plan* plan);
 int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* item_row,
                       int32_t* item_chunk, int32_t* split_row, int32_t* split_ptr);
-/* Bytes of workspace an aggregation with this plan and width needs (0 without split rows). */
+/* Bytes of workspace an aggregation with this plan and width needs: one float64 partial row per
+ * split item (0 without split rows). */
 size_t qha_agg_workspace_bytes(const qha_agg_plan* plan, int32_t d);
 
 /* ------------------------------------------------------------------------------------------
@@ -162,8 +163,9 @@ int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int
  * in qha_quantize_pack's layout (device; may be NULL when n_halo == 0).  plan may be NULL (one
  * wavefront per row); otherwise it must have been built for this rowptr, and a plan with
  * skip_empty requires beta == 1.  workspace (device) must hold qha_agg_workspace_bytes(plan, d)
- * bytes.  beta is 0 or 1.  Summation is in float32 along each row's edges in order (chunks of a
- * split row are summed separately, then added in chunk order); results are deterministic.
+ * bytes.  beta is 0 or 1.  Products and sums are accumulated in float64 along each row's edges in
+ * order (chunks of a split row are summed separately, then added in chunk order) and rounded to
+ * float32 once, after adding the old value when beta = 1; results are deterministic.
  * Errors: INVALID_ARG, UNSUPPORTED (d), WORKSPACE, HIP. */
 int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
                               const qha_agg_plan* plan, const float* r, const float* c,
@@ -193,9 +195,12 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
  * trans_b = 1 with B = W [d_out x d_in] and epilogue RELU; the backward's dA is dZ * W and its
  * dW is dZ^T * A (trans_a = 1), both with prologue RELU_MASK and aux = the forward output H, so
  * that dZ = dH * [H > 0] is formed while A is loaded (aux has op(A)'s storage layout).
- * When m*n is small and k large the reduction is split over k into the workspace (device,
- * qha_dense_project_workspace bytes) and summed in a fixed order in float64; results are
- * deterministic.  beta is 0 or 1.  Errors: INVALID_ARG, WORKSPACE, HIP. */
+ * Products are accumulated by the fp32 matrix cores over 32 values of k at a time and those
+ * partial sums are added in float64; the result is rounded to float32 once (after adding C when
+ * beta = 1, before the epilogue).  When m*n is small and k large the reduction is split over k
+ * into float64 partials in the workspace (device, 16-byte aligned, qha_dense_project_workspace
+ * bytes) and summed in a fixed order; results are deterministic.  beta is 0 or 1.
+ * Errors: INVALID_ARG, WORKSPACE, HIP. */
 int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k,
                       const float* a, int64_t lda, const float* b, int64_t ldb,
                       int32_t beta, float* c, int64_t ldc,

@@ -19,7 +19,24 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_halo_aggregation_amd.build` "
                       "(or __graft_entry__.build()); there is no CPU fallback")
 
+# libqha and torch must share one HIP runtime: torch ships its own libamdhip64 with the same soname,
+# so torch is loaded first and libqha's dependency then resolves to the runtime already in the process.
+import torch  # noqa: E402,F401
+
 _lib = C.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError(f"two HIP runtimes are loaded in this process ({_hip_runtimes()}); import torch before "
+                      "loading libqha so that both use the same one")
 
 QHA_OK, QHA_ERR_INVALID_ARG, QHA_ERR_UNSUPPORTED, QHA_ERR_HIP, QHA_ERR_WORKSPACE = range(5)
 NORM_GCN, NORM_MEAN = 0, 1

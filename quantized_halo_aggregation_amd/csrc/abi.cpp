@@ -86,7 +86,7 @@ void fill_plan_args(qha::GatherArgs& g, const qha_agg_plan* plan, int64_t n_rows
     g.split_row = nullptr;
     g.split_ptr = nullptr;
   }
-  g.partial = static_cast<float*>(ws);
+  g.partial = static_cast<double*>(ws);
 }
 
 }  // namespace
@@ -227,7 +227,7 @@ int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* 
 
 size_t qha_agg_workspace_bytes(const qha_agg_plan* plan, int32_t d) {
   if (!plan || d <= 0) return 0;
-  return static_cast<size_t>(plan->n_split_items) * static_cast<size_t>(d) * sizeof(float);
+  return static_cast<size_t>(plan->n_split_items) * static_cast<size_t>(d) * sizeof(double);
 }
 
 int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, void* stream) {
@@ -356,7 +356,7 @@ size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, 
   int32_t s;
   int64_t kps;
   qha::gemm_split_rule(m, n, k, &s, &kps);
-  return s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(m) * static_cast<size_t>(n) * sizeof(float) : 0;
+  return s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(m) * static_cast<size_t>(n) * sizeof(double) : 0;
 }
 
 int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, const float* a, int64_t lda,
@@ -399,11 +399,11 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
   g.ld_aux = ld_aux;
   g.epi = epilogue;
   qha::gemm_split_rule(m, n, k, &g.splits, &g.k_per_split);
-  g.ws = static_cast<float*>(workspace);
+  g.ws = static_cast<double*>(workspace);
   if (g.splits > 1) {
     const size_t need = qha_dense_project_workspace(trans_a, trans_b, m, n, k);
     if (!workspace || workspace_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-    if (!aligned4(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
+    if (!aligned16(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
   }
   return hip_status(qha::launch_gemm(g, static_cast<hipStream_t>(stream)), "dense_project");
 }

@@ -12,6 +12,10 @@
 // all issued before the first is consumed, so each wavefront keeps eight rows in flight.  For a
 // halo neighbour each lane fetches the one code word holding its features, shifts and masks its
 // codes out and dequantises in float32 (scale * q + min, no contraction) before the weighted add.
+// Accumulation is in float64: a float32 product w * x is exact in float64 and MI355X issues
+// float64 FMAs at the rate of unpacked float32 ones, so in this memory-bound loop the wider sum
+// costs no time and leaves the final rounding to float32 as the only error of the sum itself
+// (sums over hub rows and columns with cancellation would otherwise lose digits).
 // Heavy rows are split by the host-built plan; their slices write partial sums that a second
 // kernel adds in slice order, so results do not depend on scheduling.  Widths below 64 put several
 // items into one wavefront (d lanes each).
@@ -118,23 +122,23 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     e0 = cst(a.rowptr)[row];
     e1 = cst(a.rowptr)[row + 1];
   }
-  const float rs = a.rs ? cst(a.rs)[row] : 1.0f;
+  const double rs = a.rs ? static_cast<double>(cst(a.rs)[row]) : 1.0;
 
-  float acc[VEC];
+  double acc[VEC];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
 
   for (int32_t e = e0; e < e1; e += kBatch) {
     const int cnt = min(kBatch, e1 - e);
     int32_t u[kBatch];
-    float w[kBatch];
+    double w[kBatch];
     float xv[kBatch][VEC];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) u[i] = (i < cnt) ? cst(a.colidx)[e + i] : 0;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (i < cnt) {
-        w[i] = a.cs ? rs * cst(a.cs)[u[i]] : rs;
+        w[i] = a.cs ? rs * static_cast<double>(cst(a.cs)[u[i]]) : rs;
         if (HALO && u[i] >= a.n_inner) {
           load_halo<VEC>(a, static_cast<int64_t>(u[i]) - a.n_inner, j0, xv[i]);
         } else {
@@ -146,24 +150,29 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     for (int i = 0; i < kBatch; ++i) {
       if (i < cnt) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fmaf(w[i], xv[i][v], acc[v]);
+        for (int v = 0; v < VEC; ++v) acc[v] = fma(w[i], static_cast<double>(xv[i][v]), acc[v]);
       }
     }
   }
 
-  float* dst = split ? a.partial + item * D + j0 : a.out + row * a.ldo + j0;
-  if (!split && a.beta) {
+  if (split) {
+    double* p = a.partial + item * D + j0;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = dst[v] + acc[v];
+    for (int v = 0; v < VEC; ++v) p[v] = acc[v];
+    return;
   }
+  float* dst = a.out + row * a.ldo + j0;
+  float res[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
   if constexpr (VEC == 1) {
-    dst[0] = acc[0];
+    dst[0] = res[0];
   } else if constexpr (VEC == 2) {
-    *reinterpret_cast<float2*>(dst) = make_float2(acc[0], acc[1]);
+    *reinterpret_cast<float2*>(dst) = make_float2(res[0], res[1]);
   } else {
 #pragma unroll
     for (int q = 0; q < VEC / 4; ++q)
-      reinterpret_cast<float4*>(dst)[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      reinterpret_cast<float4*>(dst)[q] = make_float4(res[4 * q], res[4 * q + 1], res[4 * q + 2], res[4 * q + 3]);
   }
 }
 
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   const int64_t row = cst(a.split_row)[m];
   const int32_t i0 = cst(a.split_ptr)[m];
   const int32_t i1 = cst(a.split_ptr)[m + 1];
-  float acc[VEC];
+  double acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = a.partial[static_cast<int64_t>(i0) * D + j0 + v];
   for (int32_t i = i0 + 1; i < i1; ++i) {
@@ -191,7 +200,8 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   }
   float* dst = a.out + row * a.ldo + j0;
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) dst[v] = a.beta ? dst[v] + acc[v] : acc[v];
+  for (int v = 0; v < VEC; ++v)
+    dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
 }
 
 template <int D>

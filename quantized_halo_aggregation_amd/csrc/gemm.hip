@@ -4,15 +4,18 @@
 // Method: SYLVIE guide, section 2 (z_v = W a_v, h_v = sigma(z_v)) and section 7 (the weight
 // gradient sum_v (dL/dh_v * sigma'(z_v)) a_v^T).
 //
-// Mapping to gfx950: a 256-thread block owns a 128x128 tile of C; its four wavefronts own 64x64
-// quadrants, each held as 2x2 accumulators of v_mfma_f32_32x32x2f32 (64 fp32 accumulators per
-// lane).  K advances 16 at a time through LDS tiles that keep the operand's global layout
+// Mapping to gfx950: a 256-thread block owns a 64x128 tile of C; its four wavefronts own 32x64
+// pieces, each held as two v_mfma_f32_32x32x2f32 accumulators (32 fp32 per lane) plus their
+// float64 running sums.  K advances 32 at a time through LDS tiles that keep the operand's global layout
 // (k-contiguous tiles are read with 16-byte LDS reads, the others with 4-byte reads), padded so
 // neither the stores nor the fragment reads conflict on banks.  Within an 8-wide k slab, MFMA c
 // of a lane in half h consumes k = 4h + c, which lets a single 16-byte read feed four MFMAs.
-// The next tile's global loads are issued before the current tile is consumed.  Skinny
-// reductions (the weight gradient, k = node count) are split over k into fp32 partial tiles that
-// a second kernel sums in fixed order in float64.
+// The next tile's global loads are issued before the current tile is consumed.  Each 32-wide k
+// step accumulates into fresh fp32 MFMA accumulators that are then added into float64 running
+// sums, so a long dot product is rounded in float32 only over 32 terms at a time (for K = 512 this
+// keeps near-zero outputs of cancelling sums within 1e-6).  Skinny reductions (the weight
+// gradient, k = node count) are split over k into float64 partial tiles that a second kernel sums
+// in fixed order.
 #include "qha_internal.hpp"
 
 namespace qha {
@@ -20,10 +23,12 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;
+constexpr int BM = 64;
 constexpr int BN = 128;
-constexpr int BK = 16;
+constexpr int BK = 32;
 constexpr int PAD = 4;
+constexpr int A_LOADS = BM * BK / 4 / 256;   // float4 loads per thread per k step
+constexpr int B_LOADS = BN * BK / 4 / 256;
 
 template <bool TA, bool TB, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
@@ -35,8 +40,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int wm = wid >> 1;
-  const int wn = wid & 1;
+  const int wm = wid >> 1;        // 32-row half of the block tile
+  const int wn = wid & 1;         // 64-column half
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
@@ -44,86 +49,86 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * p.k_per_split;
   const int64_t kend = min(p.k, kbeg + p.k_per_split);
 
-  floatx16 acc[2][2];
+  double sum[2][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) sum[j][r] = 0.0;
 
-  float4 ra[2], rb[2];
+  float4 ra[A_LOADS], rb[B_LOADS];
   const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
-  // global -> registers for the tile starting at k0 (two float4 of A and of B per thread)
+  // global -> registers for the tile starting at k0
   auto load_tiles = [&](int64_t k0) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < A_LOADS; ++s) {
       const int f = tid + 256 * s;
-      // ---- A ----
-      {
-        int64_t gr, gc;     // storage row / column of the float4's first element
-        bool ok;
-        if (!TA) {          // A stored [m][k]: tile rows m0.., cols k0..
-          const int row = f >> 2, kq = f & 3;
-          gr = m0 + row;
-          gc = k0 + 4 * kq;
-          ok = gr < p.m && gc < kend;
-        } else {            // A stored [k][m]
-          const int kr = f >> 5, mq = f & 31;
-          gr = k0 + kr;
-          gc = m0 + 4 * mq;
-          ok = gr < kend && gc < p.m;
-        }
-        float4 v = zero4;
-        if (ok) {
-          v = *reinterpret_cast<const float4*>(p.a + gr * p.lda + gc);
-          if (MASK) {
-            const float4 x = *reinterpret_cast<const float4*>(p.aux + gr * p.ld_aux + gc);
-            v.x = x.x > 0.0f ? v.x : 0.0f;
-            v.y = x.y > 0.0f ? v.y : 0.0f;
-            v.z = x.z > 0.0f ? v.z : 0.0f;
-            v.w = x.w > 0.0f ? v.w : 0.0f;
-          }
-        }
-        ra[s] = v;
+      int64_t gr, gc;     // storage row / column of the float4's first element
+      bool ok;
+      if (!TA) {          // A stored [m][k]
+        const int row = f / (BK / 4), kq = f % (BK / 4);
+        gr = m0 + row;
+        gc = k0 + 4 * kq;
+        ok = gr < p.m && gc < kend;
+      } else {            // A stored [k][m]
+        const int kr = f / (BM / 4), mq = f % (BM / 4);
+        gr = k0 + kr;
+        gc = m0 + 4 * mq;
+        ok = gr < kend && gc < p.m;
       }
-      // ---- B ----
-      {
-        int64_t gr, gc;
-        bool ok;
-        if (TB) {           // B stored [n][k]
-          const int row = f >> 2, kq = f & 3;
-          gr = n0 + row;
-          gc = k0 + 4 * kq;
-          ok = gr < p.n && gc < kend;
-        } else {            // B stored [k][n]
-          const int kr = f >> 5, nq = f & 31;
-          gr = k0 + kr;
-          gc = n0 + 4 * nq;
-          ok = gr < kend && gc < p.n;
+      float4 v = zero4;
+      if (ok) {
+        v = *reinterpret_cast<const float4*>(p.a + gr * p.lda + gc);
+        if (MASK) {
+          const float4 x = *reinterpret_cast<const float4*>(p.aux + gr * p.ld_aux + gc);
+          v.x = x.x > 0.0f ? v.x : 0.0f;
+          v.y = x.y > 0.0f ? v.y : 0.0f;
+          v.z = x.z > 0.0f ? v.z : 0.0f;
+          v.w = x.w > 0.0f ? v.w : 0.0f;
         }
-        rb[s] = ok ? *reinterpret_cast<const float4*>(p.b + gr * p.ldb + gc) : zero4;
       }
+      ra[s] = v;
+    }
+#pragma unroll
+    for (int s = 0; s < B_LOADS; ++s) {
+      const int f = tid + 256 * s;
+      int64_t gr, gc;
+      bool ok;
+      if (TB) {           // B stored [n][k]
+        const int row = f / (BK / 4), kq = f % (BK / 4);
+        gr = n0 + row;
+        gc = k0 + 4 * kq;
+        ok = gr < p.n && gc < kend;
+      } else {            // B stored [k][n]
+        const int kr = f / (BN / 4), nq = f % (BN / 4);
+        gr = k0 + kr;
+        gc = n0 + 4 * nq;
+        ok = gr < kend && gc < p.n;
+      }
+      rb[s] = ok ? *reinterpret_cast<const float4*>(p.b + gr * p.ldb + gc) : zero4;
     }
   };
 
   auto store_tiles = [&]() {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < A_LOADS; ++s) {
       const int f = tid + 256 * s;
       if (!TA) {
-        const int row = f >> 2, kq = f & 3;
+        const int row = f / (BK / 4), kq = f % (BK / 4);
         *reinterpret_cast<float4*>(&As[row * (BK + PAD) + 4 * kq]) = ra[s];
       } else {
-        const int kr = f >> 5, mq = f & 31;
+        const int kr = f / (BM / 4), mq = f % (BM / 4);
         *reinterpret_cast<float4*>(&As[kr * (BM + PAD) + 4 * mq]) = ra[s];
       }
+    }
+#pragma unroll
+    for (int s = 0; s < B_LOADS; ++s) {
+      const int f = tid + 256 * s;
       if (TB) {
-        const int row = f >> 2, kq = f & 3;
+        const int row = f / (BK / 4), kq = f % (BK / 4);
         *reinterpret_cast<float4*>(&Bs[row * (BK + PAD) + 4 * kq]) = rb[s];
       } else {
-        const int kr = f >> 5, nq = f & 31;
+        const int kr = f / (BN / 4), nq = f % (BN / 4);
         *reinterpret_cast<float4*>(&Bs[kr * (BN + PAD) + 4 * nq]) = rb[s];
       }
     }
@@ -137,20 +142,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
     if (more) load_tiles(k0 + BK);
+    floatx16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 #pragma unroll
     for (int slab = 0; slab < BK / 8; ++slab) {
       const int kk = slab * 8 + 4 * h;
-      float af[2][4], bf[2][4];
+      float af[4], bf[2][4];
+      const int row = wm * 32 + l32;
+      if (!TA) {
+        const float4 t = *reinterpret_cast<const float4*>(&As[row * (BK + PAD) + kk]);
+        af[0] = t.x; af[1] = t.y; af[2] = t.z; af[3] = t.w;
+      } else {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int row = wm * 64 + mi * 32 + l32;
-        if (!TA) {
-          const float4 t = *reinterpret_cast<const float4*>(&As[row * (BK + PAD) + kk]);
-          af[mi][0] = t.x; af[mi][1] = t.y; af[mi][2] = t.z; af[mi][3] = t.w;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) af[mi][c] = As[(kk + c) * (BM + PAD) + row];
-        }
+        for (int c = 0; c < 4; ++c) af[c] = As[(kk + c) * (BM + PAD) + row];
       }
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
@@ -166,11 +173,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mi][c], bf[ni][c], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < 2; ++ni)
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[c], bf[ni][c], acc[ni], 0, 0, 0);
     }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum[ni][r] += static_cast<double>(acc[ni][r]);
     __syncthreads();
     if (more) {
       store_tiles();
@@ -180,25 +189,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
   // accumulator element r of lane (h, l32) is C[8*(r/4) + 4*h + r%4][l32] of the 32x32 block
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t grow = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int64_t gcol = n0 + wn * 64 + ni * 32 + l32;
-        if (grow < p.m && gcol < p.n) {
-          float v = acc[mi][ni][r];
-          if (SPLIT) {
-            p.ws[static_cast<int64_t>(blockIdx.z) * p.m * p.n + grow * p.n + gcol] = v;
-          } else {
-            float* dst = p.c + grow * p.ldc + gcol;
-            if (p.beta) v = *dst + v;
-            if (p.epi == 1) v = v > 0.0f ? v : 0.0f;
-            *dst = v;
-          }
+    for (int r = 0; r < 16; ++r) {
+      const int64_t grow = m0 + wm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t gcol = n0 + wn * 64 + ni * 32 + l32;
+      if (grow < p.m && gcol < p.n) {
+        const double s = sum[ni][r];
+        if (SPLIT) {
+          p.ws[static_cast<int64_t>(blockIdx.z) * p.m * p.n + grow * p.n + gcol] = s;
+        } else {
+          float* dst = p.c + grow * p.ldc + gcol;
+          float v = static_cast<float>(p.beta ? static_cast<double>(*dst) + s : s);
+          if (p.epi == 1) v = v > 0.0f ? v : 0.0f;
+          *dst = v;
         }
       }
+    }
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
@@ -206,11 +213,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   const int64_t mn = p.m * p.n;
   if (idx >= mn) return;
   double s = 0.0;
-  for (int z = 0; z < p.splits; ++z) s += static_cast<double>(p.ws[z * mn + idx]);
+  for (int z = 0; z < p.splits; ++z) s += p.ws[z * mn + idx];
   const int64_t i = idx / p.n, j = idx % p.n;
   float* dst = p.c + i * p.ldc + j;
-  float v = static_cast<float>(s);
-  if (p.beta) v = *dst + v;
+  float v = static_cast<float>(p.beta ? static_cast<double>(*dst) + s : s);
   if (p.epi == 1) v = v > 0.0f ? v : 0.0f;
   *dst = v;
 }

@@ -53,7 +53,7 @@ struct GatherArgs {
   int32_t beta;
   float* out;
   int64_t ldo;
-  float* partial;  // [n_split_items, d] partial sums of split rows
+  double* partial;  // [n_split_items, d] float64 partial sums of split rows
 };
 
 struct GemmArgs {
@@ -70,7 +70,7 @@ struct GemmArgs {
   const float* aux;
   int64_t ld_aux;
   int32_t epi;
-  float* ws;           // split-k partials [splits, m, n]
+  double* ws;          // float64 split-k partials [splits, m, n]
   int32_t splits;
   int64_t k_per_split;
 };

@@ -98,7 +98,7 @@ def test_agg_plan_covers_every_edge_once(skip_empty):
     assert list(split_ptr) == [0, 3, 5, 9]
     rows_with_items = set(item_row.tolist())
     assert (0 in rows_with_items) == (not skip_empty)
-    assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 4
+    assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 8
 
 
 def test_device_calls_reject_bad_arguments_before_any_hip_call():

@@ -60,7 +60,7 @@ def test_quantize_pack_bit_exact(d, n):
     codes = torch.full((max(total, 1),), -1, dtype=torch.int32, device="cuda")
     sc = torch.empty(n, dtype=torch.float32, device="cuda")
     z = torch.empty(n, dtype=torch.float32, device="cuda")
-    x_dev = H.dev(big)
+    x_dev = H.dev(big)[:, :d]          # rows of d features, leading dimension ld
     B.quantize_pack(x_dev, H.dev(row_index), n, H.dev(bits), H.dev(off_d.view(np.int32)), SEED, epoch, stream_id,
                     node_base, codes, sc, z)
     H.assert_bits_equal(H.host(codes)[:total].view(np.uint32), words, "codes")
@@ -70,7 +70,7 @@ def test_quantize_pack_bit_exact(d, n):
     # without a row index the rows are read in order
     direct = np.ascontiguousarray(big[row_index])
     codes2 = torch.full_like(codes, -1)
-    B.quantize_pack(H.dev(direct), None, n, H.dev(bits), H.dev(off_d.view(np.int32)), SEED, epoch, stream_id,
+    B.quantize_pack(H.dev(direct)[:, :d], None, n, H.dev(bits), H.dev(off_d.view(np.int32)), SEED, epoch, stream_id,
                     node_base, codes2, sc, z)
     H.assert_bits_equal(H.host(codes2)[:total].view(np.uint32), words, "codes (direct)")
 
