@@ -58,7 +58,7 @@ extern "C" {
 #define QHA_EPI_NONE 0
 #define QHA_EPI_RELU 1          /* c = c > 0 ? c : +0 */
 
-/* largest number of edges one wavefront walks for one row in an aggregation plan */
+/* largest number of edges of one row that one wavefront walks (longer rows are split) */
 #define QHA_DEFAULT_CHUNK 512
 
 int qha_abi_version(void);
@@ -92,33 +92,40 @@ int qha_validate_csr(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, cons
 int qha_csr_transpose(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, const int32_t* colidx,
                       int32_t* colptr, int32_t* rowidx);
 
-/* Work plan of an aggregation over a CSR (host construction, device use).  One work item is one
- * wavefront walking at most `chunk` edges of one row, so a heavy row of a power-law graph is
- * spread over several wavefronts; items of split rows come first (they write partial sums to the
- * workspace, combined afterwards in chunk order, which keeps results deterministic), then one
- * item per remaining row.  If skip_empty is set, rows with no edges get no item: valid only
- * with beta = 1, where such rows are left as they are.
- * qha_agg_plan_size fills the counts; the caller then allocates the four device arrays, calls
+/* Work plan of an aggregation over a CSR (host construction, device use).  Work is cut into items,
+ * one wavefront each.  A row longer than `chunk` edges is split into chunks of at most `chunk`
+ * edges, one item each; these items come first and write float64 partial sums to the workspace,
+ * which a second kernel adds in chunk order (results stay deterministic).  Every other row joins a
+ * group of up to QHA_GROUP_ROWS consecutive rows holding at most `group_edges` edges together (a
+ * row longer than that forms a group of its own), so a wavefront streams through the contiguous
+ * edge list of several short rows of a power-law graph without per-row start-up latency.  A row
+ * with no edges is an item of its own, or, if skip_empty is set, belongs to no item and is left
+ * as it is (valid only with beta = 1).
+ * qha_agg_plan_size fills the counts; the caller allocates the device arrays, calls
  * qha_agg_plan_fill with host staging buffers of the same sizes, and copies them to the device. */
+#define QHA_GROUP_ROWS 15
+#define QHA_DEFAULT_GROUP_EDGES 256
+
 typedef struct qha_agg_plan {
   int64_t n_rows;          /* rows of the CSR the plan was built for */
-  int32_t chunk;           /* edge budget of one item */
-  int32_t skip_empty;      /* 1 if rows without edges have no item */
-  int64_t n_items;         /* items in item_row */
-  int64_t n_split_items;   /* leading items that belong to split rows (= partial-sum slots) */
-  int64_t n_split_rows;    /* rows split into more than one item */
-  const int32_t* item_row;    /* device [n_items]: CSR row of each item */
-  const int32_t* item_chunk;  /* device [n_split_items]: chunk index of each split item */
+  int32_t chunk;           /* edge budget of one chunk of a split row */
+  int32_t group_edges;     /* edge budget of a group of whole rows */
+  int32_t skip_empty;      /* 1 if rows without edges belong to no item */
+  int32_t reserved;
+  int64_t n_items;         /* items */
+  int64_t n_split_items;   /* leading items that are chunks of split rows (= partial-sum slots) */
+  int64_t n_split_rows;    /* rows split into chunks */
+  const int32_t* items;       /* device int32[4 * n_items]: first row, row count, first edge, end edge */
   const int32_t* split_row;   /* device [n_split_rows]: the split rows */
   const int32_t* split_ptr;   /* device [n_split_rows + 1]: item range of each split row */
 } qha_agg_plan;
 
-int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int32_t skip_empty,
-                      qha_agg_plan* plan);
-int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* item_row,
-                      int32_t* item_chunk, int32_t* split_row, int32_t* split_ptr);
+int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int32_t group_edges,
+                      int32_t skip_empty, qha_agg_plan* plan);
+int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* items,
+                      int32_t* split_row, int32_t* split_ptr);
 /* Bytes of workspace an aggregation with this plan and width needs: one float64 partial row per
- * split item (0 without split rows). */
+ * chunk of a split row (0 without split rows). */
 size_t qha_agg_workspace_bytes(const qha_agg_plan* plan, int32_t d);
 
 /* ------------------------------------------------------------------------------------------
@@ -139,46 +146,51 @@ int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, voi
  * Row r reads x[(row_index ? row_index[r] : r) * ldx + j], j < d (device).  Its stochastic
  * rounding draws come from Philox4x32-10 with counter (node_base + r, j / 8, epoch, stream_id)
  * and key `seed`, so a call is reproducible from its arguments alone.  Writes the packed row at
- * codes[word_offset[r] ...] (layout of qha_pack_layout), scale[r] and zero_point[r] (device).
- * Floating-point steps (all float32, round-to-nearest, no contraction): mn/mx exact; zero_point
+ * codes[word_offset[r] ...] (layout of qha_pack_layout) and the row's metadata pair
+ * meta[2r] = min (the zero-point), meta[2r + 1] = scale (device; min first, then scale, the
+ * order in which they travel with the codes).
+ * Floating-point steps (all float32, round-to-nearest, no contraction): mn/mx exact; zero-point
  * = mn + 0; range = mx - mn; inv = L / range; range == 0 or inv infinite -> scale 0 and codes 0;
  * else scale = range / L, y = (x - mn) * inv, q = min(floor(y) + (u16 < frac(y) * 65536), L)
- * with u16 the element's 16-bit draw.  For b = 32, codes hold the raw bits and scale = zp = 0.
+ * with u16 the element's 16-bit draw.  For b = 32, codes hold the raw bits and min = scale = 0.
  * A row whose bits[r] is not in {1,2,4,8,32} is skipped (nothing written).
  * Errors: INVALID_ARG (nulls, n_rows < 0, ldx < d or not a multiple of 4, misalignment),
  * UNSUPPORTED (d), HIP.  n_rows == 0 is a no-op. */
 int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int64_t n_rows,
                       int32_t d, const uint8_t* bits, const uint32_t* word_offset,
                       uint64_t seed, uint32_t epoch, uint32_t stream_id, uint32_t node_base,
-                      uint32_t* codes, float* scale, float* zero_point, void* stream);
+                      uint32_t* codes, float* meta, void* stream);
 
 /* Dequantisation fused into the normalised neighbour aggregation (guide sections 2 and 6, the
  * receiver's "dequantize, then aggregate(local_h, remote_h)" of section 11).  For each CSR row
- * v < n_rows (device rowptr[n_rows+1], colidx[nnz]):
- *   out[v] = (beta ? out[v] : 0) + sum over e in row v of (r[v] * c[u]) * x~_u,  u = colidx[e]
- *   x~_u = x_inner[u * ldx + j]                         if u < n_inner
- *        = scale[k] * q_k[j] + zero_point[k]  (fp32)     if u = n_inner + k, k < n_halo
- * (raw float when bits[k] == 32).  r (device float[n_rows]) and c (device float[n_inner+n_halo])
- * may be NULL for 1.0.  codes/word_offset/bits/scale/zero_point are the received halo messages
- * in qha_quantize_pack's layout (device; may be NULL when n_halo == 0).  plan may be NULL (one
- * wavefront per row); otherwise it must have been built for this rowptr, and a plan with
- * skip_empty requires beta == 1.  workspace (device) must hold qha_agg_workspace_bytes(plan, d)
- * bytes.  beta is 0 or 1.  Products and sums are accumulated in float64 along each row's edges in
- * order (chunks of a split row are summed separately, then added in chunk order) and rounded to
- * float32 once, after adding the old value when beta = 1; results are deterministic.
+ * i < n_rows (device rowptr[n_rows+1], colidx[nnz]) and its output row v = row_ids ? row_ids[i] : i:
+ *   out[v] = (beta ? out[v] : 0) + r[i] * sum over e in row i of c[u] * x~_u,   u = colidx[e]
+ *   x~_u = x_inner[u * ldx + j]                                if u < n_inner
+ *        = meta[2k + 1] * q_k[j] + meta[2k]  (float32)          if u = n_inner + k, k < n_halo
+ * (the raw float when bits[k] == 32).  r (device float[n_rows]) and c (device
+ * float[n_inner + n_halo]) may be NULL for 1.0; for the GCN weight 1/sqrt(d_v d_u) pass
+ * r = c = qha_degree_norm(.., QHA_NORM_GCN).  codes/word_offset/bits/meta are the received halo
+ * messages in qha_quantize_pack's layout (device; may be NULL when n_halo == 0).  row_ids
+ * (device, nullable) must be distinct.  plan may be NULL (one item per row); otherwise it must
+ * have been built for this rowptr, and a plan with skip_empty requires beta == 1.  workspace
+ * (device, 16-byte aligned) must hold qha_agg_workspace_bytes(plan, d) bytes.  beta is 0 or 1.
+ * Each product c[u] * x~_u (exact in float64) is summed in float64 in edge order (chunks of a
+ * split row separately, then in chunk order), scaled by r[i], added to the old value when
+ * beta = 1 and rounded to float32 once; results are deterministic.
  * Errors: INVALID_ARG, UNSUPPORTED (d), WORKSPACE, HIP. */
 int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
-                              const qha_agg_plan* plan, const float* r, const float* c,
+                              const int32_t* row_ids, const qha_agg_plan* plan,
+                              const float* r, const float* c,
                               const float* x_inner, int64_t ldx, int64_t n_inner,
                               const uint32_t* codes, const uint32_t* word_offset,
-                              const uint8_t* bits, const float* scale, const float* zero_point,
-                              int64_t n_halo, int32_t d, int32_t beta, float* out, int64_t ldo,
+                              const uint8_t* bits, const float* meta, int64_t n_halo,
+                              int32_t d, int32_t beta, float* out, int64_t ldo,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Transposed aggregation for embedding gradients (guide sections 3 and 11: gradients flow back
  * along the same cross-partition dependencies).  Given the transpose of the forward CSR
  * (qha_csr_transpose: row u lists the forward rows v that gather u), for u < n_rows:
- *   grad_in[u] = (beta ? grad_in[u] : 0) + sum over e in row u of (r[u] * c[v]) * grad_out[v]
+ *   grad_in[u] = (beta ? grad_in[u] : 0) + r[u] * sum over e in row u of c[v] * grad_out[v]
  * with v = rowidx[e] < n_grad_rows.  With r and c the forward's c and r this is the adjoint of
  * qha_dequant_aggregate_fwd.  Same plan / workspace / beta / determinism rules.  Pass a row
  * range [u0, u1) by offsetting colptr, r and grad_in. */

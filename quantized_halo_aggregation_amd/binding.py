@@ -43,14 +43,16 @@ NORM_GCN, NORM_MEAN = 0, 1
 PRO_NONE, PRO_RELU_MASK = 0, 1
 EPI_NONE, EPI_RELU = 0, 1
 DEFAULT_CHUNK = 512
+DEFAULT_GROUP_EDGES = 256
+GROUP_ROWS = 15
 
 _i32, _i64, _u32, _u64, _sz, _vp = C.c_int32, C.c_int64, C.c_uint32, C.c_uint64, C.c_size_t, C.c_void_p
 
 
 class AggPlanStruct(C.Structure):
-    _fields_ = [("n_rows", _i64), ("chunk", _i32), ("skip_empty", _i32), ("n_items", _i64),
-                ("n_split_items", _i64), ("n_split_rows", _i64), ("item_row", _vp), ("item_chunk", _vp),
-                ("split_row", _vp), ("split_ptr", _vp)]
+    _fields_ = [("n_rows", _i64), ("chunk", _i32), ("group_edges", _i32), ("skip_empty", _i32),
+                ("reserved", _i32), ("n_items", _i64), ("n_split_items", _i64), ("n_split_rows", _i64),
+                ("items", _vp), ("split_row", _vp), ("split_ptr", _vp)]
 
 
 def _sig(name, res, *args):
@@ -67,14 +69,14 @@ _last_error = _sig("qha_last_error", C.c_char_p)
 _pack_layout = _sig("qha_pack_layout", _i32, _vp, _i64, _i32, _vp, _P(_u64))
 _validate_csr = _sig("qha_validate_csr", _i32, _i64, _i64, _vp, _vp, _i32)
 _csr_transpose = _sig("qha_csr_transpose", _i32, _i64, _i64, _vp, _vp, _vp, _vp)
-_plan_size = _sig("qha_agg_plan_size", _i32, _i64, _vp, _i32, _i32, _P(AggPlanStruct))
-_plan_fill = _sig("qha_agg_plan_fill", _i32, _vp, _P(AggPlanStruct), _vp, _vp, _vp, _vp)
+_plan_size = _sig("qha_agg_plan_size", _i32, _i64, _vp, _i32, _i32, _i32, _P(AggPlanStruct))
+_plan_fill = _sig("qha_agg_plan_fill", _i32, _vp, _P(AggPlanStruct), _vp, _vp, _vp)
 _plan_ws = _sig("qha_agg_workspace_bytes", _sz, _P(AggPlanStruct), _i32)
 _degree_norm = _sig("qha_degree_norm", _i32, _vp, _i64, _i32, _vp, _vp)
 _quantize_pack = _sig("qha_quantize_pack", _i32, _vp, _i64, _vp, _i64, _i32, _vp, _vp, _u64, _u32, _u32, _u32,
-                      _vp, _vp, _vp, _vp)
-_dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp, _P(AggPlanStruct), _vp, _vp,
-                              _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
+                      _vp, _vp, _vp)
+_dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _vp,
+                              _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
 _aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _P(AggPlanStruct), _vp, _vp, _vp, _i64, _i64,
                       _i32, _i32, _vp, _i64, _vp, _sz, _vp)
 _dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
@@ -188,23 +190,23 @@ def csr_transpose(rowptr, colidx, n_cols: int):
 class AggPlan:
     """A work plan for one CSR (host arrays built by the library, kept on the device)."""
 
-    def __init__(self, rowptr, chunk: int = DEFAULT_CHUNK, skip_empty: bool = False, device="cuda"):
+    def __init__(self, rowptr, chunk: int = DEFAULT_CHUNK, group_edges: int = DEFAULT_GROUP_EDGES,
+                 skip_empty: bool = False, device="cuda"):
         import torch
         rowptr, pr = _host(rowptr, np.int32, "rowptr")
         st = AggPlanStruct()
-        _check(_plan_size(rowptr.size - 1, pr, int(chunk), int(skip_empty), C.byref(st)), "qha_agg_plan_size")
-        item_row = np.empty(max(st.n_items, 1), np.int32)
-        item_chunk = np.empty(max(st.n_split_items, 1), np.int32)
-        split_row = np.empty(max(st.n_split_rows, 1), np.int32)
-        split_ptr = np.empty(st.n_split_rows + 1, np.int32)
-        _check(_plan_fill(pr, C.byref(st), item_row.ctypes.data, item_chunk.ctypes.data, split_row.ctypes.data,
-                          split_ptr.ctypes.data), "qha_agg_plan_fill")
-        self.host = {"item_row": item_row[:st.n_items], "item_chunk": item_chunk[:st.n_split_items],
-                     "split_row": split_row[:st.n_split_rows], "split_ptr": split_ptr}
-        self.dev = {k: torch.from_numpy(np.ascontiguousarray(v if v.size else np.zeros(1, np.int32))).to(device)
-                    for k, v in self.host.items()}
-        st.item_row = self.dev["item_row"].data_ptr()
-        st.item_chunk = self.dev["item_chunk"].data_ptr()
+        _check(_plan_size(rowptr.size - 1, pr, int(chunk), int(group_edges), int(skip_empty), C.byref(st)),
+               "qha_agg_plan_size")
+        items = np.zeros(4 * max(st.n_items, 1), np.int32)
+        split_row = np.zeros(max(st.n_split_rows, 1), np.int32)
+        split_ptr = np.zeros(st.n_split_rows + 1, np.int32)
+        _check(_plan_fill(pr, C.byref(st), items.ctypes.data, split_row.ctypes.data, split_ptr.ctypes.data),
+               "qha_agg_plan_fill")
+        self.host = {"items": items[:4 * st.n_items].reshape(-1, 4), "split_row": split_row[:st.n_split_rows],
+                     "split_ptr": split_ptr}
+        self.dev = {"items": torch.from_numpy(items).to(device), "split_row": torch.from_numpy(split_row).to(device),
+                    "split_ptr": torch.from_numpy(split_ptr).to(device)}
+        st.items = self.dev["items"].data_ptr()
         st.split_row = self.dev["split_row"].data_ptr()
         st.split_ptr = self.dev["split_ptr"].data_ptr()
         self.struct = st
@@ -240,19 +242,20 @@ def degree_norm(deg, kind: int, out, stream=None):
 
 
 def quantize_pack(x, row_index, n_rows: int, bits, word_offset, seed: int, epoch: int, stream_id: int,
-                  node_base: int, codes, scale, zero_point, stream=None):
+                  node_base: int, codes, meta, stream=None):
+    """meta receives (min, scale) per row: a float32 tensor of n_rows * 2 elements."""
     import torch
     px, ldx = _rows(x, "x")
     d = x.shape[1]
     _check(_quantize_pack(px, ldx, _dev(row_index, torch.int32, "row_index", allow_none=True), int(n_rows), int(d),
                           _dev(bits, torch.uint8, "bits"), _dev32(word_offset, "word_offset"),
                           int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch), int(stream_id), int(node_base),
-                          _dev32(codes, "codes"), _dev(scale, torch.float32, "scale"),
-                          _dev(zero_point, torch.float32, "zero_point"), _stream(stream)), "qha_quantize_pack")
+                          _dev32(codes, "codes"), _dev(meta, torch.float32, "meta"), _stream(stream)),
+           "qha_quantize_pack")
 
 
-def dequant_aggregate_fwd(rowptr, colidx, plan, r, c, x_inner, n_inner: int, codes, word_offset, bits, scale,
-                          zero_point, n_halo: int, beta: int, out, workspace=None, n_rows=None, stream=None):
+def dequant_aggregate_fwd(rowptr, colidx, plan, r, c, x_inner, n_inner: int, codes, word_offset, bits, meta,
+                          n_halo: int, beta: int, out, workspace=None, row_ids=None, n_rows=None, stream=None):
     import torch
     n_rows = rowptr.numel() - 1 if n_rows is None else int(n_rows)
     px, ldx = _rows(x_inner, "x_inner")
@@ -262,14 +265,14 @@ def dequant_aggregate_fwd(rowptr, colidx, plan, r, c, x_inner, n_inner: int, cod
     ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_dequant_aggregate_fwd(
-        n_rows, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"), _plan_ref(plan),
+        n_rows, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"),
+        _dev(row_ids, torch.int32, "row_ids", allow_none=True), _plan_ref(plan),
         _dev(r, torch.float32, "r", allow_none=True), _dev(c, torch.float32, "c", allow_none=True),
         px, ldx, int(n_inner),
         _dev32(codes, "codes") if halo else None,
         _dev32(word_offset, "word_offset") if halo else None,
         _dev(bits, torch.uint8, "bits") if halo else None,
-        _dev(scale, torch.float32, "scale") if halo else None,
-        _dev(zero_point, torch.float32, "zero_point") if halo else None,
+        _dev(meta, torch.float32, "meta") if halo else None,
         int(n_halo), int(d), int(beta), po, ldo, ws_ptr, ws_bytes, _stream(stream)), "qha_dequant_aggregate_fwd")
 
 

@@ -38,6 +38,7 @@ bool width_supported(int32_t d) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 constexpr int64_t kMaxIndex = 2147483647LL;
 
@@ -51,11 +52,11 @@ int check_rows(const char* name, const float* p, int64_t ld, int32_t d) {
 int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d, const void* ws, size_t ws_bytes) {
   if (!plan) return QHA_OK;
   if (plan->n_rows != n_rows) return fail(QHA_ERR_INVALID_ARG, "plan was built for %lld rows, call has %lld", (long long)plan->n_rows, (long long)n_rows);
-  if (plan->chunk <= 0) return fail(QHA_ERR_INVALID_ARG, "plan chunk must be positive");
+  if (plan->chunk <= 0 || plan->group_edges <= 0) return fail(QHA_ERR_INVALID_ARG, "plan budgets must be positive");
   if (plan->n_items < 0 || plan->n_split_items < 0 || plan->n_split_rows < 0 || plan->n_split_items > plan->n_items)
     return fail(QHA_ERR_INVALID_ARG, "plan counts are inconsistent");
-  if (plan->n_items > 0 && !plan->item_row) return fail(QHA_ERR_INVALID_ARG, "plan item_row is NULL");
-  if (plan->n_split_items > 0 && (!plan->item_chunk || !plan->split_row || !plan->split_ptr))
+  if (plan->n_items > 0 && !plan->items) return fail(QHA_ERR_INVALID_ARG, "plan items is NULL");
+  if (plan->n_split_rows > 0 && (!plan->split_row || !plan->split_ptr))
     return fail(QHA_ERR_INVALID_ARG, "plan split arrays are NULL");
   if (plan->skip_empty && beta != 1) return fail(QHA_ERR_INVALID_ARG, "a plan that skips empty rows needs beta = 1");
   const size_t need = qha_agg_workspace_bytes(plan, d);
@@ -70,23 +71,80 @@ void fill_plan_args(qha::GatherArgs& g, const qha_agg_plan* plan, int64_t n_rows
   if (plan) {
     g.n_items = plan->n_items;
     g.n_split_items = plan->n_split_items;
-    g.chunk = plan->chunk;
-    g.item_row = plan->item_row;
-    g.item_chunk = plan->item_chunk;
+    g.items = plan->items;
     g.n_split_rows = plan->n_split_rows;
     g.split_row = plan->split_row;
     g.split_ptr = plan->split_ptr;
   } else {
     g.n_items = n_rows;
     g.n_split_items = 0;
-    g.chunk = 0;
-    g.item_row = nullptr;
-    g.item_chunk = nullptr;
+    g.items = nullptr;
     g.n_split_rows = 0;
     g.split_row = nullptr;
     g.split_ptr = nullptr;
   }
   g.partial = static_cast<double*>(ws);
+}
+
+// Walks the rows once and either counts (out == nullptr) or writes the plan's arrays.
+struct PlanWalk {
+  int64_t items = 0, split_items = 0, split_rows = 0;
+};
+
+int walk_plan(const int32_t* rowptr, int64_t n_rows, int32_t chunk, int32_t group_edges, int32_t skip_empty,
+              PlanWalk* cnt, int32_t* items, int32_t* split_row, int32_t* split_ptr) {
+  PlanWalk w;
+  auto emit = [&](int64_t r0, int64_t nr, int64_t e0, int64_t e1) {
+    if (items) {
+      int32_t* it = items + 4 * w.items;
+      it[0] = static_cast<int32_t>(r0);
+      it[1] = static_cast<int32_t>(nr);
+      it[2] = static_cast<int32_t>(e0);
+      it[3] = static_cast<int32_t>(e1);
+    }
+    ++w.items;
+  };
+  // chunks of split rows first: their items carry the longest work
+  if (split_ptr) split_ptr[0] = 0;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t b = rowptr[r], e = rowptr[r + 1];
+    if (e < b) return fail(QHA_ERR_INVALID_ARG, "rowptr decreases at row %lld", (long long)r);
+    if (e - b > chunk) {
+      for (int64_t c = b; c < e; c += chunk) emit(r, 1, c, c + chunk < e ? c + chunk : e);
+      if (split_row) split_row[w.split_rows] = static_cast<int32_t>(r);
+      ++w.split_rows;
+      if (split_ptr) split_ptr[w.split_rows] = static_cast<int32_t>(w.items);
+    }
+  }
+  w.split_items = w.items;
+  // groups of consecutive rows
+  int64_t g0 = -1, gn = 0, ge = 0;
+  auto close = [&]() {
+    if (gn > 0) emit(g0, gn, rowptr[g0], rowptr[g0 + gn]);
+    g0 = -1;
+    gn = 0;
+    ge = 0;
+  };
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
+    if (len > chunk) {
+      close();
+      continue;
+    }
+    if (len == 0) {            // never inside a group: each edge then closes at most one row
+      close();
+      if (!skip_empty) emit(r, 1, rowptr[r], rowptr[r]);
+      continue;
+    }
+    if (gn > 0 && (gn >= QHA_GROUP_ROWS || ge + len > group_edges)) close();
+    if (gn == 0) g0 = r;
+    ++gn;
+    ge += len;
+  }
+  close();
+  if (w.items > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "too many work items");
+  *cnt = w;
+  return QHA_OK;
 }
 
 }  // namespace
@@ -162,66 +220,36 @@ int qha_csr_transpose(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, con
   return ok();
 }
 
-int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int32_t skip_empty, qha_agg_plan* plan) {
+int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int32_t group_edges, int32_t skip_empty,
+                      qha_agg_plan* plan) {
   if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
   if (!rowptr || !plan) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
-  if (chunk <= 0) return fail(QHA_ERR_INVALID_ARG, "chunk must be positive");
-  int64_t items = 0, split_items = 0, split_rows = 0;
-  for (int64_t r = 0; r < n_rows; ++r) {
-    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
-    if (len < 0) return fail(QHA_ERR_INVALID_ARG, "rowptr decreases at row %lld", (long long)r);
-    if (len == 0) {
-      if (!skip_empty) ++items;
-      continue;
-    }
-    const int64_t c = (len + chunk - 1) / chunk;
-    items += c;
-    if (c > 1) {
-      split_items += c;
-      ++split_rows;
-    }
-  }
-  if (items > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "too many work items");
+  if (chunk <= 0 || group_edges <= 0) return fail(QHA_ERR_INVALID_ARG, "chunk and group_edges must be positive");
+  PlanWalk w;
+  int st = walk_plan(rowptr, n_rows, chunk, group_edges, skip_empty, &w, nullptr, nullptr, nullptr);
+  if (st) return st;
   std::memset(plan, 0, sizeof(*plan));
   plan->n_rows = n_rows;
   plan->chunk = chunk;
+  plan->group_edges = group_edges;
   plan->skip_empty = skip_empty ? 1 : 0;
-  plan->n_items = items;
-  plan->n_split_items = split_items;
-  plan->n_split_rows = split_rows;
+  plan->n_items = w.items;
+  plan->n_split_items = w.split_items;
+  plan->n_split_rows = w.split_rows;
   return ok();
 }
 
-int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* item_row, int32_t* item_chunk,
-                      int32_t* split_row, int32_t* split_ptr) {
+int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* items, int32_t* split_row,
+                      int32_t* split_ptr) {
   if (!rowptr || !plan) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
-  if ((plan->n_items > 0 && !item_row) || (plan->n_split_items > 0 && (!item_chunk || !split_row || !split_ptr)))
+  if ((plan->n_items > 0 && !items) || !split_ptr || (plan->n_split_rows > 0 && !split_row))
     return fail(QHA_ERR_INVALID_ARG, "NULL output array");
-  const int32_t chunk = plan->chunk;
-  // split rows first (heaviest work starts first), then every other row in order
-  int64_t it = 0, sr = 0;
-  if (plan->n_split_rows > 0) split_ptr[0] = 0;
-  for (int64_t r = 0; r < plan->n_rows; ++r) {
-    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
-    const int64_t c = (len + chunk - 1) / chunk;
-    if (c > 1) {
-      for (int64_t j = 0; j < c; ++j) {
-        item_row[it] = static_cast<int32_t>(r);
-        item_chunk[it] = static_cast<int32_t>(j);
-        ++it;
-      }
-      split_row[sr] = static_cast<int32_t>(r);
-      split_ptr[++sr] = static_cast<int32_t>(it);
-    }
-  }
-  if (it != plan->n_split_items || sr != plan->n_split_rows) return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr");
-  for (int64_t r = 0; r < plan->n_rows; ++r) {
-    const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
-    if (len > chunk) continue;
-    if (len == 0 && plan->skip_empty) continue;
-    item_row[it++] = static_cast<int32_t>(r);
-  }
-  if (it != plan->n_items) return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr");
+  PlanWalk w;
+  int st = walk_plan(rowptr, plan->n_rows, plan->chunk, plan->group_edges, plan->skip_empty, &w, items, split_row,
+                     split_ptr);
+  if (st) return st;
+  if (w.items != plan->n_items || w.split_items != plan->n_split_items || w.split_rows != plan->n_split_rows)
+    return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr");
   return ok();
 }
 
@@ -239,16 +267,14 @@ int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, voi
 
 int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int64_t n_rows, int32_t d,
                       const uint8_t* bits, const uint32_t* word_offset, uint64_t seed, uint32_t epoch,
-                      uint32_t stream_id, uint32_t node_base, uint32_t* codes, float* scale, float* zero_point,
-                      void* stream) {
+                      uint32_t stream_id, uint32_t node_base, uint32_t* codes, float* meta, void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
   if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
   if (n_rows == 0) return ok();
   int st = check_rows("x", x, ldx, d);
   if (st) return st;
-  if (!bits || !word_offset || !codes || !scale || !zero_point) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned4(codes) || !aligned4(scale) || !aligned4(zero_point) || !aligned4(word_offset) ||
-      (row_index && !aligned4(row_index)))
+  if (!bits || !word_offset || !codes || !meta) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned4(codes) || !aligned8(meta) || !aligned4(word_offset) || (row_index && !aligned4(row_index)))
     return fail(QHA_ERR_INVALID_ARG, "misaligned array");
   if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_rows) - 1 > 0xFFFFFFFFull)
     return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
@@ -265,15 +291,14 @@ int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int
   a.stream_id = stream_id;
   a.node_base = node_base;
   a.codes = codes;
-  a.scale = scale;
-  a.zero_point = zero_point;
+  a.meta = meta;
   return hip_status(qha::launch_quantize(a, d, static_cast<hipStream_t>(stream)), "quantize_pack");
 }
 
-int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const qha_agg_plan* plan,
-                              const float* r, const float* c, const float* x_inner, int64_t ldx, int64_t n_inner,
-                              const uint32_t* codes, const uint32_t* word_offset, const uint8_t* bits,
-                              const float* scale, const float* zero_point, int64_t n_halo, int32_t d, int32_t beta,
+int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const int32_t* row_ids,
+                              const qha_agg_plan* plan, const float* r, const float* c, const float* x_inner,
+                              int64_t ldx, int64_t n_inner, const uint32_t* codes, const uint32_t* word_offset,
+                              const uint8_t* bits, const float* meta, int64_t n_halo, int32_t d, int32_t beta,
                               float* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex || n_inner < 0 || n_halo < 0 || n_inner + n_halo > kMaxIndex)
     return fail(QHA_ERR_INVALID_ARG, "bad sizes");
@@ -287,8 +312,10 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
     st = check_rows("x_inner", x_inner, ldx, d);
     if (st) return st;
   }
-  if (n_halo > 0 && (!codes || !word_offset || !bits || !scale || !zero_point))
+  if (n_halo > 0 && (!codes || !word_offset || !bits || !meta))
     return fail(QHA_ERR_INVALID_ARG, "halo message arrays are NULL");
+  if (n_halo > 0 && (!aligned8(meta) || !aligned4(codes) || !aligned4(word_offset)))
+    return fail(QHA_ERR_INVALID_ARG, "misaligned halo message arrays");
   st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
   if (st) return st;
   qha::GatherArgs g;
@@ -296,6 +323,7 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
   g.n_rows = n_rows;
   g.rowptr = rowptr;
   g.colidx = colidx;
+  g.row_ids = row_ids;
   fill_plan_args(g, plan, n_rows, workspace);
   g.rs = r;
   g.cs = c;
@@ -305,8 +333,7 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
   g.codes = codes;
   g.word_offset = word_offset;
   g.bits = bits;
-  g.scale = scale;
-  g.zero_point = zero_point;
+  g.meta = meta;
   g.n_halo = n_halo;
   g.beta = beta;
   g.out = out;

@@ -4,21 +4,23 @@
 // sqrt(d_v d_u)) and section 6 (a received halo row is scale * q + min, restored to float32).
 // The same kernel walks the transposed CSR for the embedding-gradient pass (sections 3 and 11).
 //
-// Mapping to gfx950: one wavefront owns one work item (a row, or a <= chunk-edge slice of a heavy
-// row).  Its 64 lanes split the d features (d/64 contiguous floats per lane), so every neighbour
-// costs one coalesced d*4-byte load.  The item's row bounds, column indices, edge weights and the
-// halo metadata are wavefront-uniform and go through the scalar unit; only feature rows and packed
-// code words use the vector memory pipe.  Edges are processed in batches of eight whose loads are
-// all issued before the first is consumed, so each wavefront keeps eight rows in flight.  For a
-// halo neighbour each lane fetches the one code word holding its features, shifts and masks its
-// codes out and dequantises in float32 (scale * q + min, no contraction) before the weighted add.
-// Accumulation is in float64: a float32 product w * x is exact in float64 and MI355X issues
-// float64 FMAs at the rate of unpacked float32 ones, so in this memory-bound loop the wider sum
-// costs no time and leaves the final rounding to float32 as the only error of the sum itself
-// (sums over hub rows and columns with cancellation would otherwise lose digits).
-// Heavy rows are split by the host-built plan; their slices write partial sums that a second
-// kernel adds in slice order, so results do not depend on scheduling.  Widths below 64 put several
-// items into one wavefront (d lanes each).
+// Mapping to gfx950: one wavefront owns one work item of the host-built plan -- a group of
+// consecutive short rows, or one chunk of a heavy row -- and streams through the item's
+// contiguous edge list in batches of B edges.  Its 64 lanes split the d features (d/64
+// contiguous floats per lane), so every neighbour costs one coalesced d*4-byte load.  Column
+// indices, edge weights and halo metadata are wavefront-uniform and come through the scalar unit;
+// only feature rows and packed code words use the vector memory pipe.  A batch runs in phases:
+// (1) scalar loads of the batch's weights and halo metadata, vector loads of its inner rows and
+// the scalar load of the next batch's column indices, all in flight together; (2) after one wait,
+// the code words of its halo rows (one word per lane holds all of its codes); (3) the sums.  Row
+// boundaries inside a group are tracked with scalar compares against the group's row pointers,
+// held one per lane and read with readlane, so crossing a row costs a store and no load.
+// A halo value is dequantised in float32 (scale * q + min, no contraction); every product is then
+// accumulated in float64 (a float32 product is exact there, and MI355X issues float64 FMAs at the
+// rate of unpacked float32 ones, so in this memory-bound loop the wider sum is free) and rounded
+// to float32 once.  Chunks of a heavy row write float64 partial sums that a second kernel adds in
+// chunk order, so results do not depend on scheduling.
+#include "../../include/qha.h"
 #include "qha_internal.hpp"
 
 namespace qha {
@@ -33,52 +35,37 @@ __device__ __forceinline__ cptr<T> cst(const T* p) {
 }
 
 constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
-constexpr int kBatch = 8;
+constexpr int batch_of(int D, bool halo) { return (D >= 512 || halo) ? 8 : 16; }
+constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
+
+__device__ __forceinline__ int rdlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float rdlanef(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 
 __device__ __forceinline__ float dequant(float sc, uint32_t q, float zp) {
   return __fadd_rn(__fmul_rn(sc, static_cast<float>(q)), zp);
 }
 
-// Value of halo row k for this lane's VEC features (j0 = first feature of the lane).
+__device__ __forceinline__ bool width_ok(uint32_t b) {
+  return b == 1u || b == 2u || b == 4u || b == 8u || b == 32u;
+}
+
 template <int VEC>
-__device__ __forceinline__ void load_halo(const GatherArgs& a, int64_t k, int j0, float (&xv)[VEC]) {
-  const uint32_t b = cst(a.bits)[k];
-  const uint32_t off = cst(a.word_offset)[k];
-  const uint32_t* row = a.codes + off;
-  if (b == 32u) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) xv[i] = __uint_as_float(row[j0 + i]);
-    return;
-  }
-  if (!(b == 1u || b == 2u || b == 4u || b == 8u)) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) xv[i] = 0.0f;
-    return;
-  }
-  const float sc = cst(a.scale)[k];
-  const float zp = cst(a.zero_point)[k];
-  const uint32_t mask = (1u << b) - 1u;
-  const uint32_t pos = static_cast<uint32_t>(j0) * b;       // first bit of the lane's codes
-  if (VEC * 8 <= 32 || b * VEC <= 32u) {
-    const uint32_t word = row[pos >> 5] >> (pos & 31u);
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) xv[i] = dequant(sc, (word >> (static_cast<uint32_t>(i) * b)) & mask, zp);
+__device__ __forceinline__ void store_row(float* p, const float (&v)[VEC]) {
+  if constexpr (VEC == 1) {
+    p[0] = v[0];
+  } else if constexpr (VEC == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
   } else {
-    // VEC * b == 64: two consecutive words, four (b = 8) codes each
-    const uint32_t w0 = row[pos >> 5];
-    const uint32_t w1 = row[(pos >> 5) + 1];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const uint32_t p = static_cast<uint32_t>(i) * b;
-      const uint32_t w = p < 32u ? (w0 >> p) : (w1 >> (p - 32u));
-      xv[i] = dequant(sc, w & mask, zp);
-    }
+    for (int q = 0; q < VEC / 4; ++q)
+      reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
 }
 
 template <int VEC>
-__device__ __forceinline__ void load_inner(const GatherArgs& a, int64_t u, int j0, float (&xv)[VEC]) {
-  const float* p = a.x + u * a.ldx + j0;
+__device__ __forceinline__ void load_row(const float* p, float (&xv)[VEC]) {
   if constexpr (VEC == 1) {
     xv[0] = p[0];
   } else if constexpr (VEC == 2) {
@@ -93,101 +80,179 @@ __device__ __forceinline__ void load_inner(const GatherArgs& a, int64_t u, int j
   }
 }
 
-template <int D, bool HALO>
+template <int D, bool HALO, bool BETA>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
-  constexpr int G = D / VEC;      // lanes per item
-  constexpr int IPW = 64 / G;     // items per wavefront
+  constexpr int G = D / VEC;           // lanes that own features
+  constexpr int B = batch_of(D, HALO);
+  constexpr int CW = (VEC * 8 > 32) ? 2 : 1;   // code words a lane may need (8-bit codes, VEC = 8)
   const int lane = threadIdx.x & 63;
-  const int j0 = (lane % G) * VEC;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 +
+  const int j0 = (G == 64 ? lane : (lane < G ? lane : 0)) * VEC;   // idle lanes shadow lane 0
+  const bool owner = (G == 64) || lane < G;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t item = wave * IPW + (IPW == 1 ? 0 : lane / G);
   if (item >= a.n_items) return;
 
-  int64_t row;
-  int32_t e0, e1;
-  bool split = false;
-  if (a.item_row != nullptr) {
-    row = cst(a.item_row)[item];
-    e0 = cst(a.rowptr)[row];
-    e1 = cst(a.rowptr)[row + 1];
-    if (item < a.n_split_items) {
-      e0 += cst(a.item_chunk)[item] * a.chunk;
-      e1 = min(e1, e0 + a.chunk);
-      split = true;
-    }
+  int32_t row0, nrows, e0, e1;
+  if (a.items != nullptr) {
+    cptr<int32_t> it = cst(a.items) + 4 * item;
+    row0 = it[0];
+    nrows = it[1];
+    e0 = it[2];
+    e1 = it[3];
   } else {
-    row = item;
-    e0 = cst(a.rowptr)[row];
-    e1 = cst(a.rowptr)[row + 1];
+    row0 = static_cast<int32_t>(item);
+    nrows = 1;
+    e0 = cst(a.rowptr)[item];
+    e1 = cst(a.rowptr)[item + 1];
   }
-  const double rs = a.rs ? static_cast<double>(cst(a.rs)[row]) : 1.0;
+  const bool split = item < a.n_split_items;
+
+  // the group's row ends, row scales and output rows, one row per lane (rows of a group are
+  // never empty, so each edge closes at most one row)
+  const int li = lane < nrows ? lane : nrows - 1;
+  const int32_t v_end = split ? 0x7FFFFFFF : a.rowptr[row0 + li + 1];
+  const float v_rs = (a.rs != nullptr) ? a.rs[row0 + li] : 1.0f;
+  const int32_t v_out = (a.row_ids != nullptr) ? a.row_ids[row0 + li] : row0 + li;
 
   double acc[VEC];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+  int cur = 0;                                  // row of the group being summed
+  int32_t cur_end = rdlane(v_end, 0);
 
-  for (int32_t e = e0; e < e1; e += kBatch) {
-    const int cnt = min(kBatch, e1 - e);
-    int32_t u[kBatch];
-    double w[kBatch];
-    float xv[kBatch][VEC];
+  auto flush = [&]() {                          // write row `cur` and start the next one
+    const double r = static_cast<double>(rdlanef(v_rs, cur));
+    const int64_t orow = rdlane(v_out, cur);
+    float* dst = a.out + orow * a.ldo + j0;
+    if (owner) {
+      float res[VEC];
+      if constexpr (BETA) {
+        float old[VEC];
+        load_row<VEC>(dst, old);
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) u[i] = (i < cnt) ? cst(a.colidx)[e + i] : 0;
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + r * acc[v]);
+      } else {
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (i < cnt) {
-        w[i] = a.cs ? rs * static_cast<double>(cst(a.cs)[u[i]]) : rs;
-        if (HALO && u[i] >= a.n_inner) {
-          load_halo<VEC>(a, static_cast<int64_t>(u[i]) - a.n_inner, j0, xv[i]);
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(r * acc[v]);
+      }
+      store_row<VEC>(dst, res);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+    ++cur;
+    cur_end = rdlane(v_end, cur < nrows ? cur : nrows - 1);
+  };
+
+  int32_t u_next[B];
+  if (e0 < e1) {
+#pragma unroll
+    for (int i = 0; i < B; ++i) u_next[i] = cst(a.colidx)[min(e0 + i, e1 - 1)];
+  }
+
+  for (int32_t e = e0; e < e1; e += B) {
+    int32_t u[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) u[i] = u_next[i];
+
+    // phase 1: weights, halo metadata and inner rows; the next batch's indices
+    float cw[B];
+    float xv[B][VEC];
+    uint32_t woff[B], bw[B];
+    float mn[B], sc[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      cw[i] = a.cs ? cst(a.cs)[u[i]] : 1.0f;
+      if (HALO && u[i] >= a.n_inner) {
+        const int64_t k = static_cast<int64_t>(u[i]) - a.n_inner;
+        woff[i] = cst(a.word_offset)[k];
+        if constexpr (D >= 32) {
+          // the width follows from the row's word count (unique for d >= 32)
+          bw[i] = ((cst(a.word_offset)[k + 1] - woff[i]) << 5) >> log2i(D);
         } else {
-          load_inner<VEC>(a, u[i], j0, xv[i]);
+          bw[i] = cst(a.bits)[k];
+        }
+        mn[i] = cst(a.meta)[2 * k];
+        sc[i] = cst(a.meta)[2 * k + 1];
+      } else {
+        load_row<VEC>(a.x + static_cast<int64_t>(u[i]) * a.ldx + j0, xv[i]);
+      }
+    }
+    if (e + B < e1) {
+#pragma unroll
+      for (int i = 0; i < B; ++i) u_next[i] = cst(a.colidx)[min(e + B + i, e1 - 1)];
+    }
+    // phase 2: the code words of the halo rows
+    uint32_t cwd[B][CW];
+    if (HALO) {
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        if (u[i] >= a.n_inner) {
+          const uint32_t b = bw[i];
+          const uint32_t* row = a.codes + woff[i];
+          if (b == 32u) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
+          } else if (width_ok(b)) {
+            const uint32_t pos = static_cast<uint32_t>(j0) * b;
+            cwd[i][0] = row[pos >> 5];
+            if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
+          }
         }
       }
     }
+    // phase 3: dequantise and sum, closing the row whose last edge this is
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (i < cnt) {
+    for (int i = 0; i < B; ++i) {
+      const int32_t p = e + i;
+      if (p < e1) {
+        if (HALO && u[i] >= a.n_inner) {
+          const uint32_t b = bw[i];
+          if (b != 32u) {
+            if (width_ok(b)) {
+              const uint32_t mask = (1u << b) - 1u;
+              const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fma(w[i], static_cast<double>(xv[i][v]), acc[v]);
+              for (int v = 0; v < VEC; ++v) {
+                const uint32_t bitpos = sh + static_cast<uint32_t>(v) * b;
+                const uint32_t w = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
+                xv[i][v] = dequant(sc[i], w & mask, mn[i]);
+              }
+            } else {
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) xv[i][v] = 0.0f;
+            }
+          }
+        }
+        const double w = static_cast<double>(cw[i]);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = fma(w, static_cast<double>(xv[i][v]), acc[v]);
+        if (p + 1 == cur_end) flush();
       }
     }
   }
 
   if (split) {
     double* p = a.partial + item * D + j0;
+    if (owner) {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) p[v] = acc[v];
-    return;
-  }
-  float* dst = a.out + row * a.ldo + j0;
-  float res[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
-  if constexpr (VEC == 1) {
-    dst[0] = res[0];
-  } else if constexpr (VEC == 2) {
-    *reinterpret_cast<float2*>(dst) = make_float2(res[0], res[1]);
-  } else {
-#pragma unroll
-    for (int q = 0; q < VEC / 4; ++q)
-      reinterpret_cast<float4*>(dst)[q] = make_float4(res[4 * q], res[4 * q + 1], res[4 * q + 2], res[4 * q + 3]);
+      for (int v = 0; v < VEC; ++v) p[v] = acc[v];
+    }
+  } else if (e0 == e1) {
+    flush();                                   // an empty row: zero, or left as it is (+0)
   }
 }
 
-// Adds the partial sums of every split row in slice order and writes the row.
+// Adds the partial sums of every split row in chunk order, scales and writes the row.
 template <int D>
 __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;
-  constexpr int IPW = 64 / G;
   const int lane = threadIdx.x & 63;
-  const int j0 = (lane % G) * VEC;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 +
-                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t m = wave * IPW + (IPW == 1 ? 0 : lane / G);
-  if (m >= a.n_split_rows) return;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * 4 +
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (m >= a.n_split_rows || lane >= G) return;
+  const int j0 = lane * VEC;
   const int64_t row = cst(a.split_row)[m];
   const int32_t i0 = cst(a.split_ptr)[m];
   const int32_t i1 = cst(a.split_ptr)[m + 1];
@@ -198,27 +263,30 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + a.partial[static_cast<int64_t>(i) * D + j0 + v];
   }
-  float* dst = a.out + row * a.ldo + j0;
+  const double r = a.rs ? static_cast<double>(a.rs[row]) : 1.0;
+  const int64_t orow = a.row_ids ? a.row_ids[row] : row;
+  float* dst = a.out + orow * a.ldo + j0;
 #pragma unroll
   for (int v = 0; v < VEC; ++v)
-    dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
+    dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + r * acc[v] : r * acc[v]);
 }
 
 template <int D>
 hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, hipStream_t s) {
-  constexpr int IPW = 64 / (D / vec_of(D));
-  constexpr int IPB = 4 * IPW;   // items per 256-thread block
   if (a.n_items > 0) {
-    const int64_t blocks = (a.n_items + IPB - 1) / IPB;
-    if (with_halo)
-      hipLaunchKernelGGL((gather_kernel<D, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gather_kernel<D, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
+    if (with_halo) {
+      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, true, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gather_kernel<D, true, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gather_kernel<D, false, false>), grid, dim3(256), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.n_split_rows > 0) {
-    const int64_t blocks = (a.n_split_rows + IPB - 1) / IPB;
+    const int64_t blocks = (a.n_split_rows + 3) / 4;
     hipLaunchKernelGGL((combine_split_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
     return hipGetLastError();
   }

@@ -17,22 +17,20 @@ struct QuantArgs {
   const uint32_t* word_offset;
   uint32_t seed_lo, seed_hi, epoch, stream_id, node_base;
   uint32_t* codes;
-  float* scale;
-  float* zero_point;
+  float* meta;          // (min, scale) per row
 };
 
-// One gather over a CSR: out[row] (+)= sum_e rs[row] * cs[col_e] * value(col_e).  value() is a
+// One gather over a CSR: out[row_ids[i]] (+)= rs[i] * sum_e cs[col_e] * value(col_e).  value() is a
 // float32 row of x for col < n_inner and a dequantised halo message for col >= n_inner.
 struct GatherArgs {
   int64_t n_rows;
   const int32_t* rowptr;
   const int32_t* colidx;
-  // work plan (item_row == nullptr: item i is row i, no splitting)
+  const int32_t* row_ids;
+  // work plan (items == nullptr: item i is row i alone)
   int64_t n_items;
   int64_t n_split_items;
-  int32_t chunk;
-  const int32_t* item_row;
-  const int32_t* item_chunk;
+  const int32_t* items;       // int32[4] per item: first row, row count, first edge, end edge
   int64_t n_split_rows;
   const int32_t* split_row;
   const int32_t* split_ptr;
@@ -46,14 +44,13 @@ struct GatherArgs {
   const uint32_t* codes;
   const uint32_t* word_offset;
   const uint8_t* bits;
-  const float* scale;
-  const float* zero_point;
+  const float* meta;
   int64_t n_halo;
   // output
   int32_t beta;
   float* out;
   int64_t ldo;
-  double* partial;  // [n_split_items, d] float64 partial sums of split rows
+  double* partial;            // [n_split_items, d] float64 partial sums of split rows
 };
 
 struct GemmArgs {

@@ -143,10 +143,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
       row_codes[gl >> 2] = word;
     }
   }
-  if (gl == 0) {
-    a.scale[r] = sc;
-    a.zero_point[r] = zp;
-  }
+  if (gl == 0) *reinterpret_cast<float2*>(a.meta + 2 * r) = make_float2(zp, sc);   // (min, scale)
 }
 
 __global__ __launch_bounds__(256) void degree_norm_kernel(const int32_t* deg, int64_t n, int32_t kind,

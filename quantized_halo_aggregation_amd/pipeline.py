@@ -25,17 +25,24 @@ QUANT_SEED = synth.QUANT_SEED
 
 @dataclasses.dataclass
 class Messages:
-    """One packed message buffer: the codes and per-row (min, scale) of the halo rows."""
+    """One packed message buffer: the codes and per-row (min, scale) pairs of the halo rows."""
     codes: torch.Tensor        # int32 words (uint32 bit patterns)
-    scale: torch.Tensor
-    zero_point: torch.Tensor
+    meta: torch.Tensor         # float32 [n_h, 2]: min (zero-point), scale
+
+    @property
+    def zero_point(self):
+        return self.meta[:, 0]
+
+    @property
+    def scale(self):
+        return self.meta[:, 1]
 
 
 class GpuPartition:
     """Device-resident CSR / CSC / norms / widths / plans of one partition (set-up, untimed)."""
 
     def __init__(self, part: synth.Partition, device: str = "cuda", chunk: int = B.DEFAULT_CHUNK,
-                 bits=None):
+                 group_edges: int = B.DEFAULT_GROUP_EDGES, bits=None):
         self.part = part
         self.device = device
         n_in, n_h, d = part.n_in, part.n_h, part.d
@@ -54,10 +61,14 @@ class GpuPartition:
         self.rowptr, self.colidx = dev(ptr), dev(idx)
         self.colptr, self.rowidx = dev(colptr), dev(rowidx)
 
-        # mirror map as a CSR over inner rows listing the halo rows that copy them
+        # mirror map as a compact CSR: one row per inner node that has halo copies, listing them,
+        # with row_ids naming the inner node
         m_ptr, m_idx = B.csr_transpose(np.arange(n_h + 1, dtype=np.int32), part.mirror, n_in)
+        targets = np.flatnonzero(np.diff(m_ptr) > 0).astype(np.int32)
+        mc_ptr = np.concatenate([[0], np.cumsum(np.diff(m_ptr)[targets])]).astype(np.int32)
         self.mirror = dev(part.mirror)
-        self.m_ptr, self.m_idx = dev(m_ptr), dev(m_idx)
+        self.m_ptr, self.m_idx, self.m_rows = dev(mc_ptr), dev(m_idx), dev(targets)
+        self.h_m_ptr = mc_ptr
 
         self.set_bits(part.bits if bits is None else bits)
 
@@ -72,10 +83,11 @@ class GpuPartition:
             B.degree_norm(row_len, B.NORM_MEAN, self.mean_r)
             self.r_fwd, self.c_fwd = self.mean_r, None
 
-        self.plan_fwd = B.AggPlan(ptr, chunk, device=device)
-        self.plan_bwd_halo = B.AggPlan(colptr[n_in:], chunk, device=device)
-        self.plan_bwd_inner = B.AggPlan(colptr[:n_in + 1], chunk, device=device)
-        self.plan_mirror = B.AggPlan(m_ptr, chunk, skip_empty=True, device=device)
+        mk = lambda rp: B.AggPlan(rp, chunk, group_edges, device=device)
+        self.plan_fwd = mk(ptr)
+        self.plan_bwd_halo = mk(colptr[n_in:])
+        self.plan_bwd_inner = mk(colptr[:n_in + 1])
+        self.plan_mirror = mk(mc_ptr)
         ws = max(p.workspace_bytes(d) for p in (self.plan_fwd, self.plan_bwd_halo, self.plan_bwd_inner,
                                                  self.plan_mirror))
         self.agg_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
@@ -92,8 +104,7 @@ class GpuPartition:
 
     def new_messages(self) -> Messages:
         return Messages(torch.empty(max(self.total_words, 1), dtype=torch.int32, device=self.device),
-                        torch.empty(self.n_h, dtype=torch.float32, device=self.device),
-                        torch.empty(self.n_h, dtype=torch.float32, device=self.device))
+                        torch.empty(self.n_h, 2, dtype=torch.float32, device=self.device))
 
     def dense_workspace(self, *shapes):
         need = max(B.dense_project_workspace(*s) for s in shapes)
@@ -108,12 +119,12 @@ class GpuPartition:
     def quantize_send(self, x, row_index, msg: Messages, epoch, stream_id, seed=QUANT_SEED):
         """a1 / a7: quantise the n_h outgoing boundary rows (x[row_index] or x itself)."""
         B.quantize_pack(x, row_index, self.n_h, self.bits, self.word_offset, seed, epoch, stream_id, self.n_in,
-                        msg.codes, msg.scale, msg.zero_point)
+                        msg.codes, msg.meta)
 
     def aggregate_fwd(self, x_inner, msg: Messages, out):
         """a3: out = sum over N(v) and v of w_vu * x~_u, halo rows dequantised from msg."""
         B.dequant_aggregate_fwd(self.rowptr, self.colidx, self.plan_fwd, self.r_fwd, self.c_fwd, x_inner, self.n_in,
-                                msg.codes, self.word_offset, self.bits, msg.scale, msg.zero_point, self.n_h, 0, out,
+                                msg.codes, self.word_offset, self.bits, msg.meta, self.n_h, 0, out,
                                 workspace=self.agg_ws)
 
     def aggregate_bwd_halo(self, grad_out, dx_halo):
@@ -139,8 +150,8 @@ class GpuPartition:
     def add_received(self, msg: Messages, dx_inner):
         """a8: dx_inner[mirror[k]] += dequantised gradient message k."""
         B.dequant_aggregate_fwd(self.m_ptr, self.m_idx, self.plan_mirror, None, None, None, 0, msg.codes,
-                                self.word_offset, self.bits, msg.scale, msg.zero_point, self.n_h, 1, dx_inner,
-                                workspace=self.agg_ws)
+                                self.word_offset, self.bits, msg.meta, self.n_h, 1, dx_inner,
+                                workspace=self.agg_ws, row_ids=self.m_rows)
 
 
 class LayerStack:

@@ -78,4 +78,5 @@ def upload_messages(gp, msg):
     from quantized_halo_aggregation_amd.pipeline import Messages
     assert np.array_equal(msg["word_offset"], gp.h_word_offset.astype(np.int64))
     words = msg["words"] if msg["words"].size else np.zeros(1, np.uint32)
-    return Messages(dev(words.view(np.int32)), dev(msg["scale"]), dev(msg["zero_point"]))
+    meta = np.stack([msg["zero_point"], msg["scale"]], axis=1).astype(np.float32)
+    return Messages(dev(words.view(np.int32)), dev(meta))

@@ -70,55 +70,67 @@ def test_csr_transpose_and_validate():
         B.validate_csr(ptr, unsorted, n_cols)
 
 
-def _plan_host(ptr, chunk, skip_empty):
+def _plan_host(ptr, chunk, skip_empty, group_edges=256):
     st = B.AggPlanStruct()
-    B._check(B._plan_size(ptr.size - 1, ptr.ctypes.data, chunk, int(skip_empty), C.byref(st)), "size")
-    arrs = [np.zeros(max(n, 1), np.int32) for n in (st.n_items, st.n_split_items, st.n_split_rows)]
+    B._check(B._plan_size(ptr.size - 1, ptr.ctypes.data, chunk, group_edges, int(skip_empty), C.byref(st)), "size")
+    items = np.zeros(4 * max(st.n_items, 1), np.int32)
+    split_row = np.zeros(max(st.n_split_rows, 1), np.int32)
     sp = np.zeros(st.n_split_rows + 1, np.int32)
-    B._check(B._plan_fill(ptr.ctypes.data, C.byref(st), arrs[0].ctypes.data, arrs[1].ctypes.data,
-                          arrs[2].ctypes.data, sp.ctypes.data), "fill")
-    return st, arrs[0][:st.n_items], arrs[1][:st.n_split_items], arrs[2][:st.n_split_rows], sp
+    B._check(B._plan_fill(ptr.ctypes.data, C.byref(st), items.ctypes.data, split_row.ctypes.data, sp.ctypes.data),
+             "fill")
+    return st, items[:4 * st.n_items].reshape(-1, 4), split_row[:st.n_split_rows], sp
 
 
 @pytest.mark.parametrize("skip_empty", [False, True])
-def test_agg_plan_covers_every_edge_once(skip_empty):
-    lens = np.array([0, 3, 1200, 5, 0, 512, 513, 2000, 1], np.int32)
+@pytest.mark.parametrize("group_edges", [1, 8, 256])
+def test_agg_plan_covers_every_edge_and_row_once(skip_empty, group_edges):
+    lens = np.array([0, 3, 1200, 5, 0, 512, 513, 2000, 1, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 7, 0],
+                    np.int32)
     ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     chunk = 512
-    st, item_row, item_chunk, split_row, split_ptr = _plan_host(ptr, chunk, skip_empty)
-    covered = np.zeros(ptr[-1], np.int32)
-    for it, row in enumerate(item_row):
-        e0, e1 = ptr[row], ptr[row + 1]
+    st, items, split_row, split_ptr = _plan_host(ptr, chunk, skip_empty, group_edges)
+    edge_cover = np.zeros(ptr[-1], np.int32)
+    row_cover = np.zeros(lens.size, np.int32)
+    for it, (r0, nr, e0, e1) in enumerate(items):
+        assert nr >= 1 and nr <= B.GROUP_ROWS
+        edge_cover[e0:e1] += 1
         if it < st.n_split_items:
-            e0 = e0 + item_chunk[it] * chunk
-            e1 = min(e1, e0 + chunk)
-        covered[e0:e1] += 1
-    assert (covered == 1).all()
+            assert nr == 1 and lens[r0] > chunk and e1 - e0 <= chunk
+        else:
+            # a group is a run of whole consecutive rows; empty rows stand alone
+            assert e0 == ptr[r0] and e1 == ptr[r0 + nr]
+            row_cover[r0:r0 + nr] += 1
+            if nr > 1:
+                assert (lens[r0:r0 + nr] > 0).all() and e1 - e0 <= max(group_edges, lens[r0:r0 + nr].max())
+    assert (edge_cover == 1).all()
+    split = lens > chunk
+    assert (row_cover[split] == 0).all()
+    want = np.where(split, 0, np.where(lens == 0, 0 if skip_empty else 1, 1))
+    assert np.array_equal(row_cover, want)
     assert list(split_row) == [2, 6, 7]
     assert list(split_ptr) == [0, 3, 5, 9]
-    rows_with_items = set(item_row.tolist())
-    assert (0 in rows_with_items) == (not skip_empty)
     assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 8
 
 
 def test_device_calls_reject_bad_arguments_before_any_hip_call():
     q = B._quantize_pack
     # unsupported width
-    assert q(FAKE, 24, None, 10, 24, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, FAKE, None) == B.QHA_ERR_UNSUPPORTED
+    assert q(FAKE, 24, None, 10, 24, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_UNSUPPORTED
     # leading dimension below d
-    assert q(FAKE, 64, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 64, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
     # misaligned rows
-    assert q(FAKE + 4, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
-    # null outputs
-    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, None, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE + 4, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # null outputs, misaligned metadata pairs
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, None, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE + 4, None) == B.QHA_ERR_INVALID_ARG
     # node ids overflow 32 bits
-    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0xFFFFFFFF, FAKE, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0xFFFFFFFF, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
     # nothing to do is OK without touching the device
-    assert q(None, 0, None, 0, 128, None, None, 1, 0, 0, 0, None, None, None, None) == B.QHA_OK
+    assert q(None, 0, None, 0, 128, None, None, 1, 0, 0, 0, None, None, None) == B.QHA_OK
 
     f = B._dequant_aggregate_fwd
-    args = dict(n_rows=10, rowptr=FAKE, colidx=FAKE, plan=None, r=None, c=None, x=FAKE, ldx=128, n_inner=5,
-                codes=FAKE, wo=FAKE, bits=FAKE, sc=FAKE, zp=FAKE, n_halo=5, d=128, beta=0, out=FAKE, ldo=128,
+    args = dict(n_rows=10, rowptr=FAKE, colidx=FAKE, row_ids=None, plan=None, r=None, c=None, x=FAKE, ldx=128,
+                n_inner=5, codes=FAKE, wo=FAKE, bits=FAKE, meta=FAKE, n_halo=5, d=128, beta=0, out=FAKE, ldo=128,
                 ws=None, wsb=0, s=None)
 
     def call(**kw):
@@ -128,16 +140,17 @@ def test_device_calls_reject_bad_arguments_before_any_hip_call():
     assert call(d=100) == B.QHA_ERR_UNSUPPORTED
     assert call(ldo=130) == B.QHA_ERR_INVALID_ARG
     assert call(codes=None) == B.QHA_ERR_INVALID_ARG
+    assert call(meta=FAKE + 4) == B.QHA_ERR_INVALID_ARG
     assert call(rowptr=None) == B.QHA_ERR_INVALID_ARG
     assert call(n_inner=-1) == B.QHA_ERR_INVALID_ARG
     # a plan that skips empty rows cannot be combined with beta = 0
     lens = np.array([0, 600, 3], np.int32)
     ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     st, *_ = _plan_host(ptr, 512, True)
-    st.item_row = st.item_chunk = st.split_row = st.split_ptr = FAKE
+    st.items = st.split_row = st.split_ptr = FAKE
     assert call(n_rows=3, plan=C.byref(st)) == B.QHA_ERR_INVALID_ARG
     st2, *_ = _plan_host(ptr, 512, False)
-    st2.item_row = st2.item_chunk = st2.split_row = st2.split_ptr = FAKE
+    st2.items = st2.split_row = st2.split_ptr = FAKE
     # split rows need a workspace
     assert call(n_rows=3, plan=C.byref(st2)) == B.QHA_ERR_WORKSPACE
     # plan built for another row count

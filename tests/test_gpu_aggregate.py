@@ -142,13 +142,13 @@ def test_plain_rows_and_degenerate_inputs():
     out = torch.full((25, d), np.nan, dtype=torch.float32, device="cuda")
     B.dequant_aggregate_fwd(H.dev(ptr), H.dev(idx), None, H.dev(r), H.dev(c), H.dev(x), n_inner,
                             H.dev(msg["words"].view(np.int32)), H.dev(off.view(np.int32)), H.dev(bits),
-                            H.dev(msg["scale"]), H.dev(msg["zero_point"]), n_halo, 0, out)
+                            H.dev(np.stack([msg["zero_point"], msg["scale"]], 1)), n_halo, 0, out)
     got = H.host(out)
     H.assert_close(got, ref, what="plain rows")
     assert not got[[0, 7, 24]].any()
     # zero rows: nothing happens
     B.dequant_aggregate_fwd(H.dev(ptr[:1]), H.dev(idx), None, None, None, H.dev(x), n_inner, None, None, None, None,
-                            None, 0, 0, out, n_rows=0)
+                            0, 0, out, n_rows=0)
     # no halo at all: only inner columns may appear
     inner_only = ptr.copy()
     keep = idx < n_inner
@@ -156,7 +156,7 @@ def test_plain_rows_and_degenerate_inputs():
     inner_only = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
     out2 = torch.full((25, d), np.nan, dtype=torch.float32, device="cuda")
     B.dequant_aggregate_fwd(H.dev(inner_only), H.dev(idx[keep]), None, None, None, H.dev(x), n_inner, None, None,
-                            None, None, None, 0, 0, out2)
+                            None, None, 0, 0, out2)
     ref2 = np.zeros((25, d))
     np.add.at(ref2, rows[keep], x[idx[keep]].astype(np.float64))
     H.assert_close(H.host(out2), ref2, what="inner-only rows, unit weights")

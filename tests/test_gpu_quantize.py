@@ -58,20 +58,19 @@ def test_quantize_pack_bit_exact(d, n):
     off_d, total = B.pack_layout(bits, d)
     assert np.array_equal(off_d.astype(np.int64), off)
     codes = torch.full((max(total, 1),), -1, dtype=torch.int32, device="cuda")
-    sc = torch.empty(n, dtype=torch.float32, device="cuda")
-    z = torch.empty(n, dtype=torch.float32, device="cuda")
+    meta = torch.empty(n, 2, dtype=torch.float32, device="cuda")
     x_dev = H.dev(big)[:, :d]          # rows of d features, leading dimension ld
     B.quantize_pack(x_dev, H.dev(row_index), n, H.dev(bits), H.dev(off_d.view(np.int32)), SEED, epoch, stream_id,
-                    node_base, codes, sc, z)
+                    node_base, codes, meta)
     H.assert_bits_equal(H.host(codes)[:total].view(np.uint32), words, "codes")
-    H.assert_bits_equal(H.host(sc), scale, "scale")
-    H.assert_bits_equal(H.host(z), zp, "zero_point")
+    H.assert_bits_equal(H.host(meta)[:, 1], scale, "scale")
+    H.assert_bits_equal(H.host(meta)[:, 0], zp, "zero_point (min)")
 
     # without a row index the rows are read in order
     direct = np.ascontiguousarray(big[row_index])
     codes2 = torch.full_like(codes, -1)
     B.quantize_pack(H.dev(direct)[:, :d], None, n, H.dev(bits), H.dev(off_d.view(np.int32)), SEED, epoch, stream_id,
-                    node_base, codes2, sc, z)
+                    node_base, codes2, meta)
     H.assert_bits_equal(H.host(codes2)[:total].view(np.uint32), words, "codes (direct)")
 
 
@@ -88,9 +87,8 @@ def test_quantize_is_reproducible_and_depends_on_every_counter_field():
 
     def run(seed, epoch, stream_id, node_base):
         c = torch.empty(total, dtype=torch.int32, device="cuda")
-        s = torch.empty(n, dtype=torch.float32, device="cuda")
-        z = torch.empty(n, dtype=torch.float32, device="cuda")
-        B.quantize_pack(x_dev, None, n, b_dev, o_dev, seed, epoch, stream_id, node_base, c, s, z)
+        m = torch.empty(n, 2, dtype=torch.float32, device="cuda")
+        B.quantize_pack(x_dev, None, n, b_dev, o_dev, seed, epoch, stream_id, node_base, c, m)
         return H.host(c)
 
     H.note("quantize reproducibility")
@@ -112,19 +110,17 @@ def test_unknown_width_rows_are_left_untouched_and_zero_rows_are_noops():
     bits = np.array([4, 4, 3, 4, 4, 4], np.uint8)
     off = np.arange(n + 1, dtype=np.uint32) * 8            # as if every row were 4-bit
     codes = torch.full((n * 8,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
-    sc = torch.full((n,), 7.0, device="cuda")
-    z = torch.full((n,), 7.0, device="cuda")
+    meta = torch.full((n, 2), 7.0, device="cuda")
     H.note("quantize unknown width")
-    B.quantize_pack(H.dev(x), None, n, H.dev(bits), H.dev(off.view(np.int32)), 1, 0, 0, 0, codes, sc, z)
+    B.quantize_pack(H.dev(x), None, n, H.dev(bits), H.dev(off.view(np.int32)), 1, 0, 0, 0, codes, meta)
     c = H.host(codes).reshape(n, 8)
-    assert (c[2] == 0x5A5A5A5A).all() and H.host(sc)[2] == 7.0
-    ok_rows = [0, 1, 3, 4, 5]
-    words, _, scale, zp = _oracle(x[ok_rows], bits[ok_rows], 1, 0, 0, 0)
+    assert (c[2] == 0x5A5A5A5A).all() and (H.host(meta)[2] == 7.0).all()
     # rows keep their own node ids (node_base + r), so recompute the oracle per row
-    for r in ok_rows:
+    for r in [0, 1, 3, 4, 5]:
         w, _, s, zz = _oracle(x[r:r + 1], bits[r:r + 1], 1, 0, 0, r)
         H.assert_bits_equal(c[r].view(np.uint32), w, f"row {r}")
-    B.quantize_pack(H.dev(x), None, 0, H.dev(bits), H.dev(off.view(np.int32)), 1, 0, 0, 0, codes, sc, z)
+        H.assert_bits_equal(H.host(meta)[r], np.array([zz[0], s[0]], np.float32), f"meta row {r}")
+    B.quantize_pack(H.dev(x), None, 0, H.dev(bits), H.dev(off.view(np.int32)), 1, 0, 0, 0, codes, meta)
 
 
 @pytest.mark.parametrize("wl_index", [2, 4])
@@ -140,10 +136,9 @@ def test_full_size_send_set_bit_exact(wl_index):
     off_d, total = B.pack_layout(part.bits, d)
     H.note(f"quantize full {wl.name}")
     codes = torch.empty(total, dtype=torch.int32, device="cuda")
-    sc = torch.empty(wl.n_h, dtype=torch.float32, device="cuda")
-    z = torch.empty(wl.n_h, dtype=torch.float32, device="cuda")
+    meta = torch.empty(wl.n_h, 2, dtype=torch.float32, device="cuda")
     B.quantize_pack(H.dev(part.x), H.dev(part.mirror), wl.n_h, H.dev(part.bits), H.dev(off_d.view(np.int32)), SEED,
-                    0, 0, wl.n_in, codes, sc, z)
+                    0, 0, wl.n_in, codes, meta)
     H.assert_bits_equal(H.host(codes).view(np.uint32), words, "codes")
-    H.assert_bits_equal(H.host(sc), scale, "scale")
-    H.assert_bits_equal(H.host(z), zp, "zero_point")
+    H.assert_bits_equal(H.host(meta)[:, 1], scale, "scale")
+    H.assert_bits_equal(H.host(meta)[:, 0], zp, "zero_point (min)")
