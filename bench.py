@@ -39,24 +39,26 @@ def row_words(d, bits):
 
 
 def quantize_bytes(n_rows, d, bits, gathered):
+    """Each row: read d floats (through the row index when gathered), write its packed codes and its
+    (min, scale) pair.  Widths and offsets come from the width classes (no per-row table)."""
     w = row_words(d, bits)
-    per_row = 4 * d + 1 + 4 + 8 + (4 if gathered else 0)
+    per_row = 4 * d + 8 + (4 if gathered else 0)
     return int(n_rows * per_row + 4 * w.sum())
 
 
-def gather_bytes(rowptr, colidx, n_inner, d, halo_words, beta, rows_weighted=True, cols_weighted=True):
-    """Per-edge gather model: every edge reads its index, its column weight and a whole feature row
-    (inner) or packed code row + metadata (halo); every row reads its bounds and weight, writes d floats
-    (and reads them first when beta = 1)."""
+def gather_bytes(rowptr, colidx, n_inner, d, halo_words, beta, weighted=True, row_ids=False):
+    """Per-edge gather model: every edge reads its column index, its weight and a whole feature row
+    (inner) or its packed code row plus (min, scale) (halo); every row reads its bound, writes d
+    floats (and reads them first when beta = 1)."""
     n_rows = rowptr.size - 1
     e = colidx.size
     halo = colidx >= n_inner
     n_halo_e = int(halo.sum())
-    edge = e * (4 + (4 if cols_weighted else 0)) + (e - n_halo_e) * 4 * d
+    edge = e * (4 + (4 if weighted else 0)) + (e - n_halo_e) * 4 * d
     if n_halo_e:
         k = colidx[halo] - n_inner
-        edge += int(4 * halo_words[k].sum()) + n_halo_e * (8 + 1 + 4)
-    rows = n_rows * (4 + (4 if rows_weighted else 0) + 4 * d * (2 if beta else 1))
+        edge += int(4 * halo_words[k].sum()) + n_halo_e * 8
+    rows = n_rows * (4 + (4 if row_ids else 0) + 4 * d * (2 if beta else 1))
     return int(edge + rows)
 
 
@@ -97,13 +99,10 @@ def main():
     b_q_fwd = quantize_bytes(n_h, d, part.bits, gathered=True)
     b_q_bwd = quantize_bytes(n_h, d, part.bits, gathered=False)
     sage = wl.model == "sage"
-    b_agg_fwd = gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0, cols_weighted=not sage)
-    b_bwd_halo = gather_bytes(nw[n_in:], gp.h_rowidx[nw[n_in]:], 1 << 62, d, hw, beta=0, rows_weighted=not sage)
-    b_bwd_inner = gather_bytes(nw[:n_in + 1], gp.h_rowidx[:nw[n_in]], 1 << 62, d, hw, beta=1 if sage else 0,
-                               rows_weighted=not sage)
-    m_ptr = np.diff(B.csr_transpose(np.arange(n_h + 1, dtype=np.int32), part.mirror, n_in)[0])
-    n_targets = int((m_ptr > 0).sum())
-    b_add = n_targets * (4 + 8 * d) + n_h * (4 + 8 + 1 + 4) + int(4 * hw.sum())
+    b_agg_fwd = gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0)
+    b_bwd_halo = gather_bytes(nw[n_in:], gp.h_rowidx[nw[n_in]:], 1 << 62, d, hw, beta=0)
+    b_bwd_inner = gather_bytes(nw[:n_in + 1], gp.h_rowidx[:nw[n_in]], 1 << 62, d, hw, beta=1 if sage else 0)
+    b_add = gather_bytes(gp.h_m_ptr, np.arange(n_h), 0, d, hw, beta=1, weighted=False, row_ids=True)
     bytes_by_stage = {"quantize_fwd": b_q_fwd, "aggregate_fwd": b_agg_fwd, "aggregate_bwd_halo": b_bwd_halo,
                       "quantize_bwd": b_q_bwd, "aggregate_bwd_inner": b_bwd_inner, "add_received": b_add}
     k_in = 2 * d if sage else d
@@ -182,7 +181,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(part, gp, bytes_by_stage)
+        cpu = cpu_baseline(part, bytes_by_stage)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -205,9 +204,12 @@ def main():
     print(json.dumps(out))
 
 
-def cpu_baseline(part, gp, bytes_by_stage):
-    """The oracle, as it is, on the host cores: quantise the send set and aggregate forward over a
-    bounded sample of rows; reported in the same GB/s units (bytes of the sampled work / time)."""
+def cpu_baseline(part, bytes_by_stage):
+    """The oracle, as it is, on the host: the quantise and aggregate calls of one full step (send-set
+    quantisation, forward aggregation, both transposed aggregations, gradient quantisation and the
+    received-gradient add) on the same partition, reported with the same bytes model."""
+    import os as _os
+
     from threadpoolctl import threadpool_limits
 
     from oracle import aggregate as OA
@@ -215,27 +217,24 @@ def cpu_baseline(part, gp, bytes_by_stage):
     from quantized_halo_aggregation_amd import synth
 
     n_in, d = part.n_in, part.d
-    rng = np.random.default_rng(0)
-    n_rows_q = min(part.n_h, 50_000)
-    rows_q = np.sort(rng.choice(part.n_h, size=n_rows_q, replace=False))
-    n_rows_a = min(n_in, 100_000)
-    rows_a = np.sort(rng.choice(n_in, size=n_rows_a, replace=False))
+    g = np.random.default_rng(7).standard_normal((n_in, d)).astype(np.float32)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        msg = OL.send_halo(part.x[part.mirror[rows_q]], part.bits[rows_q], synth.QUANT_SEED, 0, 0, n_in)
-        tq = time.perf_counter() - t0
-        x_cols = np.concatenate([part.x, np.zeros((part.n_h, d), np.float32)])
-        x_cols[n_in + rows_q] = msg["received"]
-        t0 = time.perf_counter()
-        OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, x_cols, rows=rows_a)
-        ta = time.perf_counter() - t0
-    frac_q = n_rows_q / part.n_h
-    frac_a = n_rows_a / n_in
-    byts = bytes_by_stage["quantize_fwd"] * frac_q + bytes_by_stage["aggregate_fwd"] * frac_a
-    secs = tq + ta
+        msg = OL.send_halo(part.x[part.mirror], part.bits, synth.QUANT_SEED, 0, 0, n_in)
+        x_cols = np.concatenate([part.x, msg["received"]])
+        if part.wl.model == "gcn":
+            OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, x_cols)
+            dx = OA.gcn_aggregate_t(part.nbr_ptr, part.nbr_idx, part.deg, g).astype(np.float32)
+        else:
+            OA.mean_aggregate(part.nbr_ptr, part.nbr_idx, x_cols)
+            dx = OA.mean_aggregate_t(part.nbr_ptr, part.nbr_idx, g, n_in + part.n_h).astype(np.float32)
+        back = OL.send_halo(dx[n_in:], part.bits, synth.QUANT_SEED, 0, 1, n_in)
+        OA.add_received(dx[:n_in], part.mirror, back["received"])
+        secs = time.perf_counter() - t0
+    byts = sum(bytes_by_stage.values())
     return {"value": round(byts / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle quantise of {n_rows_q} of {part.n_h} halo rows + float64 GCN aggregation of "
-                      f"{n_rows_a} of {n_in} inner rows (same bytes model, {secs:.1f} s, one thread)"}
+            "sample": f"the quantise and aggregate calls of one full layer step ({secs:.1f} s on one thread of "
+                      f"{_os.cpu_count()} host CPUs; same bytes model as value)"}
 
 
 if __name__ == "__main__":

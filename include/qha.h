@@ -79,6 +79,26 @@ const char* qha_last_error(void);
 int qha_pack_layout(const uint8_t* bits, int64_t n_rows, int32_t d,
                     uint32_t* word_offset, uint64_t* total_words);
 
+/* Width classes of a packed buffer whose rows are grouped by width (guide section 9: the sender
+ * may group the boundary vectors it packs by bit width).  Rows start[i] .. start[i+1]-1 all have
+ * width bits[i] and their codes follow each other from word base[i], so row r of class i starts
+ * at base[i] + (r - start[i]) * words(d, bits[i]) with no per-row offset table: a receiver finds a
+ * halo row's codes with arithmetic instead of a dependent memory load.  The layout is the same as
+ * qha_pack_layout's for those rows.  Numbering the halo nodes by importance level keeps the
+ * buffer grouped in every epoch, since a node's width only depends on its level and the epoch's
+ * base width (guide section 9).  qha_pack_classes fills *classes from bits (host) if the rows form
+ * at most QHA_MAX_CLASSES runs of equal width; otherwise it returns UNSUPPORTED and the per-row
+ * word_offset/bits arrays must be used. */
+#define QHA_MAX_CLASSES 8
+typedef struct qha_width_classes {
+  int32_t n;                             /* number of classes, 1 .. QHA_MAX_CLASSES */
+  int32_t bits[QHA_MAX_CLASSES];         /* width of class i: 1, 2, 4, 8 or 32 */
+  int32_t start[QHA_MAX_CLASSES + 1];    /* first row of class i; start[n] = number of rows */
+  uint32_t base[QHA_MAX_CLASSES];        /* first word of class i */
+} qha_width_classes;
+
+int qha_pack_classes(const uint8_t* bits, int64_t n_rows, int32_t d, qha_width_classes* classes);
+
 /* Checks a CSR on the host: rowptr[0] == 0, non-decreasing, rowptr[n_rows] == nnz, every
  * column in [0, n_cols), and (if require_sorted) strictly ascending columns within a row.
  * Returns QHA_OK or INVALID_ARG with the first offending row in qha_last_error(). */
@@ -135,18 +155,28 @@ size_t qha_agg_workspace_bytes(const qha_agg_plan* plan, int32_t d);
 /* Degree normalisation of the GCN aggregation (guide section 2: each term is divided by
  * sqrt(d_v d_u)).  deg (device int32[n]) is a node's global degree without the self-loop
  * (section 7 asks for global, not partition-local, degree); out (device float32[n]):
- *   QHA_NORM_GCN:  1 / sqrt(deg + 1)   -- degree of A + I, so the edge weight is out[v] * out[u]
+ *   QHA_NORM_GCN:  1 / sqrt(deg + 1)   -- degree of A + I; the edge weight is out[v] * out[u]
  *   QHA_NORM_MEAN: deg > 0 ? 1 / deg : 0  (the GraphSAGE neighbour mean of one row)
  * Both computed with correctly rounded sqrt and division. */
 int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, void* stream);
+
+/* Edge weights of a CSR (device): w[e] = (r ? r[i] : 1) * (c ? c[colidx[e]] : 1) in float32 for
+ * every edge e of row i.  With r = c = qha_degree_norm(QHA_NORM_GCN) this is the GCN weight
+ * 1/sqrt(d_v d_u) of guide section 2 as the product of the two factors; with r the mean
+ * normalisation and c = NULL it is the GraphSAGE mean weight.  Set-up work, done once per graph
+ * for the forward CSR and once for its transpose (where r and c swap roles). */
+int qha_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r,
+                     const float* c, float* w, void* stream);
 
 /* Stochastic integer quantisation and packing of message rows (guide section 6):
  *   scale = (max h - min h) / (2^b - 1), q = stochastic_round((h - min h) / scale), and the
  *   zero-point min h travels with scale; b = bits[r] in {1,2,4,8}, or 32 for a raw float32 row.
  * Row r reads x[(row_index ? row_index[r] : r) * ldx + j], j < d (device).  Its stochastic
  * rounding draws come from Philox4x32-10 with counter (node_base + r, j / 8, epoch, stream_id)
- * and key `seed`, so a call is reproducible from its arguments alone.  Writes the packed row at
- * codes[word_offset[r] ...] (layout of qha_pack_layout) and the row's metadata pair
+ * and key `seed`, so a call is reproducible from its arguments alone.  The row's width and the
+ * start of its packed codes come from `classes` (host struct) when it is given, else from
+ * bits[r] and word_offset[r] (device).  Writes the packed row (layout of qha_pack_layout) and
+ * the row's metadata pair
  * meta[2r] = min (the zero-point), meta[2r + 1] = scale (device; min first, then scale, the
  * order in which they travel with the codes).
  * Floating-point steps (all float32, round-to-nearest, no contraction): mn/mx exact; zero-point
@@ -158,44 +188,45 @@ int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, voi
  * UNSUPPORTED (d), HIP.  n_rows == 0 is a no-op. */
 int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int64_t n_rows,
                       int32_t d, const uint8_t* bits, const uint32_t* word_offset,
+                      const qha_width_classes* classes,
                       uint64_t seed, uint32_t epoch, uint32_t stream_id, uint32_t node_base,
                       uint32_t* codes, float* meta, void* stream);
 
 /* Dequantisation fused into the normalised neighbour aggregation (guide sections 2 and 6, the
  * receiver's "dequantize, then aggregate(local_h, remote_h)" of section 11).  For each CSR row
  * i < n_rows (device rowptr[n_rows+1], colidx[nnz]) and its output row v = row_ids ? row_ids[i] : i:
- *   out[v] = (beta ? out[v] : 0) + r[i] * sum over e in row i of c[u] * x~_u,   u = colidx[e]
+ *   out[v] = (beta ? out[v] : 0) + sum over e in row i of w[e] * x~_u,   u = colidx[e]
  *   x~_u = x_inner[u * ldx + j]                                if u < n_inner
  *        = meta[2k + 1] * q_k[j] + meta[2k]  (float32)          if u = n_inner + k, k < n_halo
- * (the raw float when bits[k] == 32).  r (device float[n_rows]) and c (device
- * float[n_inner + n_halo]) may be NULL for 1.0; for the GCN weight 1/sqrt(d_v d_u) pass
- * r = c = qha_degree_norm(.., QHA_NORM_GCN).  codes/word_offset/bits/meta are the received halo
- * messages in qha_quantize_pack's layout (device; may be NULL when n_halo == 0).  row_ids
- * (device, nullable) must be distinct.  plan may be NULL (one item per row); otherwise it must
- * have been built for this rowptr, and a plan with skip_empty requires beta == 1.  workspace
- * (device, 16-byte aligned) must hold qha_agg_workspace_bytes(plan, d) bytes.  beta is 0 or 1.
- * Each product c[u] * x~_u (exact in float64) is summed in float64 in edge order (chunks of a
- * split row separately, then in chunk order), scaled by r[i], added to the old value when
- * beta = 1 and rounded to float32 once; results are deterministic.
- * Errors: INVALID_ARG, UNSUPPORTED (d), WORKSPACE, HIP. */
+ * (the raw float when the row's width is 32).  w (device float[nnz], see qha_edge_weights) may
+ * be NULL for 1.0.  codes and meta are the received halo messages in qha_quantize_pack's layout;
+ * each halo row's width and code offset come from `classes` (host struct) if given, else from
+ * bits and word_offset (device); all may be NULL when n_halo == 0.  row_ids (device, nullable)
+ * must be distinct.  plan may be NULL (one item per row); otherwise it must have been built for
+ * this rowptr, and a plan with skip_empty requires beta == 1.  workspace (device, 16-byte
+ * aligned) must hold qha_agg_workspace_bytes(plan, d) bytes.  beta is 0 or 1.  Each product
+ * w[e] * x~_u (exact in float64) is summed in float64 in edge order (chunks of a split row
+ * separately, then in chunk order), added to the old value when beta = 1 and rounded to float32
+ * once; results are deterministic.  Errors: INVALID_ARG, UNSUPPORTED (d), WORKSPACE, HIP. */
 int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
-                              const int32_t* row_ids, const qha_agg_plan* plan,
-                              const float* r, const float* c,
+                              const float* w, const int32_t* row_ids, const qha_agg_plan* plan,
                               const float* x_inner, int64_t ldx, int64_t n_inner,
                               const uint32_t* codes, const uint32_t* word_offset,
-                              const uint8_t* bits, const float* meta, int64_t n_halo,
+                              const uint8_t* bits, const qha_width_classes* classes,
+                              const float* meta, int64_t n_halo,
                               int32_t d, int32_t beta, float* out, int64_t ldo,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Transposed aggregation for embedding gradients (guide sections 3 and 11: gradients flow back
  * along the same cross-partition dependencies).  Given the transpose of the forward CSR
- * (qha_csr_transpose: row u lists the forward rows v that gather u), for u < n_rows:
- *   grad_in[u] = (beta ? grad_in[u] : 0) + r[u] * sum over e in row u of c[v] * grad_out[v]
- * with v = rowidx[e] < n_grad_rows.  With r and c the forward's c and r this is the adjoint of
- * qha_dequant_aggregate_fwd.  Same plan / workspace / beta / determinism rules.  Pass a row
- * range [u0, u1) by offsetting colptr, r and grad_in. */
+ * (qha_csr_transpose: row u lists the forward rows v that gather u) and its edge weights
+ * (qha_edge_weights with the forward's r and c swapped), for u < n_rows:
+ *   grad_in[u] = (beta ? grad_in[u] : 0) + sum over e in row u of w[e] * grad_out[v]
+ * with v = rowidx[e] < n_grad_rows: the adjoint of qha_dequant_aggregate_fwd.  Same plan /
+ * workspace / beta / precision / determinism rules.  Pass a row range [u0, u1) by offsetting
+ * colptr and grad_in (w and rowidx are indexed by the absolute edge numbers in colptr). */
 int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx,
-                      const qha_agg_plan* plan, const float* r, const float* c,
+                      const float* w, const qha_agg_plan* plan,
                       const float* grad_out, int64_t ldg, int64_t n_grad_rows,
                       int32_t d, int32_t beta, float* grad_in, int64_t ldi,
                       void* workspace, size_t workspace_bytes, void* stream);

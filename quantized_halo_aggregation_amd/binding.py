@@ -55,6 +55,14 @@ class AggPlanStruct(C.Structure):
                 ("items", _vp), ("split_row", _vp), ("split_ptr", _vp)]
 
 
+MAX_CLASSES = 8
+
+
+class WidthClassesStruct(C.Structure):
+    _fields_ = [("n", _i32), ("bits", _i32 * MAX_CLASSES), ("start", _i32 * (MAX_CLASSES + 1)),
+                ("base", _u32 * MAX_CLASSES)]
+
+
 def _sig(name, res, *args):
     f = getattr(_lib, name)
     f.restype = res
@@ -67,23 +75,27 @@ _abi_version = _sig("qha_abi_version", _i32)
 _status_string = _sig("qha_status_string", C.c_char_p, _i32)
 _last_error = _sig("qha_last_error", C.c_char_p)
 _pack_layout = _sig("qha_pack_layout", _i32, _vp, _i64, _i32, _vp, _P(_u64))
+_pack_classes = _sig("qha_pack_classes", _i32, _vp, _i64, _i32, _P(WidthClassesStruct))
+_edge_weights = _sig("qha_edge_weights", _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp)
 _validate_csr = _sig("qha_validate_csr", _i32, _i64, _i64, _vp, _vp, _i32)
 _csr_transpose = _sig("qha_csr_transpose", _i32, _i64, _i64, _vp, _vp, _vp, _vp)
 _plan_size = _sig("qha_agg_plan_size", _i32, _i64, _vp, _i32, _i32, _i32, _P(AggPlanStruct))
 _plan_fill = _sig("qha_agg_plan_fill", _i32, _vp, _P(AggPlanStruct), _vp, _vp, _vp)
 _plan_ws = _sig("qha_agg_workspace_bytes", _sz, _P(AggPlanStruct), _i32)
 _degree_norm = _sig("qha_degree_norm", _i32, _vp, _i64, _i32, _vp, _vp)
-_quantize_pack = _sig("qha_quantize_pack", _i32, _vp, _i64, _vp, _i64, _i32, _vp, _vp, _u64, _u32, _u32, _u32,
-                      _vp, _vp, _vp)
-_dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _vp,
-                              _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
-_aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _P(AggPlanStruct), _vp, _vp, _vp, _i64, _i64,
-                      _i32, _i32, _vp, _i64, _vp, _sz, _vp)
+_quantize_pack = _sig("qha_quantize_pack", _i32, _vp, _i64, _vp, _i64, _i32, _vp, _vp, _P(WidthClassesStruct), _u64,
+                      _u32, _u32, _u32, _vp, _vp, _vp)
+_dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp, _vp, _vp, _P(AggPlanStruct), _vp,
+                              _i64, _i64, _vp, _vp, _vp, _P(WidthClassesStruct), _vp, _i64, _i32, _i32, _vp, _i64, _vp,
+                              _sz, _vp)
+_aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64, _i64, _i32, _i32,
+                      _vp, _i64, _vp, _sz, _vp)
 _dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
                       _i64, _i32, _vp, _i64, _i32, _vp, _sz, _vp)
 _dense_ws = _sig("qha_dense_project_workspace", _sz, _i32, _i32, _i64, _i64, _i64)
 
-EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_layout", "qha_validate_csr",
+EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_layout", "qha_pack_classes",
+            "qha_edge_weights", "qha_validate_csr",
             "qha_csr_transpose", "qha_agg_plan_size", "qha_agg_plan_fill", "qha_agg_workspace_bytes",
             "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_aggregate_bwd",
             "qha_dense_project", "qha_dense_project_workspace"]
@@ -171,6 +183,17 @@ def pack_layout(bits, d: int):
     return off, int(total.value)
 
 
+def pack_classes(bits, d: int):
+    """Width classes of a width-grouped row order, or None if the rows form too many runs."""
+    bits, pb = _host(bits, np.uint8, "bits")
+    st = WidthClassesStruct()
+    status = _pack_classes(pb, bits.size, int(d), C.byref(st))
+    if status == QHA_ERR_UNSUPPORTED and bits.size > 0:
+        return None
+    _check(status, "qha_pack_classes")
+    return st
+
+
 def validate_csr(rowptr, colidx, n_cols: int, require_sorted: bool = True):
     rowptr, pr = _host(rowptr, np.int32, "rowptr")
     colidx, pc = _host(colidx, np.int32, "colidx")
@@ -227,6 +250,10 @@ def _plan_ref(plan):
     return None if plan is None else C.byref(plan.struct)
 
 
+def _cls_ref(classes):
+    return None if classes is None else C.byref(classes)
+
+
 def dense_project_workspace(trans_a: int, trans_b: int, m: int, n: int, k: int) -> int:
     return int(_dense_ws(int(trans_a), int(trans_b), int(m), int(n), int(k)))
 
@@ -241,20 +268,29 @@ def degree_norm(deg, kind: int, out, stream=None):
                         _stream(stream)), "qha_degree_norm")
 
 
-def quantize_pack(x, row_index, n_rows: int, bits, word_offset, seed: int, epoch: int, stream_id: int,
+def edge_weights(rowptr, colidx, r, c, w, stream=None):
+    import torch
+    _check(_edge_weights(rowptr.numel() - 1, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"),
+                         _dev(r, torch.float32, "r", allow_none=True), _dev(c, torch.float32, "c", allow_none=True),
+                         _dev(w, torch.float32, "w"), _stream(stream)), "qha_edge_weights")
+
+
+def quantize_pack(x, row_index, n_rows: int, bits, word_offset, classes, seed: int, epoch: int, stream_id: int,
                   node_base: int, codes, meta, stream=None):
-    """meta receives (min, scale) per row: a float32 tensor of n_rows * 2 elements."""
+    """meta receives (min, scale) per row: a float32 tensor of n_rows * 2 elements.  classes (from
+    pack_classes) describes a width-grouped layout; bits / word_offset may then be None."""
     import torch
     px, ldx = _rows(x, "x")
     d = x.shape[1]
     _check(_quantize_pack(px, ldx, _dev(row_index, torch.int32, "row_index", allow_none=True), int(n_rows), int(d),
-                          _dev(bits, torch.uint8, "bits"), _dev32(word_offset, "word_offset"),
+                          _dev(bits, torch.uint8, "bits", allow_none=True),
+                          None if word_offset is None else _dev32(word_offset, "word_offset"), _cls_ref(classes),
                           int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch), int(stream_id), int(node_base),
                           _dev32(codes, "codes"), _dev(meta, torch.float32, "meta"), _stream(stream)),
            "qha_quantize_pack")
 
 
-def dequant_aggregate_fwd(rowptr, colidx, plan, r, c, x_inner, n_inner: int, codes, word_offset, bits, meta,
+def dequant_aggregate_fwd(rowptr, colidx, w, plan, x_inner, n_inner: int, codes, word_offset, bits, classes, meta,
                           n_halo: int, beta: int, out, workspace=None, row_ids=None, n_rows=None, stream=None):
     import torch
     n_rows = rowptr.numel() - 1 if n_rows is None else int(n_rows)
@@ -266,17 +302,17 @@ def dequant_aggregate_fwd(rowptr, colidx, plan, r, c, x_inner, n_inner: int, cod
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_dequant_aggregate_fwd(
         n_rows, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"),
-        _dev(row_ids, torch.int32, "row_ids", allow_none=True), _plan_ref(plan),
-        _dev(r, torch.float32, "r", allow_none=True), _dev(c, torch.float32, "c", allow_none=True),
-        px, ldx, int(n_inner),
+        _dev(w, torch.float32, "w", allow_none=True), _dev(row_ids, torch.int32, "row_ids", allow_none=True),
+        _plan_ref(plan), px, ldx, int(n_inner),
         _dev32(codes, "codes") if halo else None,
-        _dev32(word_offset, "word_offset") if halo else None,
-        _dev(bits, torch.uint8, "bits") if halo else None,
+        _dev32(word_offset, "word_offset") if (halo and word_offset is not None) else None,
+        _dev(bits, torch.uint8, "bits") if (halo and bits is not None) else None,
+        _cls_ref(classes) if halo else None,
         _dev(meta, torch.float32, "meta") if halo else None,
         int(n_halo), int(d), int(beta), po, ldo, ws_ptr, ws_bytes, _stream(stream)), "qha_dequant_aggregate_fwd")
 
 
-def aggregate_bwd(colptr, rowidx, plan, r, c, grad_out, n_grad_rows: int, beta: int, grad_in, workspace=None,
+def aggregate_bwd(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, beta: int, grad_in, workspace=None,
                   n_rows=None, stream=None):
     import torch
     n_rows = colptr.numel() - 1 if n_rows is None else int(n_rows)
@@ -286,9 +322,8 @@ def aggregate_bwd(colptr, rowidx, plan, r, c, grad_out, n_grad_rows: int, beta: 
     ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_aggregate_bwd(n_rows, _dev(colptr, torch.int32, "colptr"), _dev(rowidx, torch.int32, "rowidx"),
-                          _plan_ref(plan), _dev(r, torch.float32, "r", allow_none=True),
-                          _dev(c, torch.float32, "c", allow_none=True), pg, ldg, int(n_grad_rows), int(d), int(beta),
-                          pi, ldi, ws_ptr, ws_bytes, _stream(stream)), "qha_aggregate_bwd")
+                          _dev(w, torch.float32, "w", allow_none=True), _plan_ref(plan), pg, ldg, int(n_grad_rows),
+                          int(d), int(beta), pi, ldi, ws_ptr, ws_bytes, _stream(stream)), "qha_aggregate_bwd")
 
 
 def dense_project(trans_a: int, trans_b: int, a, b, beta: int, c, prologue: int = PRO_NONE, aux=None,

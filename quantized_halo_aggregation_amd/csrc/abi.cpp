@@ -86,6 +86,34 @@ void fill_plan_args(qha::GatherArgs& g, const qha_agg_plan* plan, int64_t n_rows
   g.partial = static_cast<double*>(ws);
 }
 
+uint64_t row_words(int32_t d, uint32_t b) { return b == 32 ? static_cast<uint64_t>(d) : (static_cast<uint64_t>(d) * b + 31) / 32; }
+
+// Checks a host class table against the row count and copies it into kernel arguments.
+int take_classes(const qha_width_classes* cls, int64_t n_rows, int32_t d, qha::Classes* out) {
+  std::memset(out, 0, sizeof(*out));
+  if (!cls) return QHA_OK;
+  if (cls->n < 1 || cls->n > QHA_MAX_CLASSES) return fail(QHA_ERR_INVALID_ARG, "classes: n = %d out of range", cls->n);
+  if (cls->start[0] != 0 || cls->start[cls->n] != n_rows)
+    return fail(QHA_ERR_INVALID_ARG, "classes must cover rows 0 .. %lld exactly", (long long)n_rows);
+  uint64_t expect = cls->base[0];
+  for (int i = 0; i < cls->n; ++i) {
+    const int32_t b = cls->bits[i];
+    if (!(b == 1 || b == 2 || b == 4 || b == 8 || b == 32)) return fail(QHA_ERR_INVALID_ARG, "classes: width %d", b);
+    if (cls->start[i + 1] < cls->start[i]) return fail(QHA_ERR_INVALID_ARG, "classes: starts decrease");
+    if (cls->base[i] != expect) return fail(QHA_ERR_INVALID_ARG, "classes: class %d does not follow the previous one", i);
+    expect += static_cast<uint64_t>(cls->start[i + 1] - cls->start[i]) * row_words(d, static_cast<uint32_t>(b));
+    if (expect > 0xFFFFFFFFull) return fail(QHA_ERR_INVALID_ARG, "classes: buffer exceeds 2^32-1 words");
+  }
+  out->n = cls->n;
+  for (int i = 0; i < cls->n; ++i) {
+    out->bits[i] = cls->bits[i];
+    out->start[i] = cls->start[i];
+    out->base[i] = cls->base[i];
+  }
+  out->start[cls->n] = cls->start[cls->n];
+  return QHA_OK;
+}
+
 // Walks the rows once and either counts (out == nullptr) or writes the plan's arrays.
 struct PlanWalk {
   int64_t items = 0, split_items = 0, split_rows = 0;
@@ -186,6 +214,36 @@ int qha_pack_layout(const uint8_t* bits, int64_t n_rows, int32_t d, uint32_t* wo
   return ok();
 }
 
+int qha_pack_classes(const uint8_t* bits, int64_t n_rows, int32_t d, qha_width_classes* classes) {
+  if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
+  if (!classes || (n_rows > 0 && !bits)) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  std::memset(classes, 0, sizeof(*classes));
+  uint64_t words = 0;
+  int n = 0;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const uint32_t b = bits[r];
+    if (!(b == 1 || b == 2 || b == 4 || b == 8 || b == 32))
+      return fail(QHA_ERR_INVALID_ARG, "bits[%lld] = %u is not in {1,2,4,8,32}", (long long)r, b);
+    if (n == 0 || static_cast<uint32_t>(classes->bits[n - 1]) != b) {
+      if (n == QHA_MAX_CLASSES) return fail(QHA_ERR_UNSUPPORTED, "rows form more than %d runs of equal width", QHA_MAX_CLASSES);
+      classes->bits[n] = static_cast<int32_t>(b);
+      classes->start[n] = static_cast<int32_t>(r);
+      classes->base[n] = static_cast<uint32_t>(words);
+      ++n;
+    }
+    words += row_words(d, b);
+    if (words > 0xFFFFFFFFull) return fail(QHA_ERR_INVALID_ARG, "packed buffer exceeds 2^32-1 words");
+  }
+  if (n == 0) {                       // no rows: one empty class keeps the table well formed
+    classes->bits[0] = 32;
+    n = 1;
+  }
+  classes->n = n;
+  classes->start[n] = static_cast<int32_t>(n_rows);
+  return ok();
+}
+
 int qha_validate_csr(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, const int32_t* colidx, int32_t require_sorted) {
   if (n_rows < 0 || n_cols < 0 || n_rows > kMaxIndex || n_cols > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad sizes");
   if (!rowptr) return fail(QHA_ERR_INVALID_ARG, "rowptr is NULL");
@@ -265,20 +323,32 @@ int qha_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, voi
   return hip_status(qha::launch_degree_norm(deg, n, kind, out, static_cast<hipStream_t>(stream)), "degree_norm");
 }
 
+int qha_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r, const float* c,
+                     float* w, void* stream) {
+  if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
+  if (n_rows == 0) return ok();
+  if (!rowptr || !colidx || !w) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  return hip_status(qha::launch_edge_weights(n_rows, rowptr, colidx, r, c, w, static_cast<hipStream_t>(stream)),
+                    "edge_weights");
+}
+
 int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int64_t n_rows, int32_t d,
-                      const uint8_t* bits, const uint32_t* word_offset, uint64_t seed, uint32_t epoch,
-                      uint32_t stream_id, uint32_t node_base, uint32_t* codes, float* meta, void* stream) {
+                      const uint8_t* bits, const uint32_t* word_offset, const qha_width_classes* classes,
+                      uint64_t seed, uint32_t epoch, uint32_t stream_id, uint32_t node_base, uint32_t* codes,
+                      float* meta, void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad n_rows");
   if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
   if (n_rows == 0) return ok();
   int st = check_rows("x", x, ldx, d);
   if (st) return st;
-  if (!bits || !word_offset || !codes || !meta) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned4(codes) || !aligned8(meta) || !aligned4(word_offset) || (row_index && !aligned4(row_index)))
+  if (!codes || !meta || (!classes && (!bits || !word_offset))) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned4(codes) || !aligned8(meta) || (word_offset && !aligned4(word_offset)) || (row_index && !aligned4(row_index)))
     return fail(QHA_ERR_INVALID_ARG, "misaligned array");
   if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_rows) - 1 > 0xFFFFFFFFull)
     return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
   qha::QuantArgs a;
+  st = take_classes(classes, n_rows, d, &a.cls);
+  if (st) return st;
   a.x = x;
   a.ldx = ldx;
   a.row_index = row_index;
@@ -295,11 +365,12 @@ int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int
   return hip_status(qha::launch_quantize(a, d, static_cast<hipStream_t>(stream)), "quantize_pack");
 }
 
-int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const int32_t* row_ids,
-                              const qha_agg_plan* plan, const float* r, const float* c, const float* x_inner,
-                              int64_t ldx, int64_t n_inner, const uint32_t* codes, const uint32_t* word_offset,
-                              const uint8_t* bits, const float* meta, int64_t n_halo, int32_t d, int32_t beta,
-                              float* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* w,
+                              const int32_t* row_ids, const qha_agg_plan* plan, const float* x_inner, int64_t ldx,
+                              int64_t n_inner, const uint32_t* codes, const uint32_t* word_offset,
+                              const uint8_t* bits, const qha_width_classes* classes, const float* meta,
+                              int64_t n_halo, int32_t d, int32_t beta, float* out, int64_t ldo, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex || n_inner < 0 || n_halo < 0 || n_inner + n_halo > kMaxIndex)
     return fail(QHA_ERR_INVALID_ARG, "bad sizes");
   if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
@@ -312,21 +383,24 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
     st = check_rows("x_inner", x_inner, ldx, d);
     if (st) return st;
   }
-  if (n_halo > 0 && (!codes || !word_offset || !bits || !meta))
-    return fail(QHA_ERR_INVALID_ARG, "halo message arrays are NULL");
-  if (n_halo > 0 && (!aligned8(meta) || !aligned4(codes) || !aligned4(word_offset)))
-    return fail(QHA_ERR_INVALID_ARG, "misaligned halo message arrays");
-  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
-  if (st) return st;
   qha::GatherArgs g;
   std::memset(&g, 0, sizeof(g));
+  if (n_halo > 0) {
+    if (!codes || !meta || (!classes && (!word_offset || !bits)))
+      return fail(QHA_ERR_INVALID_ARG, "halo message arrays are NULL");
+    if (!aligned8(meta) || !aligned4(codes) || (word_offset && !aligned4(word_offset)))
+      return fail(QHA_ERR_INVALID_ARG, "misaligned halo message arrays");
+    st = take_classes(classes, n_halo, d, &g.cls);
+    if (st) return st;
+  }
+  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
+  if (st) return st;
   g.n_rows = n_rows;
   g.rowptr = rowptr;
   g.colidx = colidx;
   g.row_ids = row_ids;
   fill_plan_args(g, plan, n_rows, workspace);
-  g.rs = r;
-  g.cs = c;
+  g.w = w;
   g.x = x_inner;
   g.ldx = ldx;
   g.n_inner = n_inner;
@@ -341,9 +415,9 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
   return hip_status(qha::launch_gather(g, d, n_halo > 0, static_cast<hipStream_t>(stream)), "dequant_aggregate_fwd");
 }
 
-int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const qha_agg_plan* plan,
-                      const float* r, const float* c, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
-                      int32_t d, int32_t beta, float* grad_in, int64_t ldi, void* workspace, size_t workspace_bytes,
+int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,
+                      const qha_agg_plan* plan, const float* grad_out, int64_t ldg, int64_t n_grad_rows, int32_t d,
+                      int32_t beta, float* grad_in, int64_t ldi, void* workspace, size_t workspace_bytes,
                       void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex || n_grad_rows < 0 || n_grad_rows > kMaxIndex)
     return fail(QHA_ERR_INVALID_ARG, "bad sizes");
@@ -365,8 +439,7 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
   g.rowptr = colptr;
   g.colidx = rowidx;
   fill_plan_args(g, plan, n_rows, workspace);
-  g.rs = r;
-  g.cs = c;
+  g.w = w;
   g.x = grad_out;
   g.ldx = ldg;
   g.n_inner = n_grad_rows;

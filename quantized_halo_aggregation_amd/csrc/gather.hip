@@ -8,11 +8,16 @@
 // consecutive short rows, or one chunk of a heavy row -- and streams through the item's
 // contiguous edge list in batches of B edges.  Its 64 lanes split the d features (d/64
 // contiguous floats per lane), so every neighbour costs one coalesced d*4-byte load.  Column
-// indices, edge weights and halo metadata are wavefront-uniform and come through the scalar unit;
-// only feature rows and packed code words use the vector memory pipe.  A batch runs in phases:
-// (1) scalar loads of the batch's weights and halo metadata, vector loads of its inner rows and
-// the scalar load of the next batch's column indices, all in flight together; (2) after one wait,
-// the code words of its halo rows (one word per lane holds all of its codes); (3) the sums.  Row
+// indices and edge weights are wavefront-uniform and live in scalar registers while a batch is
+// summed.  A batch runs in phases:
+// (1) vector loads of its inner rows, of its halo rows' code words (one word per lane holds all of
+// its codes) and (min, scale) pairs, and of the next batch's column indices and edge weights (one
+// edge per lane, read out with readlane when that batch starts), all in flight together; (2) the
+// sums.  When the received buffer is
+// grouped by width (the guide's section 9 packing), a halo row's code offset is arithmetic on its
+// index -- its class comes from one ballot against the class starts held one per lane -- so the
+// code load needs no earlier load; with a per-row offset table the code words are fetched in an
+// extra phase once the offsets have arrived.  Row
 // boundaries inside a group are tracked with scalar compares against the group's row pointers,
 // held one per lane and read with readlane, so crossing a row costs a store and no load.
 // A halo value is dequantised in float32 (scale * q + min, no contraction); every product is then
@@ -35,7 +40,7 @@ __device__ __forceinline__ cptr<T> cst(const T* p) {
 }
 
 constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
-constexpr int batch_of(int D, bool halo) { return (D >= 512 || halo) ? 8 : 16; }
+constexpr int batch_of(int D, bool halo) { return D >= 512 ? 8 : 16; }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 
 __device__ __forceinline__ int rdlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -80,7 +85,19 @@ __device__ __forceinline__ void load_row(const float* p, float (&xv)[VEC]) {
   }
 }
 
-template <int D, bool HALO, bool BETA>
+// Width and first code word of halo row k of a width-grouped buffer; the class table is held one
+// class per lane (v_cstart: first row, INT_MAX past the last class), so the class is the number of
+// lanes whose class starts at or before k, minus one.
+template <int D>
+__device__ __forceinline__ void class_of(int32_t v_cstart, int32_t v_cbits, uint32_t v_cbase, int32_t k, uint32_t& b,
+                                         uint32_t& off) {
+  const int c = __popcll(__ballot(v_cstart <= k)) - 1;
+  b = static_cast<uint32_t>(rdlane(v_cbits, c));
+  const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (((b << log2i(D)) + 31u) >> 5);
+  off = static_cast<uint32_t>(rdlane(static_cast<int>(v_cbase), c)) + static_cast<uint32_t>(k - rdlane(v_cstart, c)) * words;
+}
+
+template <int D, bool HALO, bool BETA, bool GROUPED>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;           // lanes that own features
@@ -108,12 +125,25 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
   const bool split = item < a.n_split_items;
 
-  // the group's row ends, row scales and output rows, one row per lane (rows of a group are
-  // never empty, so each edge closes at most one row)
+  // the group's row ends and output rows, one row per lane (rows of a group are never empty, so
+  // each edge closes at most one row)
   const int li = lane < nrows ? lane : nrows - 1;
   const int32_t v_end = split ? 0x7FFFFFFF : a.rowptr[row0 + li + 1];
-  const float v_rs = (a.rs != nullptr) ? a.rs[row0 + li] : 1.0f;
   const int32_t v_out = (a.row_ids != nullptr) ? a.row_ids[row0 + li] : row0 + li;
+
+  // width classes of a grouped halo buffer, class i in lane i
+  int32_t v_cstart = 0x7FFFFFFF, v_cbits = 0;
+  uint32_t v_cbase = 0;
+  if constexpr (HALO && GROUPED) {
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+      if (lane == c && c < a.cls.n) {
+        v_cstart = a.cls.start[c];
+        v_cbits = a.cls.bits[c];
+        v_cbase = a.cls.base[c];
+      }
+    }
+  }
 
   double acc[VEC];
 #pragma unroll
@@ -122,7 +152,6 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   int32_t cur_end = rdlane(v_end, 0);
 
   auto flush = [&]() {                          // write row `cur` and start the next one
-    const double r = static_cast<double>(rdlanef(v_rs, cur));
     const int64_t orow = rdlane(v_out, cur);
     float* dst = a.out + orow * a.ldo + j0;
     if (owner) {
@@ -131,10 +160,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
         float old[VEC];
         load_row<VEC>(dst, old);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + r * acc[v]);
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
       } else {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(r * acc[v]);
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
       }
       store_row<VEC>(dst, res);
     }
@@ -144,47 +173,78 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     cur_end = rdlane(v_end, cur < nrows ? cur : nrows - 1);
   };
 
-  int32_t u_next[B];
-  if (e0 < e1) {
-#pragma unroll
-    for (int i = 0; i < B; ++i) u_next[i] = cst(a.colidx)[min(e0 + i, e1 - 1)];
-  }
+  // the next batch's column indices and weights, edge i of the batch in lane i (vector loads, so
+  // the prefetch holds no scalar registers)
+  int32_t v_u = 0;
+  float v_w = 1.0f;
+  const bool weighted = a.w != nullptr;
+  auto fetch = [&](int32_t eb) {
+    const int32_t ei = min(eb + lane, e1 - 1);
+    v_u = a.colidx[ei];
+    if (weighted) v_w = a.w[ei];
+  };
+  if (e0 < e1) fetch(e0);
 
   for (int32_t e = e0; e < e1; e += B) {
     int32_t u[B];
-#pragma unroll
-    for (int i = 0; i < B; ++i) u[i] = u_next[i];
-
-    // phase 1: weights, halo metadata and inner rows; the next batch's indices
-    float cw[B];
-    float xv[B][VEC];
-    uint32_t woff[B], bw[B];
-    float mn[B], sc[B];
+    float ww[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      cw[i] = a.cs ? cst(a.cs)[u[i]] : 1.0f;
+      u[i] = rdlane(v_u, i);
+      ww[i] = rdlanef(v_w, i);
+    }
+
+    // phase 1: inner rows, halo metadata and (grouped layout) halo code words.  A halo row's
+    // (min, scale) pair shares the registers of its value until it is dequantised.
+    constexpr bool PAIR_IN_XV = VEC >= 2;
+    float xv[B][VEC];
+    uint32_t cwd[B][CW];
+    uint32_t woff[B], bw[B];
+    float mn1[B], sc1[B];                      // (min, scale) when VEC == 1
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
       if (HALO && u[i] >= a.n_inner) {
-        const int64_t k = static_cast<int64_t>(u[i]) - a.n_inner;
-        woff[i] = cst(a.word_offset)[k];
-        if constexpr (D >= 32) {
-          // the width follows from the row's word count (unique for d >= 32)
-          bw[i] = ((cst(a.word_offset)[k + 1] - woff[i]) << 5) >> log2i(D);
+        const int32_t k = u[i] - static_cast<int32_t>(a.n_inner);
+        uint32_t b = 0, off = 0;
+        if constexpr (GROUPED) {
+          class_of<D>(v_cstart, v_cbits, v_cbase, k, b, off);
         } else {
-          bw[i] = cst(a.bits)[k];
+          woff[i] = cst(a.word_offset)[k];
+          if constexpr (D >= 32) {
+            // the width follows from the row's word count (unique for d >= 32)
+            bw[i] = ((cst(a.word_offset)[k + 1] - woff[i]) << 5) >> log2i(D);
+          } else {
+            bw[i] = cst(a.bits)[k];
+          }
         }
-        mn[i] = cst(a.meta)[2 * k];
-        sc[i] = cst(a.meta)[2 * k + 1];
+        if (!GROUPED || b != 32u) {
+          const float2 ms = *reinterpret_cast<const float2*>(a.meta + 2 * static_cast<int64_t>(k));
+          if constexpr (PAIR_IN_XV) {
+            xv[i][0] = ms.x;
+            xv[i][1] = ms.y;
+          } else {
+            mn1[i] = ms.x;
+            sc1[i] = ms.y;
+          }
+        }
+        if constexpr (GROUPED) {
+          const uint32_t* row = a.codes + off;
+          if (b == 32u) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
+          } else {
+            const uint32_t pos = static_cast<uint32_t>(j0) * b;
+            cwd[i][0] = row[pos >> 5];
+            if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
+          }
+        }
       } else {
         load_row<VEC>(a.x + static_cast<int64_t>(u[i]) * a.ldx + j0, xv[i]);
       }
     }
-    if (e + B < e1) {
-#pragma unroll
-      for (int i = 0; i < B; ++i) u_next[i] = cst(a.colidx)[min(e + B + i, e1 - 1)];
-    }
-    // phase 2: the code words of the halo rows
-    uint32_t cwd[B][CW];
-    if (HALO) {
+    if (e + B < e1) fetch(e + B);
+    // phase 2 (per-row offset table): the code words of the halo rows, once their offsets are in
+    if constexpr (HALO && !GROUPED) {
 #pragma unroll
       for (int i = 0; i < B; ++i) {
         if (u[i] >= a.n_inner) {
@@ -207,16 +267,24 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       const int32_t p = e + i;
       if (p < e1) {
         if (HALO && u[i] >= a.n_inner) {
-          const uint32_t b = bw[i];
+          uint32_t b;
+          if constexpr (GROUPED) {
+            uint32_t off_unused;
+            class_of<D>(v_cstart, v_cbits, v_cbase, u[i] - static_cast<int32_t>(a.n_inner), b, off_unused);
+          } else {
+            b = bw[i];
+          }
           if (b != 32u) {
-            if (width_ok(b)) {
+            if (GROUPED || width_ok(b)) {
+              const float mn = PAIR_IN_XV ? xv[i][0] : mn1[i];
+              const float sc = PAIR_IN_XV ? xv[i][1 % VEC] : sc1[i];
               const uint32_t mask = (1u << b) - 1u;
               const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
 #pragma unroll
               for (int v = 0; v < VEC; ++v) {
                 const uint32_t bitpos = sh + static_cast<uint32_t>(v) * b;
-                const uint32_t w = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
-                xv[i][v] = dequant(sc[i], w & mask, mn[i]);
+                const uint32_t wd = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
+                xv[i][v] = dequant(sc, wd & mask, mn);
               }
             } else {
 #pragma unroll
@@ -224,9 +292,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
             }
           }
         }
-        const double w = static_cast<double>(cw[i]);
+        const double wt = static_cast<double>(ww[i]);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fma(w, static_cast<double>(xv[i][v]), acc[v]);
+        for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
         if (p + 1 == cur_end) flush();
       }
     }
@@ -243,7 +311,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
 }
 
-// Adds the partial sums of every split row in chunk order, scales and writes the row.
+// Adds the partial sums of every split row in chunk order and writes the row.
 template <int D>
 __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
@@ -263,12 +331,32 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + a.partial[static_cast<int64_t>(i) * D + j0 + v];
   }
-  const double r = a.rs ? static_cast<double>(a.rs[row]) : 1.0;
   const int64_t orow = a.row_ids ? a.row_ids[row] : row;
   float* dst = a.out + orow * a.ldo + j0;
 #pragma unroll
   for (int v = 0; v < VEC; ++v)
-    dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + r * acc[v] : r * acc[v]);
+    dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
+}
+
+__global__ __launch_bounds__(256) void edge_weights_kernel(int64_t n_rows, const int32_t* rowptr,
+                                                           const int32_t* colidx, const float* r, const float* c,
+                                                           float* w) {
+  // one wavefront per row: the row factor is read once, the column factors are gathered
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 +
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (row >= n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const float rf = r ? r[row] : 1.0f;
+  for (int32_t e = rowptr[row] + lane; e < rowptr[row + 1]; e += 64)
+    w[e] = __fmul_rn(rf, c ? c[colidx[e]] : 1.0f);
+}
+
+template <int D, bool HALO, bool BETA>
+void launch_variant(const GatherArgs& a, dim3 grid, hipStream_t s) {
+  if (HALO && a.cls.n > 0)
+    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, false>), grid, dim3(256), 0, s, a);
 }
 
 template <int D>
@@ -276,11 +364,11 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, hipStream_t s) {
   if (a.n_items > 0) {
     const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
     if (with_halo) {
-      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, true, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gather_kernel<D, true, false>), grid, dim3(256), 0, s, a);
+      if (a.beta) launch_variant<D, true, true>(a, grid, s);
+      else launch_variant<D, true, false>(a, grid, s);
     } else {
-      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gather_kernel<D, false, false>), grid, dim3(256), 0, s, a);
+      if (a.beta) launch_variant<D, false, true>(a, grid, s);
+      else launch_variant<D, false, false>(a, grid, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -305,6 +393,14 @@ hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStre
     case 512: return launch_gather_d<512>(a, with_halo, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r,
+                               const float* c, float* w, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(edge_weights_kernel, dim3(static_cast<unsigned>((n_rows + 3) / 4)), dim3(256), 0, s, n_rows,
+                     rowptr, colidx, r, c, w);
+  return hipGetLastError();
 }
 
 }  // namespace qha

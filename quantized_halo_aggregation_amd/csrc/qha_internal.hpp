@@ -8,6 +8,17 @@
 
 namespace qha {
 
+constexpr int kMaxClasses = 8;
+
+// Width classes of a width-grouped packed buffer (copied into kernel arguments); n == 0 means
+// the per-row bits / word_offset arrays describe the layout instead.
+struct Classes {
+  int32_t n;
+  int32_t bits[kMaxClasses];
+  int32_t start[kMaxClasses + 1];
+  uint32_t base[kMaxClasses];
+};
+
 struct QuantArgs {
   const float* x;
   int64_t ldx;
@@ -15,13 +26,14 @@ struct QuantArgs {
   int64_t n_rows;
   const uint8_t* bits;
   const uint32_t* word_offset;
+  Classes cls;
   uint32_t seed_lo, seed_hi, epoch, stream_id, node_base;
   uint32_t* codes;
   float* meta;          // (min, scale) per row
 };
 
-// One gather over a CSR: out[row_ids[i]] (+)= rs[i] * sum_e cs[col_e] * value(col_e).  value() is a
-// float32 row of x for col < n_inner and a dequantised halo message for col >= n_inner.
+// One gather over a CSR: out[row_ids[i]] (+)= sum_e w[e] * value(col_e).  value() is a float32
+// row of x for col < n_inner and a dequantised halo message for col >= n_inner.
 struct GatherArgs {
   int64_t n_rows;
   const int32_t* rowptr;
@@ -34,9 +46,7 @@ struct GatherArgs {
   int64_t n_split_rows;
   const int32_t* split_row;
   const int32_t* split_ptr;
-  // weights
-  const float* rs;
-  const float* cs;
+  const float* w;             // per-edge weights (nullptr: 1)
   // values
   const float* x;
   int64_t ldx;
@@ -44,6 +54,7 @@ struct GatherArgs {
   const uint32_t* codes;
   const uint32_t* word_offset;
   const uint8_t* bits;
+  Classes cls;
   const float* meta;
   int64_t n_halo;
   // output
@@ -76,6 +87,8 @@ struct GemmArgs {
 void gemm_split_rule(int64_t m, int64_t n, int64_t k, int32_t* splits, int64_t* k_per_split);
 
 hipError_t launch_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, hipStream_t s);
+hipError_t launch_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r,
+                               const float* c, float* w, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs& a, int32_t d, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
 
   float v[8];
   uint32_t b = 0;
+  uint32_t row_off = 0;
   if (valid) {
     const int64_t src = a.row_index ? static_cast<int64_t>(a.row_index[r]) : r;
     const float4* p = reinterpret_cast<const float4*>(a.x + src * a.ldx + gl * 8);
@@ -58,7 +59,25 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
     const float4 hi = p[1];
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    b = a.bits[r];
+    if (a.cls.n > 0) {
+      // width-grouped buffer: the row's class, width and first word by arithmetic
+      int32_t st = a.cls.start[0];
+      uint32_t base = a.cls.base[0];
+      b = static_cast<uint32_t>(a.cls.bits[0]);
+#pragma unroll
+      for (int c = 1; c < kMaxClasses; ++c) {
+        if (c < a.cls.n && r >= a.cls.start[c]) {
+          st = a.cls.start[c];
+          base = a.cls.base[c];
+          b = static_cast<uint32_t>(a.cls.bits[c]);
+        }
+      }
+      const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (b * static_cast<uint32_t>(D) + 31u) >> 5;
+      row_off = base + static_cast<uint32_t>(r - st) * words;
+    } else {
+      b = a.bits[r];
+      row_off = a.word_offset[r];
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
@@ -120,7 +139,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
   const uint32_t n3 = __shfl_down(lo_w, 3);
   if (!active) return;
 
-  uint32_t* row_codes = a.codes + a.word_offset[r];
+  uint32_t* row_codes = a.codes + row_off;
   if (raw) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) row_codes[gl * 8 + i] = __float_as_uint(v[i]);

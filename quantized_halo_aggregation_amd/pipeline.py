@@ -72,16 +72,21 @@ class GpuPartition:
 
         self.set_bits(part.bits if bits is None else bits)
 
+        # edge weights of the forward CSR and of its transpose (set-up kernels)
         self.deg = dev(part.deg)
         if self.model == "gcn":
             self.norm = torch.empty(self.n_cols, dtype=torch.float32, device=device)
             B.degree_norm(self.deg, B.NORM_GCN, self.norm)
-            self.r_fwd, self.c_fwd = self.norm[:n_in], self.norm
+            r_f, c_f, r_b, c_b = self.norm[:n_in], self.norm, self.norm, self.norm[:n_in]
         else:
             row_len = dev(np.diff(part.nbr_ptr).astype(np.int32))
             self.mean_r = torch.empty(n_in, dtype=torch.float32, device=device)
             B.degree_norm(row_len, B.NORM_MEAN, self.mean_r)
-            self.r_fwd, self.c_fwd = self.mean_r, None
+            r_f, c_f, r_b, c_b = self.mean_r, None, None, self.mean_r
+        self.w_fwd = torch.empty(max(idx.size, 1), dtype=torch.float32, device=device)
+        self.w_bwd = torch.empty(max(rowidx.size, 1), dtype=torch.float32, device=device)
+        B.edge_weights(self.rowptr, self.colidx, r_f, c_f, self.w_fwd)
+        B.edge_weights(self.colptr, self.rowidx, r_b, c_b, self.w_bwd)
 
         mk = lambda rp: B.AggPlan(rp, chunk, group_edges, device=device)
         self.plan_fwd = mk(ptr)
@@ -93,7 +98,10 @@ class GpuPartition:
         self.agg_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
         self.dense_ws = None
 
-    def set_bits(self, bits):
+    def set_bits(self, bits, grouped: bool = True):
+        """Per-halo widths.  If the halo rows are numbered so that equal widths are contiguous the
+        packed buffers use the width-class layout (offsets by arithmetic); otherwise, or with
+        grouped=False, the per-row offset table."""
         bits = np.ascontiguousarray(bits, dtype=np.uint8)
         self.h_bits = bits
         off, total = B.pack_layout(bits, self.d)
@@ -101,6 +109,7 @@ class GpuPartition:
         self.total_words = total
         self.bits = torch.from_numpy(bits).to(self.device)
         self.word_offset = torch.from_numpy(off.view(np.int32)).to(self.device)
+        self.classes = B.pack_classes(bits, self.d) if grouped else None
 
     def new_messages(self) -> Messages:
         return Messages(torch.empty(max(self.total_words, 1), dtype=torch.int32, device=self.device),
@@ -118,40 +127,30 @@ class GpuPartition:
 
     def quantize_send(self, x, row_index, msg: Messages, epoch, stream_id, seed=QUANT_SEED):
         """a1 / a7: quantise the n_h outgoing boundary rows (x[row_index] or x itself)."""
-        B.quantize_pack(x, row_index, self.n_h, self.bits, self.word_offset, seed, epoch, stream_id, self.n_in,
-                        msg.codes, msg.meta)
+        B.quantize_pack(x, row_index, self.n_h, self.bits, self.word_offset, self.classes, seed, epoch, stream_id,
+                        self.n_in, msg.codes, msg.meta)
 
     def aggregate_fwd(self, x_inner, msg: Messages, out):
         """a3: out = sum over N(v) and v of w_vu * x~_u, halo rows dequantised from msg."""
-        B.dequant_aggregate_fwd(self.rowptr, self.colidx, self.plan_fwd, self.r_fwd, self.c_fwd, x_inner, self.n_in,
-                                msg.codes, self.word_offset, self.bits, msg.meta, self.n_h, 0, out,
+        B.dequant_aggregate_fwd(self.rowptr, self.colidx, self.w_fwd, self.plan_fwd, x_inner, self.n_in, msg.codes,
+                                self.word_offset, self.bits, self.classes, msg.meta, self.n_h, 0, out,
                                 workspace=self.agg_ws)
 
     def aggregate_bwd_halo(self, grad_out, dx_halo):
         """a6 (halo range): gradients of the halo columns."""
-        n_in = self.n_in
-        if self.model == "gcn":
-            r, c = self.norm[n_in:], self.norm[:n_in]
-        else:
-            r, c = None, self.mean_r
-        B.aggregate_bwd(self.colptr[n_in:], self.rowidx, self.plan_bwd_halo, r, c, grad_out, n_in, 0, dx_halo,
-                        workspace=self.agg_ws)
+        B.aggregate_bwd(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out, self.n_in, 0,
+                        dx_halo, workspace=self.agg_ws)
 
     def aggregate_bwd_inner(self, grad_out, dx_inner, beta):
         """a6 (inner range): gradients of the inner columns (beta = 1 adds to dx_inner)."""
-        n_in = self.n_in
-        if self.model == "gcn":
-            r, c = self.norm[:n_in], self.norm[:n_in]
-        else:
-            r, c = None, self.mean_r
-        B.aggregate_bwd(self.colptr[:n_in + 1], self.rowidx, self.plan_bwd_inner, r, c, grad_out, n_in, beta,
-                        dx_inner, workspace=self.agg_ws)
+        B.aggregate_bwd(self.colptr[:self.n_in + 1], self.rowidx, self.w_bwd, self.plan_bwd_inner, grad_out,
+                        self.n_in, beta, dx_inner, workspace=self.agg_ws)
 
     def add_received(self, msg: Messages, dx_inner):
         """a8: dx_inner[mirror[k]] += dequantised gradient message k."""
-        B.dequant_aggregate_fwd(self.m_ptr, self.m_idx, self.plan_mirror, None, None, None, 0, msg.codes,
-                                self.word_offset, self.bits, msg.meta, self.n_h, 1, dx_inner,
-                                workspace=self.agg_ws, row_ids=self.m_rows)
+        B.dequant_aggregate_fwd(self.m_ptr, self.m_idx, None, self.plan_mirror, None, 0, msg.codes, self.word_offset,
+                                self.bits, self.classes, msg.meta, self.n_h, 1, dx_inner, workspace=self.agg_ws,
+                                row_ids=self.m_rows)
 
 
 class LayerStack:

@@ -12,8 +12,9 @@ What one partition holds (SYLVIE guide, sections 3 and 7: a GPU owns its inner n
   halo node k, so every row lists its inner neighbours first.
 * ``deg`` -- int32 global in-degree of every column node (inner and halo).
 * ``mirror`` -- int32, halo k is the remote copy of inner node ``mirror[k]`` (the one-GPU stand-in
-  for the partition that owns it; see ``MirrorModel`` below).
-* ``bits`` -- uint8 per-halo bit width.
+  for the partition that owns it).
+* ``bits`` -- uint8 per-halo bit width.  Halo nodes are numbered by width, widest first, so equal
+  widths are contiguous (``number_halos_by_width``).
 * ``x`` -- float32 [n_in, d] layer-1 embeddings ~ N(0, 1); ``weights`` -- per-layer W ~ N(0, 1/fan_in);
   ``grad_top`` -- float32 upstream gradient ~ N(0, 1).
 
@@ -238,6 +239,28 @@ def draw_bits(rng: np.random.Generator, recipe: tuple, halo_deg: np.ndarray) -> 
     raise ValueError(f"unknown bits recipe {recipe!r}")
 
 
+def number_halos_by_width(n_in, ptr, idx, deg, mirror, bits):
+    """Renumbers the halo nodes so that equal widths are contiguous, widest first (a stable order
+    otherwise).  This is a relabelling only: the receiver is free to number its halo nodes, and
+    doing it by width lets a width-grouped packed buffer be addressed by arithmetic."""
+    n_h = bits.size
+    perm = np.argsort(-bits.astype(np.int64), kind="stable")          # new halo id -> old halo id
+    if np.array_equal(perm, np.arange(n_h)):
+        return ptr, idx, deg, mirror, bits
+    inv = np.empty(n_h, dtype=np.int64)
+    inv[perm] = np.arange(n_h)
+    n_rows = ptr.size - 1
+    n_cols = n_in + n_h
+    cols = idx.astype(np.int64)
+    halo = cols >= n_in
+    cols[halo] = n_in + inv[cols[halo] - n_in]
+    rows = np.repeat(np.arange(n_rows, dtype=np.int64), np.diff(ptr))
+    keys = np.sort(rows * n_cols + cols)
+    new_idx = (keys - (keys // n_cols) * n_cols).astype(np.int32)
+    new_deg = np.concatenate([deg[:n_in], deg[n_in:][perm]]).astype(np.int32)
+    return ptr, new_idx, new_deg, mirror[perm], bits[perm]
+
+
 def make_partition(wl: Workload, bits_override=None, with_features: bool = True) -> Partition:
     g = np.random.default_rng(1000 + wl.index)
     k_max = wl.k_max
@@ -256,6 +279,7 @@ def make_partition(wl: Workload, bits_override=None, with_features: bool = True)
 
     recipe = bits_override if bits_override is not None else wl.bits
     bits = draw_bits(np.random.default_rng(4000 + wl.index), recipe, deg[wl.n_in:])
+    ptr, idx, deg, mirror, bits = number_halos_by_width(wl.n_in, ptr, idx, deg, mirror, bits)
 
     x = np.zeros((0, wl.d), np.float32)
     weights = []

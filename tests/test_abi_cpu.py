@@ -41,6 +41,22 @@ def test_pack_layout(d):
     assert total == sum(sizes)
 
 
+def test_pack_classes_describe_the_same_layout():
+    d = 128
+    bits = np.array([8] * 5 + [4] * 7 + [32] * 2 + [1] * 3, np.uint8)
+    off, total = B.pack_layout(bits, d)
+    cl = B.pack_classes(bits, d)
+    assert cl.n == 4
+    assert list(cl.bits[:4]) == [8, 4, 32, 1] and list(cl.start[:5]) == [0, 5, 12, 14, 17]
+    for r in range(bits.size):
+        c = max(i for i in range(cl.n) if cl.start[i] <= r)
+        w = d if cl.bits[c] == 32 else d * cl.bits[c] // 32
+        assert cl.base[c] + (r - cl.start[c]) * w == off[r]
+    # too many runs: the per-row table is needed
+    assert B.pack_classes(np.array([1, 2] * 5, np.uint8), d) is None
+    assert B.pack_classes(np.zeros(0, np.uint8), d).n == 1
+
+
 def test_pack_layout_rejects_bad_width_and_d():
     with pytest.raises(ValueError, match="not in"):
         B.pack_layout(np.array([4, 3], np.uint8), 128)
@@ -115,23 +131,30 @@ def test_agg_plan_covers_every_edge_and_row_once(skip_empty, group_edges):
 def test_device_calls_reject_bad_arguments_before_any_hip_call():
     q = B._quantize_pack
     # unsupported width
-    assert q(FAKE, 24, None, 10, 24, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_UNSUPPORTED
+    assert q(FAKE, 24, None, 10, 24, FAKE, FAKE, None, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_UNSUPPORTED
     # leading dimension below d
-    assert q(FAKE, 64, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 64, None, 10, 128, FAKE, FAKE, None, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
     # misaligned rows
-    assert q(FAKE + 4, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
-    # null outputs, misaligned metadata pairs
-    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, None, FAKE, None) == B.QHA_ERR_INVALID_ARG
-    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE + 4, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE + 4, 128, None, 10, 128, FAKE, FAKE, None, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # null outputs, misaligned metadata pairs, neither classes nor a per-row table
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, None, 1, 0, 0, 0, None, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, None, 1, 0, 0, 0, FAKE, FAKE + 4, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 128, None, 10, 128, None, None, None, 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    # classes that do not cover the rows, or do not follow each other
+    cl = B.pack_classes(np.array([4] * 9, np.uint8), 128)
+    assert q(FAKE, 128, None, 10, 128, None, None, C.byref(cl), 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    cl = B.pack_classes(np.array([4] * 5 + [8] * 5, np.uint8), 128)
+    cl.base[1] += 1
+    assert q(FAKE, 128, None, 10, 128, None, None, C.byref(cl), 1, 0, 0, 0, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
     # node ids overflow 32 bits
-    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, 1, 0, 0, 0xFFFFFFFF, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
+    assert q(FAKE, 128, None, 10, 128, FAKE, FAKE, None, 1, 0, 0, 0xFFFFFFFF, FAKE, FAKE, None) == B.QHA_ERR_INVALID_ARG
     # nothing to do is OK without touching the device
-    assert q(None, 0, None, 0, 128, None, None, 1, 0, 0, 0, None, None, None) == B.QHA_OK
+    assert q(None, 0, None, 0, 128, None, None, None, 1, 0, 0, 0, None, None, None) == B.QHA_OK
 
     f = B._dequant_aggregate_fwd
-    args = dict(n_rows=10, rowptr=FAKE, colidx=FAKE, row_ids=None, plan=None, r=None, c=None, x=FAKE, ldx=128,
-                n_inner=5, codes=FAKE, wo=FAKE, bits=FAKE, meta=FAKE, n_halo=5, d=128, beta=0, out=FAKE, ldo=128,
-                ws=None, wsb=0, s=None)
+    args = dict(n_rows=10, rowptr=FAKE, colidx=FAKE, w=None, row_ids=None, plan=None, x=FAKE, ldx=128,
+                n_inner=5, codes=FAKE, wo=FAKE, bits=FAKE, classes=None, meta=FAKE, n_halo=5, d=128, beta=0, out=FAKE,
+                ldo=128, ws=None, wsb=0, s=None)
 
     def call(**kw):
         a = dict(args, **kw)
@@ -157,8 +180,9 @@ def test_device_calls_reject_bad_arguments_before_any_hip_call():
     assert call(n_rows=4, plan=C.byref(st2)) == B.QHA_ERR_INVALID_ARG
 
     g = B._aggregate_bwd
-    assert g(10, FAKE, FAKE, None, None, None, FAKE, 128, 10, 128, 3, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
-    assert g(10, FAKE, FAKE, None, None, None, FAKE, 96, 10, 128, 0, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
+    assert g(10, FAKE, FAKE, None, None, FAKE, 128, 10, 128, 3, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
+    assert g(10, FAKE, FAKE, None, None, FAKE, 96, 10, 128, 0, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
+    assert B._edge_weights(10, None, FAKE, None, None, FAKE, None) == B.QHA_ERR_INVALID_ARG
 
     p = B._dense_project
     # contiguous extent of A not a multiple of 4

@@ -39,10 +39,12 @@ def _setup(case):
 
 
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
-def test_forward_aggregation(case):
+@pytest.mark.parametrize("grouped", [True, False], ids=["width-classes", "offset-table"])
+def test_forward_aggregation(case, grouped):
     H.require_gpu()
     import torch
     part, gp = _setup(case)
+    gp.set_bits(part.bits, grouped=grouped)
     n_in, d = part.n_in, part.d
     msg = H.oracle_messages(part.x[part.mirror], part.bits, SEED, 0, 0, n_in)
     x_cols = np.concatenate([part.x, msg["received"]])
@@ -116,7 +118,8 @@ def test_deterministic_repeats():
 
 
 def test_plain_rows_and_degenerate_inputs():
-    """No plan (one wavefront per row), rows without edges, all-halo rows, empty calls, b = 32 halos."""
+    """No plan (one item per row), rows without edges, unsorted widths, empty calls, b = 32 halos,
+    explicit edge weights."""
     H.require_gpu()
     import torch
     from quantized_halo_aggregation_amd import binding as B
@@ -134,29 +137,33 @@ def test_plain_rows_and_degenerate_inputs():
     off, _ = B.pack_layout(bits, d)
     r = rng.random(25).astype(np.float32)
     c = rng.random(n_inner + n_halo).astype(np.float32)
-    x_cols = np.concatenate([x, msg["received"]]).astype(np.float64)
     rows = np.repeat(np.arange(25), lens)
+    w_ref = (r[rows] * c[idx]).astype(np.float32)            # float32 product, as documented
+    H.note("edge weights")
+    w = torch.empty(idx.size, dtype=torch.float32, device="cuda")
+    B.edge_weights(H.dev(ptr), H.dev(idx), H.dev(r), H.dev(c), w)
+    H.assert_bits_equal(H.host(w), w_ref, "edge weights")
+    x_cols = np.concatenate([x, msg["received"]]).astype(np.float64)
     ref = np.zeros((25, d))
-    np.add.at(ref, rows, (r[rows].astype(np.float64) * c[idx])[:, None] * x_cols[idx])
+    np.add.at(ref, rows, w_ref.astype(np.float64)[:, None] * x_cols[idx])
     H.note("aggregate plain rows")
     out = torch.full((25, d), np.nan, dtype=torch.float32, device="cuda")
-    B.dequant_aggregate_fwd(H.dev(ptr), H.dev(idx), None, H.dev(r), H.dev(c), H.dev(x), n_inner,
-                            H.dev(msg["words"].view(np.int32)), H.dev(off.view(np.int32)), H.dev(bits),
+    B.dequant_aggregate_fwd(H.dev(ptr), H.dev(idx), w, None, H.dev(x), n_inner,
+                            H.dev(msg["words"].view(np.int32)), H.dev(off.view(np.int32)), H.dev(bits), None,
                             H.dev(np.stack([msg["zero_point"], msg["scale"]], 1)), n_halo, 0, out)
     got = H.host(out)
     H.assert_close(got, ref, what="plain rows")
     assert not got[[0, 7, 24]].any()
     # zero rows: nothing happens
-    B.dequant_aggregate_fwd(H.dev(ptr[:1]), H.dev(idx), None, None, None, H.dev(x), n_inner, None, None, None, None,
+    B.dequant_aggregate_fwd(H.dev(ptr[:1]), H.dev(idx), None, None, H.dev(x), n_inner, None, None, None, None, None,
                             0, 0, out, n_rows=0)
-    # no halo at all: only inner columns may appear
-    inner_only = ptr.copy()
+    # no halo at all: only inner columns, unit weights
     keep = idx < n_inner
     cnt = np.bincount(rows[keep], minlength=25)
     inner_only = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
     out2 = torch.full((25, d), np.nan, dtype=torch.float32, device="cuda")
-    B.dequant_aggregate_fwd(H.dev(inner_only), H.dev(idx[keep]), None, None, None, H.dev(x), n_inner, None, None,
-                            None, None, 0, 0, out2)
+    B.dequant_aggregate_fwd(H.dev(inner_only), H.dev(idx[keep]), None, None, H.dev(x), n_inner, None, None, None, None,
+                            None, 0, 0, out2)
     ref2 = np.zeros((25, d))
     np.add.at(ref2, rows[keep], x[idx[keep]].astype(np.float64))
     H.assert_close(H.host(out2), ref2, what="inner-only rows, unit weights")
