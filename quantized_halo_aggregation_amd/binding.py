@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqha.so")
+# QHA_LIB may name another build of the library (same ABI), e.g. one installed elsewhere
+LIB_PATH = os.environ.get("QHA_LIB") or os.path.join(_HERE, "libqha.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_halo_aggregation_amd.build` "

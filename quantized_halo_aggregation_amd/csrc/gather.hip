@@ -28,6 +28,9 @@
 #include "../../include/qha.h"
 #include "qha_internal.hpp"
 
+// the dequantisation scale * q + min is two roundings, as the message format defines it
+#pragma clang fp contract(off)
+
 namespace qha {
 namespace {
 
@@ -40,7 +43,13 @@ __device__ __forceinline__ cptr<T> cst(const T* p) {
 }
 
 constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
-constexpr int batch_of(int D, bool halo) { return D >= 512 ? 8 : 16; }
+#ifndef QHA_BATCH
+#define QHA_BATCH 16        // edges per batch of the inner-row gather
+#endif
+#ifndef QHA_HALO_BATCH
+#define QHA_HALO_BATCH 8    // edges per batch when halo rows are dequantised too
+#endif
+constexpr int batch_of(int D, bool halo) { return D >= 512 ? 8 : (halo ? QHA_HALO_BATCH : QHA_BATCH); }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 
 __device__ __forceinline__ int rdlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -66,6 +75,26 @@ __device__ __forceinline__ void store_row(float* p, const float (&v)[VEC]) {
 #pragma unroll
     for (int q = 0; q < VEC / 4; ++q)
       reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+}
+
+// VEC floats from an address that is only 4-byte aligned (a raw halo row inside a packed buffer);
+// global memory on gfx950 serves unaligned multi-dword loads.
+template <int VEC>
+__device__ __forceinline__ void load_row_unaligned(const float* p, float (&xv)[VEC]) {
+  typedef float f2u __attribute__((ext_vector_type(2), aligned(4)));
+  typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+  if constexpr (VEC == 1) {
+    xv[0] = p[0];
+  } else if constexpr (VEC == 2) {
+    const f2u t = *reinterpret_cast<const f2u*>(p);
+    xv[0] = t.x; xv[1] = t.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const f4u t = reinterpret_cast<const f4u*>(p)[q];
+      xv[4 * q + 0] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+    }
   }
 }
 
@@ -194,21 +223,103 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       ww[i] = rdlanef(v_w, i);
     }
 
-    // phase 1: inner rows, halo metadata and (grouped layout) halo code words.  A halo row's
-    // (min, scale) pair shares the registers of its value until it is dequantised.
-    constexpr bool PAIR_IN_XV = VEC >= 2;
-    float xv[B][VEC];
-    uint32_t cwd[B][CW];
-    uint32_t woff[B], bw[B];
-    float mn1[B], sc1[B];                      // (min, scale) when VEC == 1
+    if constexpr (HALO && GROUPED) {
+      // batch set-up, vectorised over the batch's edges (edge i in lane i): each edge's class,
+      // width and code offset, and the two addresses its loads will use -- the value (an inner
+      // row, the raw floats of a 32-bit halo row, or for a quantised halo row its (min, scale) pair
+      // when each lane holds two features) and the code word row (the first word of the buffer for
+      // edges without codes).
+      constexpr bool META_IN_XV = VEC == 2;
+      const int32_t vk = v_u - static_cast<int32_t>(a.n_inner);
+      const bool vh = vk >= 0;
+      uint32_t vb = 0, vst = 0, vcb = 0;
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      if (HALO && u[i] >= a.n_inner) {
-        const int32_t k = u[i] - static_cast<int32_t>(a.n_inner);
-        uint32_t b = 0, off = 0;
-        if constexpr (GROUPED) {
-          class_of<D>(v_cstart, v_cbits, v_cbase, k, b, off);
-        } else {
+      for (int c = 0; c < kMaxClasses; ++c) {
+        if (c < a.cls.n && vk >= a.cls.start[c]) {
+          vb = static_cast<uint32_t>(a.cls.bits[c]);
+          vst = static_cast<uint32_t>(a.cls.start[c]);
+          vcb = a.cls.base[c];
+        }
+      }
+      const bool vq = vh && vb != 32u;                           // a quantised halo row
+      const uint32_t vlgb = vq ? static_cast<uint32_t>(__builtin_ctz(vb)) : 0u;
+      // words per row, a power of two: ceil(d*b/32) for codes (d = 16 with 1-bit codes fills half a
+      // word), d for raw rows
+      const uint32_t vlgdb = static_cast<uint32_t>(log2i(D)) + vlgb;
+      const uint32_t vlgw = (vb == 32u) ? static_cast<uint32_t>(log2i(D)) : (vlgdb > 5u ? vlgdb - 5u : 0u);
+      const uint32_t voff = vh ? vcb + ((static_cast<uint32_t>(vk) - vst) << vlgw) : 0u;
+      const uint64_t vval = !vh ? reinterpret_cast<uint64_t>(a.x + static_cast<int64_t>(v_u) * a.ldx)
+                          : (vq && META_IN_XV) ? reinterpret_cast<uint64_t>(a.meta + 2 * static_cast<int64_t>(vk))
+                                               : reinterpret_cast<uint64_t>(a.codes + voff);
+      const uint64_t vcode = reinterpret_cast<uint64_t>(a.codes + (vq ? voff : 0u));
+      const uint64_t vmeta = reinterpret_cast<uint64_t>(a.meta + 2 * static_cast<int64_t>(vq ? vk : 0));
+      const uint32_t vkind = vq ? vb : (vh ? 32u : 0u);          // 0: inner, 32: raw halo, else width
+
+      // phase 1: per edge, two (three when d >= 256) loads from the prepared addresses
+      float xv[B][VEC];
+      float2 mp[B];
+      uint32_t cwd[B][CW];
+      uint32_t kind[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        kind[i] = static_cast<uint32_t>(rdlane(static_cast<int>(vkind), i));
+        const bool q = kind[i] != 0u && kind[i] != 32u;
+        const uint64_t va = (static_cast<uint64_t>(static_cast<uint32_t>(rdlane(static_cast<int>(vval >> 32), i))) << 32) |
+                            static_cast<uint32_t>(rdlane(static_cast<int>(vval), i));
+        load_row_unaligned<VEC>(reinterpret_cast<const float*>(va) + (q ? 0 : j0), xv[i]);
+        if constexpr (!META_IN_XV) {
+          const uint64_t ma = (static_cast<uint64_t>(static_cast<uint32_t>(rdlane(static_cast<int>(vmeta >> 32), i))) << 32) |
+                              static_cast<uint32_t>(rdlane(static_cast<int>(vmeta), i));
+          mp[i] = *reinterpret_cast<const float2*>(ma);
+        }
+        const uint64_t ca = (static_cast<uint64_t>(static_cast<uint32_t>(rdlane(static_cast<int>(vcode >> 32), i))) << 32) |
+                            static_cast<uint32_t>(rdlane(static_cast<int>(vcode), i));
+        const uint32_t lgb = static_cast<uint32_t>(rdlane(static_cast<int>(vlgb), i));
+        const uint32_t* crow = reinterpret_cast<const uint32_t*>(ca);
+        const uint32_t cw0 = q ? ((static_cast<uint32_t>(j0) << lgb) >> 5) : 0u;
+        cwd[i][0] = crow[cw0];
+        if (CW == 2) cwd[i][CW - 1] = crow[cw0 + ((q && kind[i] * VEC > 32u) ? 1u : 0u)];
+      }
+      if (e + B < e1) fetch(e + B);
+      // phase 2: dequantise and sum, closing the row whose last edge this is
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int32_t p = e + i;
+        if (p < e1) {
+          const double wt = static_cast<double>(ww[i]);
+          const uint32_t b = kind[i];
+          float val[VEC];
+          if (b != 0u && b != 32u) {
+            const float mn = META_IN_XV ? xv[i][0] : mp[i].x;
+            const float sc = META_IN_XV ? xv[i][1 % VEC] : mp[i].y;
+            const uint32_t mask = (1u << b) - 1u;
+            const uint32_t sh = (static_cast<uint32_t>(j0) << __builtin_ctz(b)) & 31u;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const uint32_t bitpos = sh + static_cast<uint32_t>(v) * b;
+              const uint32_t wd = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
+              val[v] = dequant(sc, wd & mask, mn);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) val[v] = xv[i][v];
+          }
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(val[v]), acc[v]);
+          if (p + 1 == cur_end) flush();
+        }
+      }
+    } else {
+      // phase 1: inner rows (and with a per-row offset table: the halo rows' widths, offsets and
+      // (min, scale) pairs)
+      float xv[B][VEC];
+      float2 ms[B];
+      uint32_t cwd[B][CW];
+      uint32_t woff[B], bw[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        if (HALO && u[i] >= a.n_inner) {
+          const int32_t k = u[i] - static_cast<int32_t>(a.n_inner);
           woff[i] = cst(a.word_offset)[k];
           if constexpr (D >= 32) {
             // the width follows from the row's word count (unique for d >= 32)
@@ -216,86 +327,60 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
           } else {
             bw[i] = cst(a.bits)[k];
           }
+          ms[i] = *reinterpret_cast<const float2*>(a.meta + 2 * static_cast<int64_t>(k));
+        } else {
+          load_row<VEC>(a.x + static_cast<int64_t>(u[i]) * a.ldx + j0, xv[i]);
         }
-        if (!GROUPED || b != 32u) {
-          const float2 ms = *reinterpret_cast<const float2*>(a.meta + 2 * static_cast<int64_t>(k));
-          if constexpr (PAIR_IN_XV) {
-            xv[i][0] = ms.x;
-            xv[i][1] = ms.y;
-          } else {
-            mn1[i] = ms.x;
-            sc1[i] = ms.y;
-          }
-        }
-        if constexpr (GROUPED) {
-          const uint32_t* row = a.codes + off;
-          if (b == 32u) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
-          } else {
-            const uint32_t pos = static_cast<uint32_t>(j0) * b;
-            cwd[i][0] = row[pos >> 5];
-            if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
-          }
-        }
-      } else {
-        load_row<VEC>(a.x + static_cast<int64_t>(u[i]) * a.ldx + j0, xv[i]);
       }
-    }
-    if (e + B < e1) fetch(e + B);
-    // phase 2 (per-row offset table): the code words of the halo rows, once their offsets are in
-    if constexpr (HALO && !GROUPED) {
+      if (e + B < e1) fetch(e + B);
+      // phase 2: the code words of the halo rows, once their offsets are in
+      if constexpr (HALO) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          if (u[i] >= a.n_inner) {
+            const uint32_t b = bw[i];
+            const uint32_t* row = a.codes + woff[i];
+            if (b == 32u) {
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
+            } else if (width_ok(b)) {
+              const uint32_t pos = static_cast<uint32_t>(j0) * b;
+              cwd[i][0] = row[pos >> 5];
+              if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
+            }
+          }
+        }
+      }
+      // phase 3: dequantise and sum, closing the row whose last edge this is
 #pragma unroll
       for (int i = 0; i < B; ++i) {
-        if (u[i] >= a.n_inner) {
-          const uint32_t b = bw[i];
-          const uint32_t* row = a.codes + woff[i];
-          if (b == 32u) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
-          } else if (width_ok(b)) {
-            const uint32_t pos = static_cast<uint32_t>(j0) * b;
-            cwd[i][0] = row[pos >> 5];
-            if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
-          }
-        }
-      }
-    }
-    // phase 3: dequantise and sum, closing the row whose last edge this is
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const int32_t p = e + i;
-      if (p < e1) {
-        if (HALO && u[i] >= a.n_inner) {
-          uint32_t b;
-          if constexpr (GROUPED) {
-            uint32_t off_unused;
-            class_of<D>(v_cstart, v_cbits, v_cbase, u[i] - static_cast<int32_t>(a.n_inner), b, off_unused);
-          } else {
-            b = bw[i];
-          }
-          if (b != 32u) {
-            if (GROUPED || width_ok(b)) {
-              const float mn = PAIR_IN_XV ? xv[i][0] : mn1[i];
-              const float sc = PAIR_IN_XV ? xv[i][1 % VEC] : sc1[i];
+        const int32_t p = e + i;
+        if (p < e1) {
+          const double wt = static_cast<double>(ww[i]);
+          if (HALO && u[i] >= a.n_inner && bw[i] != 32u) {
+            const uint32_t b = bw[i];
+            float q[VEC];
+            if (width_ok(b)) {
               const uint32_t mask = (1u << b) - 1u;
               const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
 #pragma unroll
               for (int v = 0; v < VEC; ++v) {
                 const uint32_t bitpos = sh + static_cast<uint32_t>(v) * b;
                 const uint32_t wd = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
-                xv[i][v] = dequant(sc, wd & mask, mn);
+                q[v] = dequant(ms[i].y, wd & mask, ms[i].x);
               }
             } else {
 #pragma unroll
-              for (int v = 0; v < VEC; ++v) xv[i][v] = 0.0f;
+              for (int v = 0; v < VEC; ++v) q[v] = 0.0f;
             }
-          }
-        }
-        const double wt = static_cast<double>(ww[i]);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
-        if (p + 1 == cur_end) flush();
+            for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(q[v]), acc[v]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
+          }
+          if (p + 1 == cur_end) flush();
+        }
       }
     }
   }
