@@ -70,11 +70,17 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="synthetic partition index (2 = 300k-node d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU runs are not part of "
-              "this build", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the multi-GPU exchange is not "
+              "implemented here", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     from quantized_halo_aggregation_amd import binding as B
@@ -172,7 +178,8 @@ def main():
     if dom in bytes_by_stage:
         ach = bytes_by_stage[dom] / (avg_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, dom),
+                "avg_us": round(avg_ms[dom] * 1e3, 1)}
     else:
         fl = flops_by_stage[dom] / (2 if dom == "dense_bwd" else 1)
         ach = fl / (single[dom] * 1e-3) / 1e12
@@ -202,6 +209,62 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+# ------------------------------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a plain copy)
+# ------------------------------------------------------------------------------------------------
+
+KERNEL_SOURCES = {
+    # the kernel source whose change invalidates a stage's counter reading
+    "aggregate_fwd": ["csrc/gather.hip"],
+    "aggregate_bwd_inner": ["csrc/gather.hip"],
+    "dense_fwd": ["csrc/gemm.hip"],
+    "dense_bwd": ["csrc/gemm.hip"],
+}
+
+
+def source_hash(stage):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(stage, []):
+        with open(os.path.join(ROOT, "quantized_halo_aggregation_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per call of `stage`, from a `traffic` line in profiles/*.txt taken on the current
+    kernel sources (None when there is none, or the sources have changed since)."""
+    pdir = os.path.join(ROOT, "profiles")
+    if stage not in KERNEL_SOURCES or not os.path.isdir(pdir):
+        return None
+    want = source_hash(stage)
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(".txt"):
+            continue
+        with open(os.path.join(pdir, name)) as fh:
+            for line in fh:
+                f = line.split()
+                if len(f) < 4 or f[0] != "traffic" or f[1] != workload or f[2] != stage:
+                    continue
+                kv = dict(x.split("=", 1) for x in f[3:] if "=" in x)
+                if kv.get("src") == want and "bytes_per_call" in kv:
+                    return int(kv["bytes_per_call"])
+    return None
+
+
+def calibrate_copy(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch, five launches."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 5}))
 
 
 def cpu_baseline(part, bytes_by_stage):
