@@ -219,8 +219,8 @@ KERNEL_SOURCES = {
     # the kernel source whose change invalidates a stage's counter reading
     "aggregate_fwd": ["csrc/gather.hip"],
     "aggregate_bwd_inner": ["csrc/gather.hip"],
-    "dense_fwd": ["csrc/gemm.hip"],
-    "dense_bwd": ["csrc/gemm.hip"],
+    "dense_fwd": ["csrc/gemm.hip", "csrc/panel.hip"],
+    "dense_bwd": ["csrc/gemm.hip", "csrc/panel.hip"],
 }
 
 

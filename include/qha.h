@@ -240,7 +240,8 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
  * that dZ = dH * [H > 0] is formed while A is loaded (aux has op(A)'s storage layout).
  * Products are accumulated by the fp32 matrix cores over 32 values of k at a time and those
  * partial sums are added in float64; the result is rounded to float32 once (after adding C when
- * beta = 1, before the epilogue).  When m*n is small and k large the reduction is split over k
+ * beta = 1, before the epilogue).  The forward shape n = k = 128 (trans_b = 1, no prologue,
+ * beta = 0) runs as a row-panel kernel that keeps B in on-chip memory.  When m*n is small and k large the reduction is split over k
  * into float64 partials in the workspace (device, 16-byte aligned, qha_dense_project_workspace
  * bytes) and summed in a fixed order; results are deterministic.  beta is 0 or 1.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */
@@ -250,6 +251,25 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
                       int32_t prologue, const float* aux, int64_t ld_aux, int32_t epilogue,
                       void* workspace, size_t workspace_bytes, void* stream);
 size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k);
+
+/* 5. dense_backward -- the backward of one dense layer H = ReLU(A W^T) over m rows, in one call
+ * (guide section 7: the weight gradient sums (dL/dh_v * sigma'(z_v)) a_v^T over the rows, and
+ * section 3: the embedding gradient dA flows back to the aggregation):
+ *   dZ = dH * [H > 0],   dA = dZ W   [m x k],   dW = dZ^T A   [n x k]
+ * dH, H: device [m x n] (leading dimensions ldg, ldh); A: device [m x k] (lda); W: device [n x k]
+ * (ldw); dA: device [m x k] (ldda), overwritten; dW: device [n x k] (lddw), overwritten (zeros
+ * when m = 0).  Leading dimensions are multiples of 4 and at least the row width; dH, H, A and W
+ * are 16-byte aligned.  dA must not overlap dH, H, A or W.  For n = k = 128 the operands are read
+ * once: W stays in on-chip memory while 64-row panels stream through, dZ is formed once and used
+ * for both products, and per-block dW partials (workspace) are added in a fixed order.  Other
+ * widths run as the two qha_dense_project products.  dA sums are fp32 matrix-core chains of 32
+ * products added in float64; dW adds fp32 chains over each block's rows in float64.  workspace:
+ * device, 16-byte aligned, qha_dense_backward_workspace bytes.  Results are deterministic.
+ * Errors: INVALID_ARG, WORKSPACE, HIP. */
+int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t ldg, const float* h, int64_t ldh,
+                       const float* a, int64_t lda, const float* w, int64_t ldw, float* da, int64_t ldda,
+                       float* dw, int64_t lddw, void* workspace, size_t workspace_bytes, void* stream);
+size_t qha_dense_backward_workspace(int64_t m, int64_t n, int64_t k);
 
 #ifdef __cplusplus
 }

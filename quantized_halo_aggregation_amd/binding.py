@@ -94,12 +94,16 @@ _aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlan
 _dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
                       _i64, _i32, _vp, _i64, _i32, _vp, _sz, _vp)
 _dense_ws = _sig("qha_dense_project_workspace", _sz, _i32, _i32, _i64, _i64, _i64)
+_dense_bwd = _sig("qha_dense_backward", _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                  _vp, _i64, _vp, _sz, _vp)
+_dense_bwd_ws = _sig("qha_dense_backward_workspace", _sz, _i64, _i64, _i64)
 
 EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_layout", "qha_pack_classes",
             "qha_edge_weights", "qha_validate_csr",
             "qha_csr_transpose", "qha_agg_plan_size", "qha_agg_plan_fill", "qha_agg_workspace_bytes",
             "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_aggregate_bwd",
-            "qha_dense_project", "qha_dense_project_workspace"]
+            "qha_dense_project", "qha_dense_project_workspace", "qha_dense_backward",
+            "qha_dense_backward_workspace"]
 
 
 class QhaError(RuntimeError):
@@ -259,6 +263,10 @@ def dense_project_workspace(trans_a: int, trans_b: int, m: int, n: int, k: int) 
     return int(_dense_ws(int(trans_a), int(trans_b), int(m), int(n), int(k)))
 
 
+def dense_backward_workspace(m: int, n: int, k: int) -> int:
+    return int(_dense_bwd_ws(int(m), int(n), int(k)))
+
+
 # ------------------------------------------------------------------------------------------------
 # device entry points
 # ------------------------------------------------------------------------------------------------
@@ -348,3 +356,24 @@ def dense_project(trans_a: int, trans_b: int, a, b, beta: int, c, prologue: int 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_dense_project(int(trans_a), int(trans_b), m, n, k, pa, lda, pb, ldb, int(beta), pc, ldc, int(prologue),
                           paux, ldaux, int(epilogue), ws_ptr, ws_bytes, _stream(stream)), "qha_dense_project")
+
+
+def dense_backward(dh, h, a, w, da, dw, workspace=None, stream=None):
+    """dZ = dH * [H > 0]; dA = dZ W (into da), dW = dZ^T A (into dw); shapes are read from the tensors:
+    dh, h [m x n], a [m x k], w [n x k], da [m x k], dw [n x k]."""
+    m, n = dh.shape
+    k = a.shape[1]
+    if tuple(h.shape) != (m, n) or tuple(a.shape) != (m, k) or tuple(w.shape) != (n, k) \
+            or tuple(da.shape) != (m, k) or tuple(dw.shape) != (n, k):
+        raise ValueError(f"shape mismatch: dh {tuple(dh.shape)}, h {tuple(h.shape)}, a {tuple(a.shape)}, "
+                         f"w {tuple(w.shape)}, da {tuple(da.shape)}, dw {tuple(dw.shape)}")
+    pg, ldg = _rows(dh, "dh")
+    ph, ldh = _rows(h, "h")
+    pa, lda = _rows(a, "a")
+    pw, ldw = _rows(w, "w")
+    pda, ldda = _rows(da, "da")
+    pdw, lddw = _rows(dw, "dw")
+    ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_dense_bwd(int(m), int(n), int(k), pg, ldg, ph, ldh, pa, lda, pw, ldw, pda, ldda, pdw, lddw, ws_ptr,
+                      ws_bytes, _stream(stream)), "qha_dense_backward")

@@ -498,6 +498,19 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
   g.aux = aux;
   g.ld_aux = ld_aux;
   g.epi = epilogue;
+  if (!trans_a && trans_b && prologue == QHA_PRO_NONE && beta == 0 && m > 0 && qha::panel_fits(n, k)) {
+    qha::PanelArgs p;
+    std::memset(&p, 0, sizeof(p));
+    p.m = m;
+    p.a = a;
+    p.lda = lda;
+    p.w = b;
+    p.ldw = ldb;
+    p.out = c;
+    p.ldo = ldc;
+    p.relu = epilogue == QHA_EPI_RELU;
+    return hip_status(qha::launch_panel_fwd(p, static_cast<hipStream_t>(stream)), "dense_project");
+  }
   qha::gemm_split_rule(m, n, k, &g.splits, &g.k_per_split);
   g.ws = static_cast<double*>(workspace);
   if (g.splits > 1) {
@@ -506,6 +519,72 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
     if (!aligned16(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
   }
   return hip_status(qha::launch_gemm(g, static_cast<hipStream_t>(stream)), "dense_project");
+}
+
+size_t qha_dense_backward_workspace(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  if (qha::panel_fits(n, k)) return qha::panel_bwd_workspace(m);
+  // dA = dZ W needs none; dW = dZ^T A may split its m-long reduction
+  return qha_dense_project_workspace(1, 0, n, k, m);
+}
+
+int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t ldg, const float* h, int64_t ldh,
+                       const float* a, int64_t lda, const float* w, int64_t ldw, float* da, int64_t ldda,
+                       float* dw, int64_t lddw, void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || n < 0 || k < 0 || m > kMaxIndex || n > kMaxIndex || k > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if (n == 0 || k == 0) return ok();
+  if ((n & 3) || (k & 3)) return fail(QHA_ERR_INVALID_ARG, "n (%lld) and k (%lld) must be multiples of 4", (long long)n, (long long)k);
+  if (!w || ldw < k || (ldw & 3) || !aligned16(w)) return fail(QHA_ERR_INVALID_ARG, "W / ldw out of contract");
+  if (!dw || lddw < k || !aligned4(dw)) return fail(QHA_ERR_INVALID_ARG, "dW / lddw out of contract");
+  if (m > 0) {
+    if (!dh || ldg < n || (ldg & 3) || !aligned16(dh)) return fail(QHA_ERR_INVALID_ARG, "dH / ldg out of contract");
+    if (!h || ldh < n || (ldh & 3) || !aligned16(h)) return fail(QHA_ERR_INVALID_ARG, "H / ldh out of contract");
+    if (!a || lda < k || (lda & 3) || !aligned16(a)) return fail(QHA_ERR_INVALID_ARG, "A / lda out of contract");
+    if (!da || ldda < k || !aligned4(da)) return fail(QHA_ERR_INVALID_ARG, "dA / ldda out of contract");
+  }
+  const size_t need = qha_dense_backward_workspace(m, n, k);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+    if (!aligned16(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m > 0 && qha::panel_fits(n, k)) {
+    qha::PanelArgs p;
+    std::memset(&p, 0, sizeof(p));
+    p.m = m;
+    p.a = a;
+    p.lda = lda;
+    p.w = w;
+    p.ldw = ldw;
+    p.dh = dh;
+    p.lddh = ldg;
+    p.h = h;
+    p.ldh = ldh;
+    p.da = da;
+    p.ldda = ldda;
+    p.dw = dw;
+    p.lddw = lddw;
+    p.ws = static_cast<float*>(workspace);
+    return hip_status(qha::launch_panel_bwd(p, s), "dense_backward");
+  }
+  // general widths: dA = dZ W (masked A operand), then dW = dZ^T A
+  qha::GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  if (m > 0) {
+    g.ta = 0; g.tb = 0; g.m = m; g.n = k; g.k = n;
+    g.a = dh; g.lda = ldg; g.b = w; g.ldb = ldw; g.beta = 0; g.c = da; g.ldc = ldda;
+    g.pro = QHA_PRO_RELU_MASK; g.aux = h; g.ld_aux = ldh; g.epi = QHA_EPI_NONE;
+    qha::gemm_split_rule(g.m, g.n, g.k, &g.splits, &g.k_per_split);
+    if (g.splits > 1) return fail(QHA_ERR_INVALID_ARG, "unexpected split of dA");
+    const int st = hip_status(qha::launch_gemm(g, s), "dense_backward");
+    if (st) return st;
+  }
+  g.ta = 1; g.tb = 0; g.m = n; g.n = k; g.k = m;
+  g.a = dh; g.lda = m > 0 ? ldg : n; g.b = a; g.ldb = m > 0 ? lda : k; g.beta = 0; g.c = dw; g.ldc = lddw;
+  g.pro = m > 0 ? QHA_PRO_RELU_MASK : QHA_PRO_NONE; g.aux = h; g.ld_aux = m > 0 ? ldh : n; g.epi = QHA_EPI_NONE;
+  qha::gemm_split_rule(g.m, g.n, g.k, &g.splits, &g.k_per_split);
+  g.ws = static_cast<double*>(workspace);
+  return hip_status(qha::launch_gemm(g, s), "dense_backward");
 }
 
 }  // extern "C"

@@ -83,6 +83,32 @@ struct GemmArgs {
   int64_t k_per_split;
 };
 
+// Row-panel products of width-128 layers (W resident in LDS, 64-row panels streamed).
+constexpr int kPanelBlocks = 256;    // one block per compute unit of an MI355X
+struct PanelArgs {
+  int64_t m;
+  const float* a;      // [m x 128]: the forward input, or the backward's A (for dW)
+  int64_t lda;
+  const float* w;      // W [128 x 128]
+  int64_t ldw;
+  float* out;          // forward: H [m x 128]
+  int64_t ldo;
+  int32_t relu;
+  const float* dh;     // backward: dH [m x 128]
+  int64_t lddh;
+  const float* h;      // backward: the forward output H (ReLU mask) [m x 128]
+  int64_t ldh;
+  float* da;           // backward: dA [m x 128]
+  int64_t ldda;
+  float* dw;           // backward: dW [128 x 128]
+  int64_t lddw;
+  float* ws;           // backward: per-block dW partials [blocks][128][128]
+};
+bool panel_fits(int64_t n, int64_t k);
+size_t panel_bwd_workspace(int64_t m);
+hipError_t launch_panel_fwd(const PanelArgs& p, hipStream_t s);
+hipError_t launch_panel_bwd(const PanelArgs& p, hipStream_t s);
+
 // Split-k rule shared by the workspace query and the launcher.
 void gemm_split_rule(int64_t m, int64_t n, int64_t k, int32_t* splits, int64_t* k_per_split);
 

@@ -3,7 +3,7 @@
 The per-layer data path of the SYLVIE guide (sections 5 and 11) on one GPU:
 
   forward   quantize_pack(send set) -> [exchange] -> dequant_aggregate_fwd -> dense_project(+ReLU)
-  backward  dense_project(dA, dW; ReLU mask) -> aggregate_bwd(halo columns) -> quantize_pack
+  backward  dense_backward(dA, dW; ReLU mask) -> aggregate_bwd(halo columns) -> quantize_pack
             -> [exchange] -> aggregate_bwd(inner columns) -> dequant_aggregate_fwd(received, add)
 
 The exchange is the identity under the mirror model (halo k is the remote copy of inner node
@@ -115,8 +115,10 @@ class GpuPartition:
         return Messages(torch.empty(max(self.total_words, 1), dtype=torch.int32, device=self.device),
                         torch.empty(self.n_h, 2, dtype=torch.float32, device=self.device))
 
-    def dense_workspace(self, *shapes):
+    def dense_workspace(self, *shapes, backward=None):
         need = max(B.dense_project_workspace(*s) for s in shapes)
+        if backward is not None:
+            need = max(need, B.dense_backward_workspace(*backward))
         if need and (self.dense_ws is None or self.dense_ws.numel() * 4 < need):
             self.dense_ws = torch.empty(need // 4 + 4, dtype=torch.float32, device=self.device)
         return self.dense_ws
@@ -190,7 +192,7 @@ class LayerStack:
         self.dX_halo = torch.empty(gp.n_h, d, dtype=torch.float32, device=dev)
         self.msg_f = [gp.new_messages() for _ in range(self.L)]
         self.msg_b = [gp.new_messages() for _ in range(self.L)]
-        self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), (0, 0, n_in, k_in, d), (1, 0, d, k_in, n_in))
+        self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), backward=(n_in, d, k_in))
 
     def forward_layer(self, l, epoch, hook=None):
         gp, d = self.gp, self.gp.d
@@ -206,10 +208,7 @@ class LayerStack:
     def backward_layer(self, l, epoch, hook=None):
         gp, d = self.gp, self.gp.d
         dH = self.grad_top if l == self.L - 1 else self.dX[l + 1]
-        B.dense_project(0, 0, dH, self.W[l], 0, self.dA[l], prologue=B.PRO_RELU_MASK, aux=self.H[l],
-                        workspace=self.dense_ws)
-        B.dense_project(1, 0, dH, self.A[l], 0, self.dW[l], prologue=B.PRO_RELU_MASK, aux=self.H[l],
-                        workspace=self.dense_ws)
+        B.dense_backward(dH, self.H[l], self.A[l], self.W[l], self.dA[l], self.dW[l], workspace=self.dense_ws)
         if hook: hook("dense_bwd", l)
         g = self.dA[l][:, d:] if self.sage else self.dA[l]
         gp.aggregate_bwd_halo(g, self.dX_halo)

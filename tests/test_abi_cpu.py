@@ -194,3 +194,25 @@ def test_device_calls_reject_bad_arguments_before_any_hip_call():
     assert p(1, 0, 128, 128, 300000, FAKE, 128, FAKE, 128, 0, FAKE, 128, 0, None, 0, 0, None, 0, None) == B.QHA_ERR_WORKSPACE
     assert B._last_error().decode().startswith("workspace")
     assert B._degree_norm(FAKE, 10, 7, FAKE, None) == B.QHA_ERR_INVALID_ARG
+
+    b = B._dense_bwd
+    bargs = dict(m=1000, n=128, k=128, dh=FAKE, ldg=128, h=FAKE, ldh=128, a=FAKE, lda=128, w=FAKE, ldw=128,
+                 da=FAKE, ldda=128, dw=FAKE, lddw=128, ws=None, wsb=0, s=None)
+
+    def bcall(**kw):
+        a = dict(bargs, **kw)
+        return b(*a.values())
+    # the width-128 panel path needs one float dW partial per block
+    assert B.dense_backward_workspace(1000, 128, 128) == 16 * 128 * 128 * 4
+    assert B.dense_backward_workspace(300000, 128, 128) == 256 * 128 * 128 * 4
+    assert bcall() == B.QHA_ERR_WORKSPACE
+    assert bcall(ws=FAKE + 8, wsb=1 << 30) == B.QHA_ERR_INVALID_ARG     # misaligned workspace
+    assert bcall(n=126, ldg=126, ldh=126) == B.QHA_ERR_INVALID_ARG     # widths not multiples of 4
+    assert bcall(h=FAKE + 4) == B.QHA_ERR_INVALID_ARG                   # misaligned H
+    assert bcall(lda=64) == B.QHA_ERR_INVALID_ARG                       # leading dimension below k
+    assert bcall(w=None) == B.QHA_ERR_INVALID_ARG
+    assert bcall(m=-1) == B.QHA_ERR_INVALID_ARG
+    # other widths take the general products, whose dW reduction may split
+    assert B.dense_backward_workspace(300000, 256, 512) == B.dense_project_workspace(1, 0, 256, 512, 300000)
+    assert bcall(n=256, k=512, ldg=256, ldh=256, lda=512, ldw=512, ldda=512, lddw=512, m=300000) == B.QHA_ERR_WORKSPACE
+    assert bcall(n=0) == B.QHA_OK

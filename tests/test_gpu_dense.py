@@ -9,8 +9,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("m,d_in,d_out", [(1, 16, 16), (1001, 16, 16), (777, 64, 64), (3001, 128, 128),
+                                          (1, 128, 128), (65, 128, 128), (70001, 128, 128),
                                           (1000, 256, 256), (513, 512, 256), (130, 32, 48)])
 def test_forward_projection_relu(m, d_in, d_out):
+    """d_in = d_out = 128 runs the row-panel kernel (W in LDS; ragged last panel, several panels per
+    block at m = 70001); beta = 1 always takes the general kernel."""
     H.require_gpu()
     import torch
     from quantized_halo_aggregation_amd import binding as B
@@ -79,7 +82,61 @@ def test_strided_operands_and_empty_reduction():
     c = torch.full((m, d), np.nan, dtype=torch.float32, device="cuda")
     B.dense_project(0, 1, a_d[:, :d], H.dev(np.ascontiguousarray(w[:, d:])), 0, c)
     H.assert_close(H.host(c), acat[:, :d].astype(np.float64) @ w[:, d:].T.astype(np.float64), what="strided A")
+    # the width-128 row-panel kernel with strided A and C
+    big2 = torch.full((m, 3 * d), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, a_d[:, d:], H.dev(np.ascontiguousarray(w[:, :d])), 0, big2[:, d:2 * d], epilogue=B.EPI_RELU)
+    got2 = H.host(big2)
+    H.assert_close(got2[:, d:2 * d], OD.project(acat[:, d:], np.ascontiguousarray(w[:, :d])), what="panel strided")
+    assert np.isnan(got2[:, :d]).all() and np.isnan(got2[:, 2 * d:]).all()
     # an empty reduction writes zeros (then the epilogue)
     z = torch.full((m, d), np.nan, dtype=torch.float32, device="cuda")
     B.dense_project(0, 1, a_d[:, :0], torch.empty((d, 0), dtype=torch.float32, device="cuda"), 0, z)
     assert not H.host(z).any()
+
+
+@pytest.mark.parametrize("m,d_in,d_out", [(1, 128, 128), (63, 128, 128), (65, 128, 128), (3001, 128, 128),
+                                          (70001, 128, 128), (1001, 16, 16), (2000, 256, 256), (4099, 512, 256)])
+def test_fused_dense_backward(m, d_in, d_out):
+    """qha_dense_backward: dA and dW in one call.  Width 128 runs the fused row-panel kernel (ragged
+    panels, several panels per block at m = 70001, strided dH / H rows); other widths the general
+    products.  Bitwise repeatable."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(m * 7 + d_in)
+    a = rng.standard_normal((m, d_in)).astype(np.float32)
+    w = (rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).astype(np.float32)
+    h = OD.project(a, w).astype(np.float32)
+    dh = rng.standard_normal((m, d_out)).astype(np.float32)
+    da_ref, dw_ref = OD.project_backward(a, w, h, dh)
+    ws_bytes = B.dense_backward_workspace(m, d_out, d_in)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    H.note(f"dense_backward m={m} {d_in}->{d_out} ws={ws_bytes}")
+    # dH and H as column slices of wider buffers (row stride 2 * d_out)
+    wide = torch.full((m, 4 * d_out), np.nan, dtype=torch.float32, device="cuda")
+    wide[:, :d_out] = H.dev(dh)
+    wide[:, 2 * d_out:3 * d_out] = H.dev(h)
+    dh_d, h_d = wide[:, :d_out], wide[:, 2 * d_out:3 * d_out]
+    a_d, w_d = H.dev(a), H.dev(w)
+    da = torch.full((m, d_in), np.nan, dtype=torch.float32, device="cuda")
+    dw = torch.full((d_out, d_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_backward(dh_d, h_d, a_d, w_d, da, dw, workspace=ws)
+    got_da, got_dw = H.host(da), H.host(dw)
+    H.assert_close(got_da, da_ref, what="dA")
+    H.assert_close_normwise(got_dw, dw_ref, what="dW")
+    da2, dw2 = torch.empty_like(da), torch.empty_like(dw)
+    B.dense_backward(dh_d, h_d, a_d, w_d, da2, dw2, workspace=ws)
+    assert np.array_equal(H.host(da2).view(np.uint32), got_da.view(np.uint32))
+    assert np.array_equal(H.host(dw2).view(np.uint32), got_dw.view(np.uint32))
+
+
+def test_dense_backward_of_no_rows_writes_zero_weight_gradient():
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    e = torch.empty((0, 128), dtype=torch.float32, device="cuda")
+    w = torch.ones((128, 128), dtype=torch.float32, device="cuda")
+    dw = torch.full((128, 128), np.nan, dtype=torch.float32, device="cuda")
+    H.note("dense_backward m=0")
+    B.dense_backward(e, e, e, w, e, dw)
+    assert not H.host(dw).any()
