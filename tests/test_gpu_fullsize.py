@@ -1,0 +1,153 @@
+"""Full-size parity: every call of a layer on the synthetic partitions at their real sizes (300k to
+1.8M inner nodes, 7.5M to 62M edges), in the launch configuration bench.py times (the same
+GpuPartition plans, workspaces and layouts), against the oracle.
+
+Each call is fed seeded inputs of its real shape, or the oracle's own messages, so that no oracle
+input comes from the GPU.  Quantised messages are compared bit for bit in full; aggregations and
+projections on sampled rows and columns (random ones plus the heaviest rows and columns, which
+the plan splits into chunks, and the first and last), which the oracle computes one by one from
+its sparse matrix; dW is compared in full.
+"""
+import numpy as np
+import pytest
+
+import gpu_helpers as H
+from oracle import aggregate as OA
+from oracle import dense as OD
+from oracle import layer as OL
+from quantized_halo_aggregation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = synth.QUANT_SEED
+N_SAMPLE = 1500
+
+
+def _sample(rng, n, weight, k=N_SAMPLE, heavy=16):
+    pick = set(rng.choice(n, size=min(k, n), replace=False).tolist())
+    pick.update(np.argsort(weight)[-heavy:].tolist())
+    pick.update([0, n - 1])
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def _rows_product(mat, rows, x):
+    """mat[rows] @ x in float64, touching only the columns those rows use."""
+    sub = mat[rows]
+    used = np.unique(sub.indices)
+    remap = np.zeros(mat.shape[1], dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    import scipy.sparse as sp
+    small = sp.csr_matrix((sub.data, remap[sub.indices], sub.indptr), shape=(rows.size, used.size))
+    return np.asarray(small @ np.asarray(x[used], dtype=np.float64))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wl_index", [2, 3, 4, 5])
+def test_full_size_layer_calls(wl_index):
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition
+
+    wl = synth.WORKLOADS[wl_index]
+    H.note(f"full size {wl.name}: generating")
+    part = synth.make_partition(wl)
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    sage = wl.model == "sage"
+    k_in = 2 * d if sage else d
+    layer = wl.layers - 1                      # the stream ids of the last layer
+    gp = GpuPartition(part)
+    rng = np.random.default_rng(700 + wl_index)
+
+    # the oracle's normalised matrix (rows: inner nodes, columns: inner then halo nodes)
+    mat = OA.mean_matrix(part.nbr_ptr, part.nbr_idx, n_in + n_h) if sage else \
+        OA.gcn_matrix(part.nbr_ptr, part.nbr_idx, part.deg)
+    mat_c = mat.tocsc()
+    rows = _sample(rng, n_in, np.diff(mat.indptr))
+    cols = _sample(rng, n_in + n_h, np.diff(mat_c.indptr))
+    cols_in, cols_h = cols[cols < n_in], cols[cols >= n_in] - n_in
+
+    # ---- a1: quantise the send set x[mirror] (full message, bit for bit) ----------------------
+    H.note(f"full size {wl.name}: quantize fwd")
+    x = part.x
+    x_d = H.dev(x)
+    msg = gp.new_messages()
+    gp.quantize_send(x_d, gp.mirror, msg, 0, 2 * layer)
+    ref_f = OL.send_halo(x[part.mirror], part.bits, SEED, 0, 2 * layer, n_in)
+    H.assert_bits_equal(H.host(msg.codes).view(np.uint32)[:ref_f["words"].size], ref_f["words"], "codes fwd")
+    H.assert_bits_equal(H.host(msg.scale), ref_f["scale"], "scale fwd")
+    H.assert_bits_equal(H.host(msg.zero_point), ref_f["zero_point"], "zero-point fwd")
+    del msg
+
+    # ---- a3: dequantise + aggregate with the oracle's message ---------------------------------
+    H.note(f"full size {wl.name}: aggregate fwd")
+    omsg = H.upload_messages(gp, ref_f)
+    if sage:
+        acat = torch.full((n_in, 2 * d), np.nan, dtype=torch.float32, device="cuda")
+        out = acat[:, d:]
+    else:
+        out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_fwd(x_d, omsg, out)
+    x_cols = np.concatenate([x, ref_f["received"]])
+    H.assert_close(H.host(out)[rows], _rows_product(mat, rows, x_cols), what="aggregate fwd (sampled rows)")
+    del out, omsg, x_cols
+    if sage:
+        del acat
+
+    # ---- a4: dense forward on a seeded input ---------------------------------------------------
+    H.note(f"full size {wl.name}: dense fwd")
+    w = part.weights[layer]
+    a_in = rng.standard_normal((n_in, k_in)).astype(np.float32)
+    a_d, w_d = H.dev(a_in), H.dev(w)
+    h_out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, a_d, w_d, 0, h_out, epilogue=B.EPI_RELU)
+    H.assert_close(H.host(h_out)[rows], OD.project(a_in[rows], w), what="dense fwd (sampled rows)")
+    del h_out
+
+    # ---- a5: dense backward on seeded dH and H -------------------------------------------------
+    H.note(f"full size {wl.name}: dense bwd")
+    dh = rng.standard_normal((n_in, d)).astype(np.float32)
+    hh = np.maximum(rng.standard_normal((n_in, d)), 0).astype(np.float32)
+    ws = gp.dense_workspace((0, 1, n_in, d, k_in), backward=(n_in, d, k_in))
+    da = torch.full((n_in, k_in), np.nan, dtype=torch.float32, device="cuda")
+    dw = torch.full((d, k_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_backward(H.dev(dh), H.dev(hh), a_d, w_d, da, dw, workspace=ws)
+    dz = np.where(hh > 0, dh, 0).astype(np.float64)
+    H.assert_close(H.host(da)[rows], dz[rows] @ w.astype(np.float64), what="dA (sampled rows)")
+    H.assert_close_normwise(H.host(dw), dz.T @ a_in.astype(np.float64), what="dW")
+    del da, dw, a_d, dz, dh, hh, a_in
+
+    # ---- a6: transposed aggregation over halo and inner columns, seeded upstream gradient -----
+    H.note(f"full size {wl.name}: aggregate bwd")
+    g = rng.standard_normal((n_in, d)).astype(np.float32)
+    g_d = H.dev(g)
+    dxh = torch.full((n_h, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_halo(g_d, dxh)
+    ref_h = np.asarray(mat_c[:, n_in + cols_h].T @ g.astype(np.float64))
+    H.assert_close(H.host(dxh)[cols_h], ref_h, what="dX halo (sampled columns)")
+    beta = 1 if sage else 0
+    dxi0 = rng.standard_normal((n_in, d)).astype(np.float32)
+    dxi = H.dev(dxi0)
+    gp.aggregate_bwd_inner(g_d, dxi, beta)
+    ref_i = np.asarray(mat_c[:, cols_in].T @ g.astype(np.float64)) + (dxi0[cols_in] if beta else 0)
+    H.assert_close(H.host(dxi)[cols_in], ref_i, what="dX inner (sampled columns)")
+    del g_d, dxh, dxi
+
+    # ---- a7: quantise halo gradients (same widths, backward stream) ----------------------------
+    H.note(f"full size {wl.name}: quantize bwd")
+    gh = (0.05 * rng.standard_normal((n_h, d))).astype(np.float32)
+    msg_b = gp.new_messages()
+    gp.quantize_send(H.dev(gh), None, msg_b, 0, 2 * layer + 1)
+    ref_b = OL.send_halo(gh, part.bits, SEED, 0, 2 * layer + 1, n_in)
+    H.assert_bits_equal(H.host(msg_b.codes).view(np.uint32)[:ref_b["words"].size], ref_b["words"], "codes bwd")
+    H.assert_bits_equal(H.host(msg_b.scale), ref_b["scale"], "scale bwd")
+    H.assert_bits_equal(H.host(msg_b.zero_point), ref_b["zero_point"], "zero-point bwd")
+    del msg_b
+
+    # ---- a8: dequantise + add the received gradients into their mirrors -----------------------
+    H.note(f"full size {wl.name}: received add")
+    omsg_b = H.upload_messages(gp, ref_b)
+    dxr = H.dev(dxi0)
+    gp.add_received(omsg_b, dxr)
+    ref_r = OA.add_received(dxi0, part.mirror, ref_b["received"])
+    H.assert_close(H.host(dxr)[rows], ref_r[rows], what="received add (sampled rows)")
