@@ -20,6 +20,10 @@ What it computes, and in what precision (SYLVIE guide, referred to below as "the
                    gradient of guide section 7.  Float64.
 * ``layer``     -- whole layers (forward and backward) for one GPU's share of a partition, chained
                    from the pieces above.
+* ``control``   -- the host-side width control: the Graph Extractor's importance and mask levels
+                   (guide section 7), the Quant Orchestrator's per-epoch widths (section 9) and the
+                   Coordinator's loss-descent-rate rule for the base width and execution mode
+                   (section 8).  Exact integer decisions; the Coordinator in float64.
 
 Readings of points the guide leaves open are stated where they are used.
 """
