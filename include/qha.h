@@ -271,6 +271,58 @@ int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t
                        float* dw, int64_t lddw, void* workspace, size_t workspace_bytes, void* stream);
 size_t qha_dense_backward_workspace(int64_t m, int64_t n, int64_t k);
 
+/* ------------------------------------------------------------------------------------------
+ * Host-side width control (plain host memory, no device work)
+ * ---------------------------------------------------------------------------------------- */
+
+/* Graph Extractor (guide section 7).  deg: host [n] global in-degrees of the boundary-node pool.
+ * A node's importance is the fraction of the pool whose degree is at most its own (the largest
+ * degree gets 1, equal degrees equal importance, relabelling nodes changes nothing); with
+ * n_levels candidate widths its mask level is ceil(importance * n_levels) - 1, computed exactly
+ * in integers.  Writes level (host [n]) and, if not NULL, importance (host [n]).
+ * Errors: INVALID_ARG (null arrays, n < 0, n_levels outside 1 .. QHA_MAX_LEVELS). */
+#define QHA_MAX_LEVELS 8
+int qha_mask_levels(const int32_t* deg, int64_t n, int32_t n_levels, uint8_t* level, double* importance);
+
+/* Quant Orchestrator (guide section 9, Figure 7): the epoch's per-node widths from the mask
+ * levels and the Coordinator's base width, bits[i] = min(base_bits << level[i], max_bits).
+ * base_bits and max_bits are 1, 2, 4 or 8, base_bits <= max_bits; levels < QHA_MAX_LEVELS.
+ * Host arrays.  Errors: INVALID_ARG. */
+int qha_node_bits(const uint8_t* level, int64_t n, int32_t base_bits, int32_t max_bits, uint8_t* bits);
+
+/* A halo numbering by descending mask level (ties keep their order): order[i] is the node placed
+ * at position i.  Widths from qha_node_bits never increase along it, for every base width, so a
+ * buffer packed in this order stays grouped by width (qha_pack_classes) in every epoch.
+ * Host arrays.  Errors: INVALID_ARG. */
+int qha_level_order(const uint8_t* level, int64_t n, int32_t* order);
+
+/* Coordinator (guide section 8, Eq. 3-5).  One call per epoch t with the partitions' losses and
+ * the epoch's time: L_t = mean loss, F_t = lambda F_{t-1} + (1 - lambda) L_t (F starts at L_0),
+ * LDR_t = (F_t - F_{t-1}) / time.  The returned base width for epoch t + 1 is b_min after epoch 0;
+ * for t > delta it doubles (at most b_max) if LDR_t < LDR_{t-delta} and halves (at least b_min)
+ * otherwise, with the next epoch synchronous in the first case and asynchronous in the second;
+ * for 0 < t <= delta width and mode stay.  descent_magnitude = 1 compares -LDR instead (the
+ * reading where "LDR got worse" means the descent slowed).  The state is caller-owned and plain
+ * data.  Errors: INVALID_ARG (lambda outside [0, 1], delta outside 1 .. QHA_LDR_MAX_DELTA, widths
+ * not powers of two in 1 .. 8 with b_min <= b_max, no partitions, a non-positive time). */
+#define QHA_LDR_MAX_DELTA 64
+typedef struct qha_coordinator {
+  double lambda;
+  double sign;                           /* +1, or -1 with descent_magnitude */
+  double f_prev;                         /* F_{t-1} */
+  double last_ldr;                       /* LDR of the last recorded epoch */
+  double ldr[QHA_LDR_MAX_DELTA + 1];     /* the last delta + 1 LDR values, by t % (delta + 1) */
+  int64_t t;                             /* epochs recorded so far */
+  int32_t delta, b_min, b_max;
+  int32_t bits;                          /* base width of the next epoch */
+  int32_t sync;                          /* 1: the next epoch runs synchronously */
+} qha_coordinator;
+
+int qha_coordinator_init(qha_coordinator* c, double lambda, int32_t delta, int32_t b_min, int32_t b_max,
+                         int32_t descent_magnitude);
+int qha_coordinator_step(qha_coordinator* c, const double* losses, int32_t n_partitions, double epoch_time,
+                         int32_t* next_bits, int32_t* next_sync);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,16 @@ class WidthClassesStruct(C.Structure):
                 ("base", _u32 * MAX_CLASSES)]
 
 
+MAX_LEVELS = 8
+LDR_MAX_DELTA = 64
+
+
+class CoordinatorStruct(C.Structure):
+    _fields_ = [("lambda_", C.c_double), ("sign", C.c_double), ("f_prev", C.c_double), ("last_ldr", C.c_double),
+                ("ldr", C.c_double * (LDR_MAX_DELTA + 1)), ("t", _i64), ("delta", _i32), ("b_min", _i32),
+                ("b_max", _i32), ("bits", _i32), ("sync", _i32)]
+
+
 def _sig(name, res, *args):
     f = getattr(_lib, name)
     f.restype = res
@@ -77,6 +87,11 @@ _status_string = _sig("qha_status_string", C.c_char_p, _i32)
 _last_error = _sig("qha_last_error", C.c_char_p)
 _pack_layout = _sig("qha_pack_layout", _i32, _vp, _i64, _i32, _vp, _P(_u64))
 _pack_classes = _sig("qha_pack_classes", _i32, _vp, _i64, _i32, _P(WidthClassesStruct))
+_mask_levels = _sig("qha_mask_levels", _i32, _vp, _i64, _i32, _vp, _vp)
+_node_bits = _sig("qha_node_bits", _i32, _vp, _i64, _i32, _i32, _vp)
+_level_order = _sig("qha_level_order", _i32, _vp, _i64, _vp)
+_coord_init = _sig("qha_coordinator_init", _i32, _P(CoordinatorStruct), C.c_double, _i32, _i32, _i32, _i32)
+_coord_step = _sig("qha_coordinator_step", _i32, _P(CoordinatorStruct), _vp, _i32, C.c_double, _P(_i32), _P(_i32))
 _edge_weights = _sig("qha_edge_weights", _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp)
 _validate_csr = _sig("qha_validate_csr", _i32, _i64, _i64, _vp, _vp, _i32)
 _csr_transpose = _sig("qha_csr_transpose", _i32, _i64, _i64, _vp, _vp, _vp, _vp)
@@ -103,7 +118,8 @@ EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_
             "qha_csr_transpose", "qha_agg_plan_size", "qha_agg_plan_fill", "qha_agg_workspace_bytes",
             "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_aggregate_bwd",
             "qha_dense_project", "qha_dense_project_workspace", "qha_dense_backward",
-            "qha_dense_backward_workspace"]
+            "qha_dense_backward_workspace", "qha_mask_levels", "qha_node_bits", "qha_level_order",
+            "qha_coordinator_init", "qha_coordinator_step"]
 
 
 class QhaError(RuntimeError):
@@ -197,6 +213,47 @@ def pack_classes(bits, d: int):
         return None
     _check(status, "qha_pack_classes")
     return st
+
+
+def mask_levels(deg, n_levels: int = 4):
+    """Graph Extractor: (levels uint8, importance float64) of a boundary pool's global degrees."""
+    deg, pd = _host(deg, np.int32, "deg")
+    level = np.empty(deg.size, np.uint8)
+    imp = np.empty(deg.size, np.float64)
+    _check(_mask_levels(pd, deg.size, int(n_levels), level.ctypes.data, imp.ctypes.data), "qha_mask_levels")
+    return level, imp
+
+
+def node_bits(level, base_bits: int, max_bits: int = 8):
+    """Quant Orchestrator: the epoch's per-node widths (uint8)."""
+    level, pl = _host(level, np.uint8, "level")
+    bits = np.empty(level.size, np.uint8)
+    _check(_node_bits(pl, level.size, int(base_bits), int(max_bits), bits.ctypes.data), "qha_node_bits")
+    return bits
+
+
+def level_order(level):
+    level, pl = _host(level, np.uint8, "level")
+    order = np.empty(level.size, np.int32)
+    _check(_level_order(pl, level.size, order.ctypes.data), "qha_level_order")
+    return order
+
+
+class Coordinator:
+    """The base width and execution mode per epoch (guide section 8); state lives in the C struct."""
+
+    def __init__(self, lam: float = 0.9, delta: int = 5, b_min: int = 1, b_max: int = 8,
+                 descent_magnitude: bool = False):
+        self.state = CoordinatorStruct()
+        _check(_coord_init(C.byref(self.state), float(lam), int(delta), int(b_min), int(b_max),
+                           int(bool(descent_magnitude))), "qha_coordinator_init")
+
+    def step(self, partition_losses, epoch_time: float):
+        losses = np.ascontiguousarray(partition_losses, dtype=np.float64)
+        bits, sync = _i32(), _i32()
+        _check(_coord_step(C.byref(self.state), losses.ctypes.data, losses.size, float(epoch_time), C.byref(bits),
+                           C.byref(sync)), "qha_coordinator_step")
+        return int(bits.value), bool(sync.value)
 
 
 def validate_csr(rowptr, colidx, n_cols: int, require_sorted: bool = True):

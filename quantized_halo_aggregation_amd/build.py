@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqha.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["abi.cpp", "quantize.hip", "gather.hip", "gemm.hip", "panel.hip"]
+SOURCES = ["abi.cpp", "control.cpp", "quantize.hip", "gather.hip", "gemm.hip", "panel.hip"]
 HEADERS = ["qha_internal.hpp"]
 
 ARCH = "gfx950"

@@ -11,8 +11,10 @@
 #include <vector>
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
+
+namespace qha {
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -26,6 +28,13 @@ int ok() {
   g_err[0] = '\0';
   return QHA_OK;
 }
+
+}  // namespace qha
+
+using qha::fail;
+using qha::ok;
+
+namespace {
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();

@@ -8,6 +8,10 @@
 
 namespace qha {
 
+// Status helpers of the C ABI (the message is kept per thread for qha_last_error).
+int fail(int status, const char* fmt, ...);
+int ok();
+
 constexpr int kMaxClasses = 8;
 
 // Width classes of a width-grouped packed buffer (copied into kernel arguments); n == 0 means
