@@ -3,9 +3,10 @@
 
 A step is one pass of the whole hot path over the 300k-inner + 150k-halo, d = 128 partition
 (power-law in-degree, mean 25; halo widths 4 bits, 8 bits for the top 10% by degree):
-quantise the send set, fused dequantise + aggregate, project + ReLU, project backward (dA, dW),
-transposed aggregate over the halo columns, quantise the halo gradients, transposed aggregate over
-the inner columns, dequantise + add the received gradients.
+quantise the send set, fused dequantise + aggregate, project + ReLU, project backward (dA and dW in
+one pass), transposed aggregate over the halo columns, quantise the halo gradients (or both in one
+call with --fused-halo-bwd), transposed aggregate over the inner columns, dequantise + add the
+received gradients.
 
 Prints one JSON line.  value = algorithmic bytes of the quantise and aggregate calls of a step
 divided by the whole step's wall time (the dense projections are inside the timed step too).
@@ -46,6 +47,14 @@ def quantize_bytes(n_rows, d, bits, gathered):
     return int(n_rows * per_row + 4 * w.sum())
 
 
+def gather_quant_bytes(colptr, n_edges, d, halo_words):
+    """The transposed gather over the halo columns with the quantisation fused in: every edge reads
+    its row index, its weight and a d-float gradient row; every halo column reads its bound and
+    writes its packed codes and (min, scale) instead of d floats."""
+    n_rows = colptr.size - 1
+    return int(n_edges * (8 + 4 * d) + n_rows * (4 + 8) + 4 * halo_words.sum())
+
+
 def gather_bytes(rowptr, colidx, n_inner, d, halo_words, beta, weighted=True, row_ids=False):
     """Per-edge gather model: every edge reads its column index, its weight and a whole feature row
     (inner) or its packed code row plus (min, scale) (halo); every row reads its bound, writes d
@@ -70,6 +79,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="synthetic partition index (2 = 300k-node d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--fused-halo-bwd", action="store_true",
+                    help="quantise the halo gradients inside the transposed gather (one call) instead of "
+                         "gathering them into a buffer and quantising that")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -94,7 +106,7 @@ def main():
     gen_s = time.time() - t0
     print(f"[bench] generated {wl.describe()} in {gen_s:.1f}s", file=sys.stderr, flush=True)
     gp = GpuPartition(part, chunk=args.chunk or B.DEFAULT_CHUNK)
-    st = LayerStack(gp, part.weights, part.x, part.grad_top)
+    st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd)
     torch.cuda.synchronize()
     print("[bench] device set-up done", file=sys.stderr, flush=True)
 
@@ -103,14 +115,17 @@ def main():
     nw = gp.h_colptr
     # algorithmic bytes per call of one layer
     b_q_fwd = quantize_bytes(n_h, d, part.bits, gathered=True)
-    b_q_bwd = quantize_bytes(n_h, d, part.bits, gathered=False)
     sage = wl.model == "sage"
     b_agg_fwd = gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0)
-    b_bwd_halo = gather_bytes(nw[n_in:], gp.h_rowidx[nw[n_in]:], 1 << 62, d, hw, beta=0)
     b_bwd_inner = gather_bytes(nw[:n_in + 1], gp.h_rowidx[:nw[n_in]], 1 << 62, d, hw, beta=1 if sage else 0)
     b_add = gather_bytes(gp.h_m_ptr, np.arange(n_h), 0, d, hw, beta=1, weighted=False, row_ids=True)
-    bytes_by_stage = {"quantize_fwd": b_q_fwd, "aggregate_fwd": b_agg_fwd, "aggregate_bwd_halo": b_bwd_halo,
-                      "quantize_bwd": b_q_bwd, "aggregate_bwd_inner": b_bwd_inner, "add_received": b_add}
+    if args.fused_halo_bwd:
+        halo_bwd = {"aggregate_bwd_halo_quantize": gather_quant_bytes(nw[n_in:], int(nw[-1] - nw[n_in]), d, hw)}
+    else:
+        halo_bwd = {"aggregate_bwd_halo": gather_bytes(nw[n_in:], gp.h_rowidx[nw[n_in]:], 1 << 62, d, hw, beta=0),
+                    "quantize_bwd": quantize_bytes(n_h, d, part.bits, gathered=False)}
+    bytes_by_stage = {"quantize_fwd": b_q_fwd, "aggregate_fwd": b_agg_fwd, **halo_bwd,
+                      "aggregate_bwd_inner": b_bwd_inner, "add_received": b_add}
     k_in = 2 * d if sage else d
     flops_by_stage = {"dense_fwd": 2 * n_in * k_in * d, "dense_bwd": 4 * n_in * k_in * d}
     qa_bytes_step = wl.layers * sum(bytes_by_stage.values())
@@ -118,8 +133,8 @@ def main():
 
     # ---- timing ------------------------------------------------------------------------------
     stream = torch.cuda.current_stream()
-    stages = ["quantize_fwd", "aggregate_fwd", "dense_fwd", "dense_bwd", "aggregate_bwd_halo", "quantize_bwd",
-              "aggregate_bwd_inner", "add_received"]
+    stages = ["quantize_fwd", "aggregate_fwd", "dense_fwd", "dense_bwd", *halo_bwd, "aggregate_bwd_inner",
+              "add_received"]
     events = []
 
     def hook(name, layer):

@@ -11,7 +11,9 @@
  *   qha_quantize_pack         per-vector stochastic integer quantisation + bit packing
  *   qha_dequant_aggregate_fwd dequantisation fused into the normalised neighbour gather (SpMM)
  *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
- *   qha_dense_project         the dense projection (fp32 MFMA) with ReLU, and its gradients
+ *   qha_aggregate_bwd_quantize the same over the halo columns, quantising each gradient row
+ *   qha_dense_project         the dense projection (fp32 MFMA) with ReLU
+ *   qha_dense_backward        its gradients dA and dW in one pass
  *
  * plus small set-up helpers.  Conventions shared by every entry point:
  *   - Array arguments are caller-owned.  Pointers documented as "device" must be HIP device
@@ -231,6 +233,22 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
                       int32_t d, int32_t beta, float* grad_in, int64_t ldi,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* The transposed gather over the halo columns with the sender's quantisation fused in (guide
+ * section 11: the gradients of the boundary nodes are quantised with the same per-node widths and
+ * sent; section 6 for the code).  For every row r < n_rows of the transposed CSR it forms
+ * g_r = sum over the row's entries of w * grad_out (as qha_aggregate_bwd with beta = 0, rounded to
+ * float32) and codes g_r exactly as qha_quantize_pack codes a row holding g_r (node id
+ * node_base + r, the same seed / epoch / stream_id, widths from classes or bits / word_offset,
+ * codes and (min, scale) written in place), without storing g_r.  The plan must not skip empty
+ * rows: an empty row is a zero gradient and is coded as one.  Arguments as in qha_aggregate_bwd
+ * and qha_quantize_pack; errors likewise. */
+int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,
+                               const qha_agg_plan* plan, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
+                               int32_t d, const uint8_t* bits, const uint32_t* word_offset,
+                               const qha_width_classes* classes, uint64_t seed, uint32_t epoch, uint32_t stream_id,
+                               uint32_t node_base, uint32_t* codes, float* meta, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Dense projection and its gradients (guide section 2: z_v = W a_v, h_v = sigma(z_v); section 7:
  * dL/dW = sum_v (dL/dh_v * sigma'(z_v)) a_v^T) on fp32 matrix cores (MFMA):
  *   C[m x n] = (beta ? C : 0) + op(A)[m x k] * op(B)[k x n]
@@ -252,7 +270,7 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
                       void* workspace, size_t workspace_bytes, void* stream);
 size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k);
 
-/* 5. dense_backward -- the backward of one dense layer H = ReLU(A W^T) over m rows, in one call
+/* The backward of one dense layer H = ReLU(A W^T) over m rows, in one call
  * (guide section 7: the weight gradient sums (dL/dh_v * sigma'(z_v)) a_v^T over the rows, and
  * section 3: the embedding gradient dA flows back to the aggregation):
  *   dZ = dH * [H > 0],   dA = dZ W   [m x k],   dW = dZ^T A   [n x k]

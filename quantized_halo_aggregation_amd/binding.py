@@ -106,6 +106,9 @@ _dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp,
                               _sz, _vp)
 _aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64, _i64, _i32, _i32,
                       _vp, _i64, _vp, _sz, _vp)
+_aggregate_bwd_quantize = _sig("qha_aggregate_bwd_quantize", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64,
+                               _i64, _i32, _vp, _vp, _P(WidthClassesStruct), _u64, _u32, _u32, _u32, _vp, _vp, _vp,
+                               _sz, _vp)
 _dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
                       _i64, _i32, _vp, _i64, _i32, _vp, _sz, _vp)
 _dense_ws = _sig("qha_dense_project_workspace", _sz, _i32, _i32, _i64, _i64, _i64)
@@ -117,7 +120,7 @@ EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_
             "qha_edge_weights", "qha_validate_csr",
             "qha_csr_transpose", "qha_agg_plan_size", "qha_agg_plan_fill", "qha_agg_workspace_bytes",
             "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_aggregate_bwd",
-            "qha_dense_project", "qha_dense_project_workspace", "qha_dense_backward",
+            "qha_aggregate_bwd_quantize", "qha_dense_project", "qha_dense_project_workspace", "qha_dense_backward",
             "qha_dense_backward_workspace", "qha_mask_levels", "qha_node_bits", "qha_level_order",
             "qha_coordinator_init", "qha_coordinator_step"]
 
@@ -390,6 +393,24 @@ def aggregate_bwd(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, beta: int
     _check(_aggregate_bwd(n_rows, _dev(colptr, torch.int32, "colptr"), _dev(rowidx, torch.int32, "rowidx"),
                           _dev(w, torch.float32, "w", allow_none=True), _plan_ref(plan), pg, ldg, int(n_grad_rows),
                           int(d), int(beta), pi, ldi, ws_ptr, ws_bytes, _stream(stream)), "qha_aggregate_bwd")
+
+
+def aggregate_bwd_quantize(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, d: int, bits, word_offset, classes,
+                           seed: int, epoch: int, stream_id: int, node_base: int, codes, meta, workspace=None,
+                           n_rows=None, stream=None):
+    """The transposed gather over colptr's rows, each gradient row quantised into codes / meta."""
+    import torch
+    n_rows = colptr.numel() - 1 if n_rows is None else int(n_rows)
+    pg, ldg = _rows(grad_out, "grad_out")
+    ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_aggregate_bwd_quantize(n_rows, _dev(colptr, torch.int32, "colptr"), _dev(rowidx, torch.int32, "rowidx"),
+                                   _dev(w, torch.float32, "w", allow_none=True), _plan_ref(plan), pg, ldg,
+                                   int(n_grad_rows), int(d), _dev(bits, torch.uint8, "bits", allow_none=True),
+                                   None if word_offset is None else _dev32(word_offset, "word_offset"),
+                                   _cls_ref(classes), int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch), int(stream_id),
+                                   int(node_base), _dev32(codes, "codes"), _dev(meta, torch.float32, "meta"), ws_ptr,
+                                   ws_bytes, _stream(stream)), "qha_aggregate_bwd_quantize")
 
 
 def dense_project(trans_a: int, trans_b: int, a, b, beta: int, c, prologue: int = PRO_NONE, aux=None,

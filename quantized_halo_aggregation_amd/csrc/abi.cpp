@@ -458,6 +458,55 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
   return hip_status(qha::launch_gather(g, d, false, static_cast<hipStream_t>(stream)), "aggregate_bwd");
 }
 
+int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,
+                               const qha_agg_plan* plan, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
+                               int32_t d, const uint8_t* bits, const uint32_t* word_offset,
+                               const qha_width_classes* classes, uint64_t seed, uint32_t epoch, uint32_t stream_id,
+                               uint32_t node_base, uint32_t* codes, float* meta, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > kMaxIndex || n_grad_rows < 0 || n_grad_rows > kMaxIndex)
+    return fail(QHA_ERR_INVALID_ARG, "bad sizes");
+  if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  if (n_rows == 0) return ok();
+  if (!colptr || !rowidx) return fail(QHA_ERR_INVALID_ARG, "colptr/rowidx is NULL");
+  int st = 0;
+  if (n_grad_rows > 0) {
+    st = check_rows("grad_out", grad_out, ldg, d);
+    if (st) return st;
+  }
+  if (!codes || !meta || (!classes && (!bits || !word_offset))) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned4(codes) || !aligned8(meta) || (word_offset && !aligned4(word_offset)))
+    return fail(QHA_ERR_INVALID_ARG, "misaligned array");
+  if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_rows) - 1 > 0xFFFFFFFFull)
+    return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
+  st = check_plan(plan, n_rows, 0, d, workspace, workspace_bytes);
+  if (st) return st;
+  if (plan->skip_empty) return fail(QHA_ERR_INVALID_ARG, "every row is coded: the plan may not skip empty rows");
+  qha::GatherArgs g;
+  std::memset(&g, 0, sizeof(g));
+  st = take_classes(classes, n_rows, d, &g.q.cls);
+  if (st) return st;
+  g.n_rows = n_rows;
+  g.rowptr = colptr;
+  g.colidx = rowidx;
+  fill_plan_args(g, plan, n_rows, workspace);
+  g.w = w;
+  g.x = grad_out;
+  g.ldx = ldg;
+  g.n_inner = n_grad_rows;
+  g.q.codes = codes;
+  g.q.meta = meta;
+  g.q.bits = bits;
+  g.q.word_offset = word_offset;
+  g.q.seed_lo = static_cast<uint32_t>(seed);
+  g.q.seed_hi = static_cast<uint32_t>(seed >> 32);
+  g.q.epoch = epoch;
+  g.q.stream_id = stream_id;
+  g.q.node_base = node_base;
+  return hip_status(qha::launch_gather(g, d, false, static_cast<hipStream_t>(stream), true),
+                    "aggregate_bwd_quantize");
+}
+
 size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k) {
   (void)trans_a;
   (void)trans_b;

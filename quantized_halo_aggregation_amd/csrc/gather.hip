@@ -27,6 +27,7 @@
 // chunk order, so results do not depend on scheduling.
 #include "../../include/qha.h"
 #include "qha_internal.hpp"
+#include "quant_common.hpp"
 
 // the dequantisation scale * q + min is two roundings, as the message format defines it
 #pragma clang fp contract(off)
@@ -59,10 +60,6 @@ __device__ __forceinline__ float rdlanef(float v, int lane) {
 
 __device__ __forceinline__ float dequant(float sc, uint32_t q, float zp) {
   return __fadd_rn(__fmul_rn(sc, static_cast<float>(q)), zp);
-}
-
-__device__ __forceinline__ bool width_ok(uint32_t b) {
-  return b == 1u || b == 2u || b == 4u || b == 8u || b == 32u;
 }
 
 template <int VEC>
@@ -126,7 +123,83 @@ __device__ __forceinline__ void class_of(int32_t v_cstart, int32_t v_cbits, uint
   off = static_cast<uint32_t>(rdlane(static_cast<int>(v_cbase), c)) + static_cast<uint32_t>(k - rdlane(v_cstart, c)) * words;
 }
 
-template <int D, bool HALO, bool BETA, bool GROUPED>
+// Quantises output row k of a gather, held VEC features per lane (lane l owns features l*VEC ..,
+// idle lanes of narrow rows shadow lane 0), with the arithmetic of quantize_pack_kernel: exact
+// row min / max, one Philox call per group of 8 features, codes packed least-significant first
+// and the pieces of lanes that share a word merged with lane shuffles.  Every lane must call it.
+template <int D>
+__device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, const float (&v)[vec_of(D)], int lane,
+                                                 int j0, bool owner) {
+  constexpr int VEC = vec_of(D);
+  constexpr int G = D / VEC;
+  uint32_t b, off;
+  if (q.cls.n > 0) {
+    int32_t st = q.cls.start[0];
+    uint32_t base = q.cls.base[0];
+    b = static_cast<uint32_t>(q.cls.bits[0]);
+#pragma unroll
+    for (int c = 1; c < kMaxClasses; ++c) {
+      if (c < q.cls.n && k >= q.cls.start[c]) {
+        st = q.cls.start[c];
+        base = q.cls.base[c];
+        b = static_cast<uint32_t>(q.cls.bits[c]);
+      }
+    }
+    const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (b * static_cast<uint32_t>(D) + 31u) >> 5;
+    off = base + static_cast<uint32_t>(k - st) * words;
+  } else {
+    b = q.bits[k];
+    off = q.word_offset[k];
+  }
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < VEC; ++i) {
+    mn = fminf(mn, v[i]);
+    mx = fmaxf(mx, v[i]);
+  }
+#pragma unroll
+  for (int o = G / 2; o >= 1; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if (!width_valid(b)) return;              // a row of an unknown width is left untouched
+  uint32_t* row = q.codes + off;
+  if (b == 32u) {
+    if (owner) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) row[j0 + i] = __float_as_uint(v[i]);
+    }
+    if (lane == 0) *reinterpret_cast<float2*>(q.meta + 2 * k) = make_float2(0.0f, 0.0f);
+    return;
+  }
+  const RowScale rs = row_scale(mn, mx, b);
+  uint32_t c0 = q.node_base + static_cast<uint32_t>(k);
+  uint32_t c1 = static_cast<uint32_t>(j0 >> 3);
+  uint32_t c2 = q.epoch;
+  uint32_t c3 = q.stream_id;
+  philox4x32_10(c0, c1, c2, c3, q.seed_lo, q.seed_hi);
+  const uint32_t w[4] = {c0, c1, c2, c3};
+  uint64_t piece = 0;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i)
+    piece |= static_cast<uint64_t>(code_of(v[i], mn, rs, draw16(w, j0 + i))) << (static_cast<uint32_t>(i) * b);
+  const uint32_t lane_bits = static_cast<uint32_t>(VEC) * b;
+  const uint32_t first = (static_cast<uint32_t>(j0) * b) >> 5;
+  if (lane_bits <= 32u) {
+    uint32_t word = static_cast<uint32_t>(piece) << ((static_cast<uint32_t>(j0) * b) & 31u);
+    const uint32_t share = 32u / lane_bits;          // lanes whose pieces fill one word
+    for (uint32_t o = 1; o < share; o <<= 1) word |= __shfl_xor(word, static_cast<int>(o));
+    if (owner && (static_cast<uint32_t>(lane) & (share - 1u)) == 0u) row[first] = word;
+  } else {
+    if (owner) {
+      row[first] = static_cast<uint32_t>(piece);
+      row[first + 1] = static_cast<uint32_t>(piece >> 32);
+    }
+  }
+  if (lane == 0) *reinterpret_cast<float2*>(q.meta + 2 * k) = make_float2(rs.zp, rs.sc);
+}
+
+template <int D, bool HALO, bool BETA, bool GROUPED, bool QUANT>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;           // lanes that own features
@@ -182,8 +255,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
   auto flush = [&]() {                          // write row `cur` and start the next one
     const int64_t orow = rdlane(v_out, cur);
-    float* dst = a.out + orow * a.ldo + j0;
-    if (owner) {
+    if constexpr (QUANT) {
+      float res[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+      quantize_out_row<D>(a.q, orow, res, lane, j0, owner);
+    } else if (owner) {
+      float* dst = a.out + orow * a.ldo + j0;
       float res[VEC];
       if constexpr (BETA) {
         float old[VEC];
@@ -343,7 +421,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
             if (b == 32u) {
 #pragma unroll
               for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
-            } else if (width_ok(b)) {
+            } else if (width_valid(b)) {
               const uint32_t pos = static_cast<uint32_t>(j0) * b;
               cwd[i][0] = row[pos >> 5];
               if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
@@ -360,7 +438,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
           if (HALO && u[i] >= a.n_inner && bw[i] != 32u) {
             const uint32_t b = bw[i];
             float q[VEC];
-            if (width_ok(b)) {
+            if (width_valid(b)) {
               const uint32_t mask = (1u << b) - 1u;
               const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
 #pragma unroll
@@ -396,16 +474,17 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
 }
 
-// Adds the partial sums of every split row in chunk order and writes the row.
-template <int D>
+// Adds the partial sums of every split row in chunk order and writes (or quantises) the row.
+template <int D, bool QUANT>
 __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;
   const int lane = threadIdx.x & 63;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * 4 +
                     __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  if (m >= a.n_split_rows || lane >= G) return;
-  const int j0 = lane * VEC;
+  if (m >= a.n_split_rows) return;
+  const bool owner = lane < G;
+  const int j0 = (owner ? lane : 0) * VEC;          // idle lanes shadow lane 0
   const int64_t row = cst(a.split_row)[m];
   const int32_t i0 = cst(a.split_ptr)[m];
   const int32_t i1 = cst(a.split_ptr)[m + 1];
@@ -417,10 +496,17 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
     for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + a.partial[static_cast<int64_t>(i) * D + j0 + v];
   }
   const int64_t orow = a.row_ids ? a.row_ids[row] : row;
-  float* dst = a.out + orow * a.ldo + j0;
+  if constexpr (QUANT) {
+    float res[VEC];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v)
-    dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
+    for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+    quantize_out_row<D>(a.q, orow, res, lane, j0, owner);
+  } else if (owner) {
+    float* dst = a.out + orow * a.ldo + j0;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v)
+      dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
+  }
 }
 
 __global__ __launch_bounds__(256) void edge_weights_kernel(int64_t n_rows, const int32_t* rowptr,
@@ -439,16 +525,18 @@ __global__ __launch_bounds__(256) void edge_weights_kernel(int64_t n_rows, const
 template <int D, bool HALO, bool BETA>
 void launch_variant(const GatherArgs& a, dim3 grid, hipStream_t s) {
   if (HALO && a.cls.n > 0)
-    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, true, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, false, false>), grid, dim3(256), 0, s, a);
 }
 
 template <int D>
-hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, hipStream_t s) {
+hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_out, hipStream_t s) {
   if (a.n_items > 0) {
     const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
-    if (with_halo) {
+    if (quantize_out) {
+      hipLaunchKernelGGL((gather_kernel<D, false, false, false, true>), grid, dim3(256), 0, s, a);
+    } else if (with_halo) {
       if (a.beta) launch_variant<D, true, true>(a, grid, s);
       else launch_variant<D, true, false>(a, grid, s);
     } else {
@@ -460,7 +548,10 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, hipStream_t s) {
   }
   if (a.n_split_rows > 0) {
     const int64_t blocks = (a.n_split_rows + 3) / 4;
-    hipLaunchKernelGGL((combine_split_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    if (quantize_out)
+      hipLaunchKernelGGL((combine_split_kernel<D, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((combine_split_kernel<D, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -468,14 +559,14 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s) {
+hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s, bool quantize_out) {
   switch (d) {
-    case 16: return launch_gather_d<16>(a, with_halo, s);
-    case 32: return launch_gather_d<32>(a, with_halo, s);
-    case 64: return launch_gather_d<64>(a, with_halo, s);
-    case 128: return launch_gather_d<128>(a, with_halo, s);
-    case 256: return launch_gather_d<256>(a, with_halo, s);
-    case 512: return launch_gather_d<512>(a, with_halo, s);
+    case 16: return launch_gather_d<16>(a, with_halo, quantize_out, s);
+    case 32: return launch_gather_d<32>(a, with_halo, quantize_out, s);
+    case 64: return launch_gather_d<64>(a, with_halo, quantize_out, s);
+    case 128: return launch_gather_d<128>(a, with_halo, quantize_out, s);
+    case 256: return launch_gather_d<256>(a, with_halo, quantize_out, s);
+    case 512: return launch_gather_d<512>(a, with_halo, quantize_out, s);
     default: return hipErrorInvalidValue;
   }
 }

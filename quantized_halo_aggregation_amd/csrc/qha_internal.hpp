@@ -36,6 +36,17 @@ struct QuantArgs {
   float* meta;          // (min, scale) per row
 };
 
+// Quantised output of a gather: each output row r is coded like qha_quantize_pack row r
+// (node id node_base + r) instead of being stored.
+struct QuantOut {
+  uint32_t* codes;
+  float* meta;
+  const uint8_t* bits;
+  const uint32_t* word_offset;
+  Classes cls;
+  uint32_t seed_lo, seed_hi, epoch, stream_id, node_base;
+};
+
 // One gather over a CSR: out[row_ids[i]] (+)= sum_e w[e] * value(col_e).  value() is a float32
 // row of x for col < n_inner and a dequantised halo message for col >= n_inner.
 struct GatherArgs {
@@ -66,6 +77,7 @@ struct GatherArgs {
   float* out;
   int64_t ldo;
   double* partial;            // [n_split_items, d] float64 partial sums of split rows
+  QuantOut q;                 // with launch_gather(..., quantize_out = true)
 };
 
 struct GemmArgs {
@@ -120,7 +132,7 @@ hipError_t launch_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float
 hipError_t launch_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r,
                                const float* c, float* w, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs& a, int32_t d, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s, bool quantize_out = false);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 }  // namespace qha

@@ -11,33 +11,12 @@
 // pieces are merged with lane shuffles (1- and 2-bit rows), so every word is written once.
 // d = 128 gives 16 lanes per row and four rows per wavefront.
 #include "qha_internal.hpp"
+#include "quant_common.hpp"
 
 #pragma clang fp contract(off)
 
 namespace qha {
 namespace {
-
-// Philox4x32-10 (Salmon et al., SC'11): ten rounds of the 4x32 S-box with Weyl key schedule.
-__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
-                                              uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
-    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
-    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
-    c1 = static_cast<uint32_t>(p1);
-    c3 = static_cast<uint32_t>(p0);
-    c0 = n0;
-    c2 = n2;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-}
-
-__device__ __forceinline__ bool width_ok(uint32_t b) {
-  return b == 1u || b == 2u || b == 4u || b == 8u || b == 32u;
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
@@ -96,37 +75,23 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, off));
   }
 
-  const bool active = valid && width_ok(b);
+  const bool active = valid && width_valid(b);
   const bool raw = b == 32u;
   uint32_t lo_w = 0, hi_w = 0;
   float sc = 0.0f, zp = 0.0f;
   if (active && !raw) {
-    const uint32_t Li = (1u << b) - 1u;
-    const float L = static_cast<float>(Li);
-    zp = mn + 0.0f;                     // canonical zero-point (-0 -> +0)
-    const float range = mx - mn;
-    float inv = __fdiv_rn(L, range);
-    const bool flat = (range == 0.0f) || isinf(inv);
-    if (flat) inv = 0.0f;
-    sc = flat ? 0.0f : __fdiv_rn(range, L);
-
+    const RowScale rs = row_scale(mn, mx, b);
+    zp = rs.zp;
+    sc = rs.sc;
     uint32_t c0 = a.node_base + static_cast<uint32_t>(r);
-    uint32_t c1 = static_cast<uint32_t>(gl);
+    uint32_t c1 = static_cast<uint32_t>(gl);          // this lane's 8 features are group gl
     uint32_t c2 = a.epoch;
     uint32_t c3 = a.stream_id;
     philox4x32_10(c0, c1, c2, c3, a.seed_lo, a.seed_hi);
     const uint32_t w[4] = {c0, c1, c2, c3};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float t = v[i] - mn;
-      const float y = t * inv;
-      const float f = floorf(y);
-      const float fr = y - f;
-      const uint32_t u16 = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-      const uint32_t up = (static_cast<float>(u16) < fr * 65536.0f) ? 1u : 0u;
-      uint32_t q = static_cast<uint32_t>(f) + up;
-      q = q > Li ? Li : q;
-      q = flat ? 0u : q;
+      const uint32_t q = code_of(v[i], mn, rs, draw16(w, i));
       const uint32_t pos = static_cast<uint32_t>(i) * b;       // < 64
       if (pos < 32u) lo_w |= q << pos;
       else hi_w |= q << (pos - 32u);

@@ -3,8 +3,9 @@
 The per-layer data path of the SYLVIE guide (sections 5 and 11) on one GPU:
 
   forward   quantize_pack(send set) -> [exchange] -> dequant_aggregate_fwd -> dense_project(+ReLU)
-  backward  dense_backward(dA, dW; ReLU mask) -> aggregate_bwd(halo columns) -> quantize_pack
-            -> [exchange] -> aggregate_bwd(inner columns) -> dequant_aggregate_fwd(received, add)
+  backward  dense_backward(dA, dW; ReLU mask) -> aggregate_bwd_quantize(halo columns; or
+            aggregate_bwd then quantize_pack) -> [exchange] -> aggregate_bwd(inner columns)
+            -> dequant_aggregate_fwd(received, add)
 
 The exchange is the identity under the mirror model (halo k is the remote copy of inner node
 mirror[k]): the codes sent are the codes received.  Everything numeric runs in libqha's kernels;
@@ -143,6 +144,13 @@ class GpuPartition:
         B.aggregate_bwd(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out, self.n_in, 0,
                         dx_halo, workspace=self.agg_ws)
 
+    def aggregate_bwd_halo_quantize(self, grad_out, msg: Messages, epoch, stream_id, seed=QUANT_SEED):
+        """a6 (halo range) + a7 fused: the halo columns' gradients, each quantised into msg as
+        quantize_send would code it, without storing the gradient rows."""
+        B.aggregate_bwd_quantize(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out,
+                                 self.n_in, self.d, self.bits, self.word_offset, self.classes, seed, epoch, stream_id,
+                                 self.n_in, msg.codes, msg.meta, workspace=self.agg_ws)
+
     def aggregate_bwd_inner(self, grad_out, dx_inner, beta):
         """a6 (inner range): gradients of the inner columns (beta = 1 adds to dx_inner)."""
         B.aggregate_bwd(self.colptr[:self.n_in + 1], self.rowidx, self.w_bwd, self.plan_bwd_inner, grad_out,
@@ -158,9 +166,10 @@ class GpuPartition:
 class LayerStack:
     """Buffers and call order of a stack of GCN or GraphSAGE-mean layers on one partition."""
 
-    def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED):
+    def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False):
         self.gp = gp
         self.seed = seed
+        self.fused_halo_bwd = fused_halo_bwd
         dev = gp.device
         n_in, d = gp.n_in, gp.d
         self.L = len(weights)
@@ -189,7 +198,7 @@ class LayerStack:
             self.dX = [self.dA[l][:, :d] for l in range(self.L)]
         else:
             self.dX = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
-        self.dX_halo = torch.empty(gp.n_h, d, dtype=torch.float32, device=dev)
+        self.dX_halo = None if fused_halo_bwd else torch.empty(gp.n_h, d, dtype=torch.float32, device=dev)
         self.msg_f = [gp.new_messages() for _ in range(self.L)]
         self.msg_b = [gp.new_messages() for _ in range(self.L)]
         self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), backward=(n_in, d, k_in))
@@ -211,10 +220,14 @@ class LayerStack:
         B.dense_backward(dH, self.H[l], self.A[l], self.W[l], self.dA[l], self.dW[l], workspace=self.dense_ws)
         if hook: hook("dense_bwd", l)
         g = self.dA[l][:, d:] if self.sage else self.dA[l]
-        gp.aggregate_bwd_halo(g, self.dX_halo)
-        if hook: hook("aggregate_bwd_halo", l)
-        gp.quantize_send(self.dX_halo, None, self.msg_b[l], epoch, 2 * l + 1, self.seed)
-        if hook: hook("quantize_bwd", l)
+        if self.fused_halo_bwd:
+            gp.aggregate_bwd_halo_quantize(g, self.msg_b[l], epoch, 2 * l + 1, self.seed)
+            if hook: hook("aggregate_bwd_halo_quantize", l)
+        else:
+            gp.aggregate_bwd_halo(g, self.dX_halo)
+            if hook: hook("aggregate_bwd_halo", l)
+            gp.quantize_send(self.dX_halo, None, self.msg_b[l], epoch, 2 * l + 1, self.seed)
+            if hook: hook("quantize_bwd", l)
         gp.aggregate_bwd_inner(g, self.dX[l], 1 if self.sage else 0)
         if hook: hook("aggregate_bwd_inner", l)
         gp.add_received(self.msg_b[l], self.dX[l])

@@ -90,16 +90,65 @@ def test_backward_aggregation_and_received_add(case):
     gp.aggregate_bwd_inner(g_dev, dxi0, 0)
     H.assert_close(H.host(dxi0), ref[:n_in], what="aggregate_bwd inner (beta=0)")
 
-    # received halo gradients: quantised by the oracle, dequantised and added on the GPU
+    # received halo gradients: quantised by the oracle, dequantised and added on the GPU to the
+    # oracle's inner gradients
     halo_grad = ref[n_in:].astype(np.float32)
     msg = H.oracle_messages(halo_grad, part.bits, SEED, 0, 1, n_in)
-    want = OA.add_received(H.host(dxi0).astype(np.float64), part.mirror, msg["received"])
-    start = H.host(dxi0)
-    gp.add_received(H.upload_messages(gp, msg), dxi0)
-    got = H.host(dxi0)
+    start = ref[:n_in].astype(np.float32)
+    want = OA.add_received(start, part.mirror, msg["received"])
+    dxr = H.dev(start)
+    gp.add_received(H.upload_messages(gp, msg), dxr)
+    got = H.host(dxr)
     H.assert_close(got, want, what="received add")
     untouched = np.setdiff1d(np.arange(n_in), part.mirror)
     H.assert_bits_equal(got[untouched], start[untouched], "rows without a halo copy")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("grouped", [True, False], ids=["width-classes", "offset-table"])
+def test_fused_halo_gradient_quantisation(case, grouped):
+    """qha_aggregate_bwd_quantize codes each halo column's gradient exactly as qha_aggregate_bwd
+    followed by qha_quantize_pack does (every word and (min, scale) pair, heavy columns split into
+    chunks included), and the dequantised codes lie within one quantisation step of the oracle's
+    float64 gradients."""
+    H.require_gpu()
+    import torch
+    from oracle import quantize as OQ
+    part, gp = _setup(case)
+    gp.set_bits(part.bits, grouped=grouped)
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    g = np.random.default_rng(9).standard_normal((n_in, d)).astype(np.float32)
+    g_dev = H.dev(g)
+    H.note(f"aggregate_bwd_quantize {_case_id(case)} grouped={grouped}")
+    dxh = torch.empty((n_h, d), dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_halo(g_dev, dxh)
+    two = gp.new_messages()
+    gp.quantize_send(dxh, None, two, 3, 5)
+    fused = gp.new_messages()
+    fused.codes.fill_(-559038737)                       # 0xDEADBEEF: every word must be written
+    fused.meta.fill_(float("nan"))
+    gp.aggregate_bwd_halo_quantize(g_dev, fused, 3, 5)
+    words = H.host(fused.codes).view(np.uint32)
+    H.assert_bits_equal(words[:gp.total_words], H.host(two.codes).view(np.uint32)[:gp.total_words], "codes")
+    H.assert_bits_equal(H.host(fused.meta), H.host(two.meta), "(min, scale)")
+
+    if part.wl.model == "gcn":
+        ref = OA.gcn_aggregate_t(part.nbr_ptr, part.nbr_idx, part.deg, g)[n_in:]
+    else:
+        ref = OA.mean_aggregate_t(part.nbr_ptr, part.nbr_idx, g, n_in + n_h)[n_in:]
+    meta = H.host(fused.meta)
+    zp, sc = meta[:, 0].astype(np.float64), meta[:, 1].astype(np.float64)
+    codes = OQ.unpack(words[:gp.total_words], gp.h_word_offset, part.bits, d)
+    deq = OQ.dequantize(codes, meta[:, 1], meta[:, 0], part.bits).astype(np.float64)
+    tol = 1e-6 + 1e-5 * np.abs(ref)
+    step = sc[:, None] * (1 + 2.0 ** -20)
+    assert np.all(np.abs(deq - ref) <= step + tol + np.spacing(np.abs(ref).astype(np.float32))), "dequantised codes"
+    q = part.bits != 32
+    rmin, rmax = ref.min(axis=1), ref.max(axis=1)
+    assert np.all(np.abs(zp[q] - rmin[q]) <= 1e-6 + 1e-5 * np.abs(rmin[q])), "zero-points"
+    levels = (2.0 ** part.bits[q].astype(np.float64)) - 1
+    range_tol = 2e-6 + 2e-5 * np.abs(ref[q]).max(axis=1)          # both ends within the tolerance
+    assert np.all(np.abs(sc[q] - (rmax[q] - rmin[q]) / levels) <= range_tol / levels + 3e-7 * sc[q]), "scales"
 
 
 def test_deterministic_repeats():
