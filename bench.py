@@ -78,6 +78,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="synthetic partition index (2 = 300k-node d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-async", action="store_true", help="skip timing the asynchronous (stale-halo) mode")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--fused-halo-bwd", action="store_true",
                     help="quantise the halo gradients inside the transposed gather (one call) instead of "
@@ -201,6 +202,26 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None}
 
+    # the asynchronous mode (halo messages one epoch stale, quantised on a second stream): the same
+    # partition and weights, epoch 0 synchronous, then asynchronous epochs
+    async_rec = None
+    if not args.no_async:
+        ast = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd,
+                         pipelined=True)
+        ast.step(epoch=0)
+        for w in range(args.warmup):
+            ast.step(epoch=1 + w, sync=False)
+        torch.cuda.synchronize()
+        a0 = time.perf_counter()
+        for s_ in range(args.steps):
+            ast.step(epoch=1 + args.warmup + s_, sync=False)
+        torch.cuda.synchronize()
+        a_ms = (time.perf_counter() - a0) * 1e3 / args.steps
+        async_rec = {"ms_per_step": round(a_ms, 4), "value": round(qa_bytes_step / (a_ms * 1e-3) / 1e9, 1),
+                     "vs_sync": round(ms_per_step / a_ms, 4)}
+        print(f"[bench] asynchronous epochs: {a_ms:.3f} ms/step", file=sys.stderr, flush=True)
+        del ast
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(part, bytes_by_stage)
@@ -221,6 +242,7 @@ def main():
         "message_bytes": {"main": int(4 * hw.sum()), "scales": 8 * n_h},
         "kernels": kernels,
         "roofline": roof,
+        "async_mode": async_rec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -144,12 +144,15 @@ class GpuPartition:
         B.aggregate_bwd(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out, self.n_in, 0,
                         dx_halo, workspace=self.agg_ws)
 
-    def aggregate_bwd_halo_quantize(self, grad_out, msg: Messages, epoch, stream_id, seed=QUANT_SEED):
+    def aggregate_bwd_halo_quantize(self, grad_out, msg: Messages, epoch, stream_id, seed=QUANT_SEED,
+                                    workspace=None):
         """a6 (halo range) + a7 fused: the halo columns' gradients, each quantised into msg as
-        quantize_send would code it, without storing the gradient rows."""
+        quantize_send would code it, without storing the gradient rows.  A call that may run
+        concurrently with another aggregation needs a workspace of its own."""
         B.aggregate_bwd_quantize(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out,
                                  self.n_in, self.d, self.bits, self.word_offset, self.classes, seed, epoch, stream_id,
-                                 self.n_in, msg.codes, msg.meta, workspace=self.agg_ws)
+                                 self.n_in, msg.codes, msg.meta,
+                                 workspace=self.agg_ws if workspace is None else workspace)
 
     def aggregate_bwd_inner(self, grad_out, dx_inner, beta):
         """a6 (inner range): gradients of the inner columns (beta = 1 adds to dx_inner)."""
@@ -164,12 +167,23 @@ class GpuPartition:
 
 
 class LayerStack:
-    """Buffers and call order of a stack of GCN or GraphSAGE-mean layers on one partition."""
+    """Buffers and call order of a stack of GCN or GraphSAGE-mean layers on one partition.
 
-    def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False):
+    pipelined=True adds the guide's asynchronous execution mode (section 10): the halo messages of
+    every layer and direction are double-buffered, and in an asynchronous epoch t the aggregations
+    read the messages of epoch t-1 while the messages of epoch t are quantised on a second stream
+    (so they overlap the compute stream's work) for use in epoch t+1.  Inner rows are always
+    current; halo rows are one epoch stale.  A synchronous epoch quantises and then aggregates its
+    own messages, as without pipelining.  Slot t % 2 holds epoch t's messages; both streams join at
+    the end of every epoch, so no buffer is overwritten while it is still to be read.
+    """
+
+    def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False,
+                 pipelined: bool = False):
         self.gp = gp
         self.seed = seed
         self.fused_halo_bwd = fused_halo_bwd
+        self.pipelined = pipelined
         dev = gp.device
         n_in, d = gp.n_in, gp.d
         self.L = len(weights)
@@ -198,43 +212,89 @@ class LayerStack:
             self.dX = [self.dA[l][:, :d] for l in range(self.L)]
         else:
             self.dX = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
-        self.dX_halo = None if fused_halo_bwd else torch.empty(gp.n_h, d, dtype=torch.float32, device=dev)
-        self.msg_f = [gp.new_messages() for _ in range(self.L)]
-        self.msg_b = [gp.new_messages() for _ in range(self.L)]
+        # halo gradient rows before quantisation: one buffer, or one per layer when the quantisation
+        # of layer l may still run on the second stream while layer l-1 gathers
+        n_halo_bufs = 0 if fused_halo_bwd else (self.L if pipelined else 1)
+        self.dX_halo = [torch.empty(gp.n_h, d, dtype=torch.float32, device=dev) for _ in range(n_halo_bufs)]
+        n_slots = 2 if pipelined else 1
+        self.msg_f = [[gp.new_messages() for _ in range(n_slots)] for _ in range(self.L)]
+        self.msg_b = [[gp.new_messages() for _ in range(n_slots)] for _ in range(self.L)]
+        self.msg_epoch = [None] * n_slots          # epoch whose messages each slot holds
+        self.comm = torch.cuda.Stream(device=dev) if pipelined else None
+        # split-row partials of the gather that runs on the second stream (the compute stream's
+        # gathers keep using the partition's workspace meanwhile)
+        self.comm_ws = torch.empty_like(gp.agg_ws) if (pipelined and fused_halo_bwd) else None
         self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), backward=(n_in, d, k_in))
 
-    def forward_layer(self, l, epoch, hook=None):
+    def _on_comm(self, fn):
+        """Runs fn on the second stream once the compute stream's work so far is done."""
+        ready = torch.cuda.Event()
+        ready.record(torch.cuda.current_stream())
+        self.comm.wait_event(ready)
+        with torch.cuda.stream(self.comm):
+            fn()
+
+    def forward_layer(self, l, epoch, hook=None, slot=0, sync=True):
         gp, d = self.gp, self.gp.d
         x = self.X[l]
-        gp.quantize_send(x, gp.mirror, self.msg_f[l], epoch, 2 * l, self.seed)
-        if hook: hook("quantize_fwd", l)
         agg_out = self.A[l][:, d:] if self.sage else self.A[l]
-        gp.aggregate_fwd(x, self.msg_f[l], agg_out)
+        msg = self.msg_f[l][slot]
+        if sync:
+            gp.quantize_send(x, gp.mirror, msg, epoch, 2 * l, self.seed)
+            if hook: hook("quantize_fwd", l)
+            gp.aggregate_fwd(x, msg, agg_out)
+        else:
+            self._on_comm(lambda: gp.quantize_send(x, gp.mirror, msg, epoch, 2 * l, self.seed))
+            gp.aggregate_fwd(x, self.msg_f[l][1 - slot], agg_out)
         if hook: hook("aggregate_fwd", l)
         B.dense_project(0, 1, self.A[l], self.W[l], 0, self.H[l], epilogue=B.EPI_RELU, workspace=self.dense_ws)
         if hook: hook("dense_fwd", l)
 
-    def backward_layer(self, l, epoch, hook=None):
+    def backward_layer(self, l, epoch, hook=None, slot=0, sync=True):
         gp, d = self.gp, self.gp.d
         dH = self.grad_top if l == self.L - 1 else self.dX[l + 1]
         B.dense_backward(dH, self.H[l], self.A[l], self.W[l], self.dA[l], self.dW[l], workspace=self.dense_ws)
         if hook: hook("dense_bwd", l)
         g = self.dA[l][:, d:] if self.sage else self.dA[l]
+        msg = self.msg_b[l][slot]
+        stream_id = 2 * l + 1
         if self.fused_halo_bwd:
-            gp.aggregate_bwd_halo_quantize(g, self.msg_b[l], epoch, 2 * l + 1, self.seed)
-            if hook: hook("aggregate_bwd_halo_quantize", l)
+            send = lambda: gp.aggregate_bwd_halo_quantize(g, msg, epoch, stream_id, self.seed,
+                                                          workspace=None if sync else self.comm_ws)
+            if sync:
+                send()
+                if hook: hook("aggregate_bwd_halo_quantize", l)
+            else:
+                self._on_comm(send)
         else:
-            gp.aggregate_bwd_halo(g, self.dX_halo)
+            buf = self.dX_halo[l if len(self.dX_halo) > 1 else 0]
+            gp.aggregate_bwd_halo(g, buf)
             if hook: hook("aggregate_bwd_halo", l)
-            gp.quantize_send(self.dX_halo, None, self.msg_b[l], epoch, 2 * l + 1, self.seed)
-            if hook: hook("quantize_bwd", l)
+            send = lambda: gp.quantize_send(buf, None, msg, epoch, stream_id, self.seed)
+            if sync:
+                send()
+                if hook: hook("quantize_bwd", l)
+            else:
+                self._on_comm(send)
         gp.aggregate_bwd_inner(g, self.dX[l], 1 if self.sage else 0)
         if hook: hook("aggregate_bwd_inner", l)
-        gp.add_received(self.msg_b[l], self.dX[l])
+        gp.add_received(msg if sync else self.msg_b[l][1 - slot], self.dX[l])
         if hook: hook("add_received", l)
 
-    def step(self, epoch=0, hook=None):
+    def step(self, epoch=0, hook=None, sync=True):
+        """One epoch: every layer forward, then backward.  sync=False (pipelined stacks only) runs the
+        asynchronous mode, which needs the messages of epoch - 1."""
+        slot = epoch % 2 if self.pipelined else 0
+        if not sync:
+            if not self.pipelined:
+                raise ValueError("the asynchronous mode needs a pipelined stack")
+            if self.msg_epoch[1 - slot] != epoch - 1:
+                raise ValueError(f"epoch {epoch} cannot run asynchronously: the messages of epoch {epoch - 1} "
+                                 "are not there (run it, synchronously or not, first)")
         for l in range(self.L):
-            self.forward_layer(l, epoch, hook)
+            self.forward_layer(l, epoch, hook, slot, sync)
         for l in reversed(range(self.L)):
-            self.backward_layer(l, epoch, hook)
+            self.backward_layer(l, epoch, hook, slot, sync)
+        if not sync:
+            torch.cuda.current_stream().wait_stream(self.comm)
+        self.msg_epoch[slot] = epoch
