@@ -25,10 +25,25 @@ QUANT_SEED = synth.QUANT_SEED
 
 
 @dataclasses.dataclass
+class Layout:
+    """How the halo rows of a packed message buffer are laid out: per-row widths and word offsets,
+    and the width classes when equal widths are contiguous (None: use the per-row arrays)."""
+    h_bits: np.ndarray             # uint8 [n_h] (host)
+    h_word_offset: np.ndarray      # uint32 [n_h + 1] (host)
+    total_words: int
+    bits: torch.Tensor             # the same two arrays on the device
+    word_offset: torch.Tensor
+    classes: object
+
+
+@dataclasses.dataclass
 class Messages:
-    """One packed message buffer: the codes and per-row (min, scale) pairs of the halo rows."""
+    """One packed message buffer: the codes and per-row (min, scale) pairs of the halo rows, and the
+    layout they were packed with (the receiver dequantises with the sender's widths, which matters
+    when an asynchronous epoch reads messages packed at the previous epoch's widths)."""
     codes: torch.Tensor        # int32 words (uint32 bit patterns)
     meta: torch.Tensor         # float32 [n_h, 2]: min (zero-point), scale
+    layout: Layout = None      # None: the partition's current layout
 
     @property
     def zero_point(self):
@@ -100,21 +115,38 @@ class GpuPartition:
         self.dense_ws = None
 
     def set_bits(self, bits, grouped: bool = True):
-        """Per-halo widths.  If the halo rows are numbered so that equal widths are contiguous the
-        packed buffers use the width-class layout (offsets by arithmetic); otherwise, or with
-        grouped=False, the per-row offset table."""
+        """Per-halo widths of the messages quantised from now on.  If the halo rows are numbered so
+        that equal widths are contiguous the packed buffers use the width-class layout (offsets by
+        arithmetic); otherwise, or with grouped=False, the per-row offset table."""
         bits = np.ascontiguousarray(bits, dtype=np.uint8)
-        self.h_bits = bits
         off, total = B.pack_layout(bits, self.d)
-        self.h_word_offset = off
-        self.total_words = total
-        self.bits = torch.from_numpy(bits).to(self.device)
-        self.word_offset = torch.from_numpy(off.view(np.int32)).to(self.device)
-        self.classes = B.pack_classes(bits, self.d) if grouped else None
+        self.layout = Layout(bits, off, total, torch.from_numpy(bits).to(self.device),
+                             torch.from_numpy(off.view(np.int32)).to(self.device),
+                             B.pack_classes(bits, self.d) if grouped else None)
 
-    def new_messages(self) -> Messages:
-        return Messages(torch.empty(max(self.total_words, 1), dtype=torch.int32, device=self.device),
+    # the current layout's arrays
+    h_bits = property(lambda self: self.layout.h_bits)
+    h_word_offset = property(lambda self: self.layout.h_word_offset)
+    total_words = property(lambda self: self.layout.total_words)
+    bits = property(lambda self: self.layout.bits)
+    word_offset = property(lambda self: self.layout.word_offset)
+    classes = property(lambda self: self.layout.classes)
+
+    def words_at(self, max_bits: int) -> int:
+        """Words of a buffer holding every halo row at max_bits (a bound for widths up to it)."""
+        w = self.d if max_bits == 32 else (self.d * max_bits + 31) // 32
+        return self.n_h * w
+
+    def new_messages(self, capacity_words: int = 0) -> Messages:
+        return Messages(torch.empty(max(self.total_words, capacity_words, 1), dtype=torch.int32, device=self.device),
                         torch.empty(self.n_h, 2, dtype=torch.float32, device=self.device))
+
+    def _stamp(self, msg: Messages):
+        lay = self.layout
+        if msg.codes.numel() < lay.total_words:
+            raise ValueError(f"message buffer of {msg.codes.numel()} words, the layout needs {lay.total_words}")
+        msg.layout = lay
+        return lay
 
     def dense_workspace(self, *shapes, backward=None):
         need = max(B.dense_project_workspace(*s) for s in shapes)
@@ -129,14 +161,17 @@ class GpuPartition:
     # -------------------------------------------------------------------------------------
 
     def quantize_send(self, x, row_index, msg: Messages, epoch, stream_id, seed=QUANT_SEED):
-        """a1 / a7: quantise the n_h outgoing boundary rows (x[row_index] or x itself)."""
-        B.quantize_pack(x, row_index, self.n_h, self.bits, self.word_offset, self.classes, seed, epoch, stream_id,
+        """a1 / a7: quantise the n_h outgoing boundary rows (x[row_index] or x itself) with the
+        current widths."""
+        lay = self._stamp(msg)
+        B.quantize_pack(x, row_index, self.n_h, lay.bits, lay.word_offset, lay.classes, seed, epoch, stream_id,
                         self.n_in, msg.codes, msg.meta)
 
     def aggregate_fwd(self, x_inner, msg: Messages, out):
         """a3: out = sum over N(v) and v of w_vu * x~_u, halo rows dequantised from msg."""
+        lay = msg.layout or self.layout
         B.dequant_aggregate_fwd(self.rowptr, self.colidx, self.w_fwd, self.plan_fwd, x_inner, self.n_in, msg.codes,
-                                self.word_offset, self.bits, self.classes, msg.meta, self.n_h, 0, out,
+                                lay.word_offset, lay.bits, lay.classes, msg.meta, self.n_h, 0, out,
                                 workspace=self.agg_ws)
 
     def aggregate_bwd_halo(self, grad_out, dx_halo):
@@ -149,8 +184,9 @@ class GpuPartition:
         """a6 (halo range) + a7 fused: the halo columns' gradients, each quantised into msg as
         quantize_send would code it, without storing the gradient rows.  A call that may run
         concurrently with another aggregation needs a workspace of its own."""
+        lay = self._stamp(msg)
         B.aggregate_bwd_quantize(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out,
-                                 self.n_in, self.d, self.bits, self.word_offset, self.classes, seed, epoch, stream_id,
+                                 self.n_in, self.d, lay.bits, lay.word_offset, lay.classes, seed, epoch, stream_id,
                                  self.n_in, msg.codes, msg.meta,
                                  workspace=self.agg_ws if workspace is None else workspace)
 
@@ -161,8 +197,9 @@ class GpuPartition:
 
     def add_received(self, msg: Messages, dx_inner):
         """a8: dx_inner[mirror[k]] += dequantised gradient message k."""
-        B.dequant_aggregate_fwd(self.m_ptr, self.m_idx, None, self.plan_mirror, None, 0, msg.codes, self.word_offset,
-                                self.bits, self.classes, msg.meta, self.n_h, 1, dx_inner, workspace=self.agg_ws,
+        lay = msg.layout or self.layout
+        B.dequant_aggregate_fwd(self.m_ptr, self.m_idx, None, self.plan_mirror, None, 0, msg.codes, lay.word_offset,
+                                lay.bits, lay.classes, msg.meta, self.n_h, 1, dx_inner, workspace=self.agg_ws,
                                 row_ids=self.m_rows)
 
 
@@ -179,7 +216,7 @@ class LayerStack:
     """
 
     def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False,
-                 pipelined: bool = False):
+                 pipelined: bool = False, max_bits: int = 0):
         self.gp = gp
         self.seed = seed
         self.fused_halo_bwd = fused_halo_bwd
@@ -217,8 +254,10 @@ class LayerStack:
         n_halo_bufs = 0 if fused_halo_bwd else (self.L if pipelined else 1)
         self.dX_halo = [torch.empty(gp.n_h, d, dtype=torch.float32, device=dev) for _ in range(n_halo_bufs)]
         n_slots = 2 if pipelined else 1
-        self.msg_f = [[gp.new_messages() for _ in range(n_slots)] for _ in range(self.L)]
-        self.msg_b = [[gp.new_messages() for _ in range(n_slots)] for _ in range(self.L)]
+        # message buffers sized for the current widths, or for any widths up to max_bits
+        cap = gp.words_at(max_bits) if max_bits else 0
+        self.msg_f = [[gp.new_messages(cap) for _ in range(n_slots)] for _ in range(self.L)]
+        self.msg_b = [[gp.new_messages(cap) for _ in range(n_slots)] for _ in range(self.L)]
         self.msg_epoch = [None] * n_slots          # epoch whose messages each slot holds
         self.comm = torch.cuda.Stream(device=dev) if pipelined else None
         # split-row partials of the gather that runs on the second stream (the compute stream's
@@ -298,3 +337,34 @@ class LayerStack:
         if not sync:
             torch.cuda.current_stream().wait_stream(self.comm)
         self.msg_epoch[slot] = epoch
+
+
+class AdaptiveEpochs:
+    """The online loop of the guide's section 11 on one GPU's share.  Each epoch runs with the node
+    widths the Quant Orchestrator derives from the mask levels and the Coordinator's base width, in
+    the execution mode the Coordinator chose; the epoch's partition losses and time then go to the
+    Coordinator, which sets the base width and mode of the next epoch.  The stack must be pipelined
+    (for asynchronous epochs) with message buffers for max_bits, and its halo nodes numbered by
+    descending level (qha_level_order) so that every epoch's buffer stays grouped by width."""
+
+    def __init__(self, stack: LayerStack, levels, coordinator, max_bits: int = 8):
+        self.stack = stack
+        self.levels = np.ascontiguousarray(levels, dtype=np.uint8)
+        self.coordinator = coordinator
+        self.max_bits = max_bits
+        self.base = coordinator.state.bits
+        self.sync = bool(coordinator.state.sync)
+        self.t = 0
+
+    def run_epoch(self):
+        """Runs epoch t; returns (t, base width, synchronous, node widths)."""
+        bits = B.node_bits(self.levels, self.base, self.max_bits)
+        self.stack.gp.set_bits(bits)
+        self.stack.step(epoch=self.t, sync=self.sync)
+        return self.t, self.base, self.sync, bits
+
+    def report(self, partition_losses, epoch_time: float):
+        """The losses and time of the epoch just run: sets the next epoch's base width and mode."""
+        self.base, self.sync = self.coordinator.step(partition_losses, epoch_time)
+        self.t += 1
+

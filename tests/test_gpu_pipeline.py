@@ -124,3 +124,43 @@ def test_epoch_tags_of_quantised_messages(fused):
     for a, b in zip(first, (st.H[0], st.dX[0], st.dW[0])):
         assert np.array_equal(a.view(np.uint32), H.host(b).view(np.uint32))
     torch.cuda.synchronize()
+
+
+def test_adaptive_epochs_follow_the_coordinator():
+    """The online loop (guide section 11): per epoch the Coordinator's base width and mode, the Quant
+    Orchestrator's node widths on a partition numbered by the Graph Extractor's levels, and an
+    asynchronous epoch that changes the widths still dequantises the previous epoch's messages with
+    the widths they were packed with.  Every epoch's first-layer aggregation is checked against the
+    oracle fed with the right epoch's inputs and widths."""
+    H.require_gpu()
+    from oracle import control as OC
+    from quantized_halo_aggregation_amd import binding as B
+    from quantized_halo_aggregation_amd.pipeline import AdaptiveEpochs, GpuPartition, LayerStack
+    from test_oracle_control import LITERAL, TRACE
+
+    part0 = synth.make_partition(synth.small_workload(1500, 700, 20000, 128, bits=("const", 4), index=94))
+    n_in, d = part0.n_in, part0.d
+    lv0 = OC.mask_levels(part0.deg[n_in:])
+    ptr, idx, deg, mirror, lv = synth.number_halos_by_width(n_in, part0.nbr_ptr, part0.nbr_idx, part0.deg,
+                                                            part0.mirror, lv0)
+    part = dataclasses.replace(part0, nbr_ptr=ptr, nbr_idx=idx, deg=deg, mirror=mirror,
+                               bits=OC.combine_and_clip(lv, 1))
+    gp = GpuPartition(part)
+    st = LayerStack(gp, part.weights, part.x, part.grad_top, pipelined=True, max_bits=8)
+    run = AdaptiveEpochs(st, B.mask_levels(deg[n_in:])[0], B.Coordinator(lam=0.0, delta=2))
+    xs = [np.random.default_rng(40 + t).standard_normal((n_in, d)).astype(np.float32) for t in range(len(TRACE))]
+    want = [(1, True)] + LITERAL[:-1]            # the mode of epoch t is the decision after epoch t - 1
+    used = {}
+    for t, loss in enumerate(TRACE):
+        H.note(f"adaptive epoch {t}: expect base {want[t][0]}, sync {want[t][1]}")
+        st.X[0].copy_(H.dev(xs[t]))
+        t_run, base, sync, bits = run.run_epoch()
+        assert (t_run, base, sync) == (t, *want[t])
+        assert np.array_equal(bits, OC.combine_and_clip(lv, base))
+        used[t] = base
+        src = t if sync else t - 1
+        ref = OL.send_halo(xs[src][mirror], OC.combine_and_clip(lv, used[src]), SEED, src, 0, n_in)
+        x_cols = np.concatenate([xs[t], ref["received"]])
+        H.assert_close(H.host(st.A[0]), OA.gcn_aggregate(ptr, idx, deg, x_cols),
+                       what=f"epoch {t} aggregate (halos of epoch {src} at base {used[src]})")
+        run.report([loss], 1.0)
