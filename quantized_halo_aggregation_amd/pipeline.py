@@ -3,9 +3,10 @@
 The per-layer data path of the SYLVIE guide (sections 5 and 11) on one GPU:
 
   forward   quantize_pack(send set) -> [exchange] -> dequant_aggregate_fwd -> dense_project(+ReLU)
-  backward  dense_backward(dA, dW; ReLU mask) -> aggregate_bwd_quantize(halo columns; or
-            aggregate_bwd then quantize_pack) -> [exchange] -> aggregate_bwd(inner columns)
-            -> dequant_aggregate_fwd(received, add)
+  backward  dense_backward(dA, dW; ReLU mask) -> aggregate_bwd(halo columns) then quantize_pack
+            (or both in aggregate_bwd_quantize) -> [exchange] -> one dequant_aggregate_fwd over the
+            inner columns' transposed rows plus the received messages of their halo copies (or
+            aggregate_bwd, then a dequant_aggregate_fwd over the mirror map that adds them)
 
 The exchange is the identity under the mirror model (halo k is the remote copy of inner node
 mirror[k]): the codes sent are the codes received.  Everything numeric runs in libqha's kernels;
@@ -104,13 +105,31 @@ class GpuPartition:
         B.edge_weights(self.rowptr, self.colidx, r_f, c_f, self.w_fwd)
         B.edge_weights(self.colptr, self.rowidx, r_b, c_b, self.w_bwd)
 
+        # the inner columns' transposed rows, each followed by the received halo messages of that
+        # node's copies (halo ids n_in + k, weight 1): one dequantising gather then forms an inner
+        # node's gradient and adds what its copies received (a6 inner range + a8)
+        t_cnt = np.diff(colptr[:n_in + 1]).astype(np.int64)
+        m_cnt = np.diff(m_ptr).astype(np.int64)
+        r_ptr = np.concatenate([[0], np.cumsum(t_cnt + m_cnt)]).astype(np.int64)
+        pos_t = np.repeat(r_ptr[:-1] - colptr[:n_in].astype(np.int64), t_cnt) + np.arange(int(colptr[n_in]))
+        pos_m = np.repeat(r_ptr[:-1] + t_cnt - m_ptr[:-1].astype(np.int64), m_cnt) + np.arange(int(m_ptr[-1]))
+        r_idx = np.empty(int(r_ptr[-1]), dtype=np.int32)
+        r_idx[pos_t] = rowidx[:colptr[n_in]]
+        r_idx[pos_m] = n_in + m_idx
+        self.h_r_ptr, self.h_r_idx = r_ptr.astype(np.int32), r_idx
+        self.r_ptr, self.r_idx = dev(self.h_r_ptr), dev(r_idx)
+        self.w_recv = torch.ones(max(r_idx.size, 1), dtype=torch.float32, device=device)
+        if pos_t.size:
+            self.w_recv[torch.from_numpy(pos_t).to(device)] = self.w_bwd[:pos_t.size]
+
         mk = lambda rp: B.AggPlan(rp, chunk, group_edges, device=device)
         self.plan_fwd = mk(ptr)
         self.plan_bwd_halo = mk(colptr[n_in:])
         self.plan_bwd_inner = mk(colptr[:n_in + 1])
         self.plan_mirror = mk(mc_ptr)
+        self.plan_recv = mk(self.h_r_ptr)
         ws = max(p.workspace_bytes(d) for p in (self.plan_fwd, self.plan_bwd_halo, self.plan_bwd_inner,
-                                                 self.plan_mirror))
+                                                 self.plan_mirror, self.plan_recv))
         self.agg_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
         self.dense_ws = None
 
@@ -195,6 +214,14 @@ class GpuPartition:
         B.aggregate_bwd(self.colptr[:self.n_in + 1], self.rowidx, self.w_bwd, self.plan_bwd_inner, grad_out,
                         self.n_in, beta, dx_inner, workspace=self.agg_ws)
 
+    def aggregate_bwd_inner_received(self, grad_out, msg: Messages, dx_inner, beta):
+        """a6 (inner range) + a8 in one gather: dx_inner (+)= the inner columns' transposed sums plus
+        the dequantised gradient messages received for each inner node's halo copies."""
+        lay = msg.layout or self.layout
+        B.dequant_aggregate_fwd(self.r_ptr, self.r_idx, self.w_recv, self.plan_recv, grad_out, self.n_in, msg.codes,
+                                lay.word_offset, lay.bits, lay.classes, msg.meta, self.n_h, beta, dx_inner,
+                                workspace=self.agg_ws)
+
     def add_received(self, msg: Messages, dx_inner):
         """a8: dx_inner[mirror[k]] += dequantised gradient message k."""
         lay = msg.layout or self.layout
@@ -216,10 +243,11 @@ class LayerStack:
     """
 
     def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False,
-                 pipelined: bool = False, max_bits: int = 0):
+                 pipelined: bool = False, max_bits: int = 0, fold_received: bool = False):
         self.gp = gp
         self.seed = seed
         self.fused_halo_bwd = fused_halo_bwd
+        self.fold_received = fold_received
         self.pipelined = pipelined
         dev = gp.device
         n_in, d = gp.n_in, gp.d
@@ -315,10 +343,16 @@ class LayerStack:
                 if hook: hook("quantize_bwd", l)
             else:
                 self._on_comm(send)
-        gp.aggregate_bwd_inner(g, self.dX[l], 1 if self.sage else 0)
-        if hook: hook("aggregate_bwd_inner", l)
-        gp.add_received(msg if sync else self.msg_b[l][1 - slot], self.dX[l])
-        if hook: hook("add_received", l)
+        received = msg if sync else self.msg_b[l][1 - slot]
+        beta = 1 if self.sage else 0
+        if self.fold_received:
+            gp.aggregate_bwd_inner_received(g, received, self.dX[l], beta)
+            if hook: hook("aggregate_bwd_inner_received", l)
+        else:
+            gp.aggregate_bwd_inner(g, self.dX[l], beta)
+            if hook: hook("aggregate_bwd_inner", l)
+            gp.add_received(received, self.dX[l])
+            if hook: hook("add_received", l)
 
     def step(self, epoch=0, hook=None, sync=True):
         """One epoch: every layer forward, then backward.  sync=False (pipelined stacks only) runs the

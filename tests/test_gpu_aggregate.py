@@ -103,6 +103,19 @@ def test_backward_aggregation_and_received_add(case):
     untouched = np.setdiff1d(np.arange(n_in), part.mirror)
     H.assert_bits_equal(got[untouched], start[untouched], "rows without a halo copy")
 
+    # the folded call: the inner columns' gradients and the received messages in one gather
+    # (beta = 1 adds both to what the rows hold)
+    H.note(f"aggregate_bwd_inner_received {_case_id(case)}")
+    omsg = H.upload_messages(gp, msg)
+    folded = H.dev(base)
+    gp.aggregate_bwd_inner_received(g_dev, omsg, folded, 1)
+    H.assert_close(H.host(folded), OA.add_received(ref[:n_in] + base.astype(np.float64), part.mirror,
+                                                   msg["received"]), what="folded inner + received (beta=1)")
+    folded0 = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_inner_received(g_dev, omsg, folded0, 0)
+    H.assert_close(H.host(folded0), OA.add_received(ref[:n_in], part.mirror, msg["received"]),
+                   what="folded inner + received (beta=0)")
+
 
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
 @pytest.mark.parametrize("grouped", [True, False], ids=["width-classes", "offset-table"])

@@ -151,3 +151,12 @@ def test_full_size_layer_calls(wl_index):
     gp.add_received(omsg_b, dxr)
     ref_r = OA.add_received(dxi0, part.mirror, ref_b["received"])
     H.assert_close(H.host(dxr)[rows], ref_r[rows], what="received add (sampled rows)")
+    del dxr
+
+    # ---- a6 (inner range) + a8 folded into one gather, as the bench runs them ----------------
+    H.note(f"full size {wl.name}: inner gradients + received, one gather")
+    dxf = H.dev(dxi0) if beta else torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_inner_received(H.dev(g), omsg_b, dxf, beta)
+    recv = OA.add_received(np.zeros((n_in, d), np.float32), part.mirror, ref_b["received"])
+    ref_f = np.asarray(mat_c[:, cols_in].T @ g.astype(np.float64)) + recv[cols_in] + (dxi0[cols_in] if beta else 0)
+    H.assert_close(H.host(dxf)[cols_in], ref_f, what="inner gradients + received (sampled columns)")
