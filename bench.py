@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="synthetic partition index (2 = 300k-node d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-async", action="store_true", help="skip timing the asynchronous (stale-halo) mode")
+    ap.add_argument("--sweep-bits", action="store_true",
+                    help="instead of the step line: one line with the step, quantise and aggregate times and "
+                         "message bytes for every halo width in {1, 2, 4, 8, 32} on the chosen partition")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--fused-halo-bwd", action="store_true",
                     help="quantise the halo gradients inside the transposed gather (one call) instead of "
@@ -112,6 +115,9 @@ def main():
     print("[bench] device set-up done", file=sys.stderr, flush=True)
 
     n_in, n_h, d = part.n_in, part.n_h, part.d
+    if args.sweep_bits:
+        sweep_bits(args, wl, part, gp)
+        return
     hw = row_words(d, part.bits)
     nw = gp.h_colptr
     # algorithmic bytes per call of one layer
@@ -246,6 +252,57 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def sweep_bits(args, wl, part, gp):
+    """The step at every uniform halo width (the guide's fixed-width ablation, section 14, and its
+    Table XII split of message bytes into main data and scales), one JSON line."""
+    import torch
+    from quantized_halo_aggregation_amd.pipeline import LayerStack
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    stream = torch.cuda.current_stream()
+    out = []
+    for b in (1, 2, 4, 8, 32):
+        bits = np.full(n_h, b, dtype=np.uint8)
+        gp.set_bits(bits)
+        st = LayerStack(gp, part.weights, part.x, part.grad_top)
+        hw = row_words(d, bits)
+        q_bytes = quantize_bytes(n_h, d, bits, gathered=True)
+        a_bytes = gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0)
+        per = {}
+        recs = []
+
+        def hook(name, layer):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            recs[-1].append((name, ev))
+
+        for w in range(args.warmup):
+            st.step(epoch=w)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            first = torch.cuda.Event(enable_timing=True)
+            first.record(stream)
+            recs.append([("", first)])
+            st.step(epoch=args.warmup + s_, hook=hook)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        for r in recs:
+            for (_, a), (name, e) in zip(r[:-1], r[1:]):
+                per.setdefault(name, []).append(a.elapsed_time(e))
+        qa = {k: float(np.mean(v)) for k, v in per.items() if k in ("quantize_fwd", "aggregate_fwd")}
+        out.append({"bits": b, "ms_per_step": round(ms, 4),
+                    "quantize_fwd_us": round(qa["quantize_fwd"] * 1e3, 1),
+                    "aggregate_fwd_us": round(qa["aggregate_fwd"] * 1e3, 1),
+                    "quant_aggregate_gbs": round((q_bytes + a_bytes) / ((qa["quantize_fwd"] + qa["aggregate_fwd"]) * 1e-3)
+                                                 / 1e9, 1),
+                    "message_main_MB": round(4 * hw.sum() / 1e6, 2),
+                    "message_scales_MB": round((8 * n_h if b != 32 else 0) / 1e6, 2)})
+        print(f"[bench] {b}-bit halos: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+        del st
+    print(json.dumps({"metric": "per-width sweep", "workload": wl.name, "n_inner": n_in, "n_halo": n_h, "d": d,
+                      "layers": wl.layers, "steps": args.steps, "warmup": args.warmup, "widths": out}))
 
 
 # ------------------------------------------------------------------------------------------------
