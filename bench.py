@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="synthetic partition index (2 = 300k-node d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-async", action="store_true", help="skip timing the asynchronous (stale-halo) mode")
+    ap.add_argument("--split-interior", action="store_true",
+                    help="aggregate the interior rows (no halo neighbour) on a second stream while the send set "
+                         "is quantised, then the boundary rows")
     ap.add_argument("--sweep-bits", action="store_true",
                     help="instead of the step line: one line with the step, quantise and aggregate times and "
                          "message bytes for every halo width in {1, 2, 4, 8, 32} on the chosen partition")
@@ -110,7 +113,8 @@ def main():
     gen_s = time.time() - t0
     print(f"[bench] generated {wl.describe()} in {gen_s:.1f}s", file=sys.stderr, flush=True)
     gp = GpuPartition(part, chunk=args.chunk or B.DEFAULT_CHUNK)
-    st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd)
+    st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd,
+                    split_interior=args.split_interior)
     torch.cuda.synchronize()
     print("[bench] device set-up done", file=sys.stderr, flush=True)
 

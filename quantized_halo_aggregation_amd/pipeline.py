@@ -122,6 +122,8 @@ class GpuPartition:
         if pos_t.size:
             self.w_recv[torch.from_numpy(pos_t).to(device)] = self.w_bwd[:pos_t.size]
 
+        self.chunk, self.group_edges = chunk, group_edges
+        self.int_rows = None
         mk = lambda rp: B.AggPlan(rp, chunk, group_edges, device=device)
         self.plan_fwd = mk(ptr)
         self.plan_bwd_halo = mk(colptr[n_in:])
@@ -132,6 +134,38 @@ class GpuPartition:
                                                  self.plan_mirror, self.plan_recv))
         self.agg_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
         self.dense_ws = None
+
+    def split_interior(self):
+        """Builds the interior / boundary split of the forward CSR (guide section 10: inner work runs
+        while the boundary messages are produced): interior rows have no halo neighbour, so their
+        aggregation needs no message.  Each part is a sub-CSR whose rows write out[row_ids]; their
+        edge weights come from the same weight kernel, so every row's sum is the unsplit one."""
+        if getattr(self, "int_rows", None) is not None:
+            return
+        ptr, idx, n_in = self.h_ptr, self.h_idx, self.n_in
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+        cs = np.concatenate([[0], np.cumsum(idx >= n_in)])
+        interior = (cs[ptr[1:]] - cs[ptr[:-1]]) == 0
+        self.n_interior = int(interior.sum())
+
+        def sub(rows):
+            lens = np.diff(ptr)[rows].astype(np.int64)
+            sptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            take = np.repeat(ptr[rows].astype(np.int64) - sptr[:-1], lens) + np.arange(int(sptr[-1]))
+            sidx = idx[take]
+            rows_d, sptr_d, sidx_d = dev(rows.astype(np.int32)), dev(sptr), dev(sidx)
+            r = self.norm[rows_d.long()] if self.model == "gcn" else self.mean_r[rows_d.long()]
+            c = self.norm if self.model == "gcn" else None
+            w = torch.empty(max(sidx.size, 1), dtype=torch.float32, device=self.device)
+            B.edge_weights(sptr_d, sidx_d, r.contiguous(), c, w)
+            return rows_d, sptr_d, sidx_d, w, B.AggPlan(sptr, self.chunk, self.group_edges, device=self.device)
+
+        self.int_rows, self.int_ptr, self.int_idx, self.int_w, self.plan_int = sub(np.flatnonzero(interior))
+        self.bnd_rows, self.bnd_ptr, self.bnd_idx, self.bnd_w, self.plan_bnd = sub(np.flatnonzero(~interior))
+        ws = max(self.plan_int.workspace_bytes(self.d), self.plan_bnd.workspace_bytes(self.d))
+        self.int_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=self.device)
+        if ws > self.agg_ws.numel() * 4:
+            self.agg_ws = torch.empty(ws // 4, dtype=torch.float32, device=self.device)
 
     def set_bits(self, bits, grouped: bool = True):
         """Per-halo widths of the messages quantised from now on.  If the halo rows are numbered so
@@ -193,6 +227,19 @@ class GpuPartition:
                                 lay.word_offset, lay.bits, lay.classes, msg.meta, self.n_h, 0, out,
                                 workspace=self.agg_ws)
 
+    def aggregate_fwd_interior(self, x_inner, out):
+        """a3 on the interior rows only (no message needed; split_interior() first)."""
+        if self.n_interior:
+            B.dequant_aggregate_fwd(self.int_ptr, self.int_idx, self.int_w, self.plan_int, x_inner, self.n_in, None,
+                                    None, None, None, None, 0, 0, out, workspace=self.int_ws, row_ids=self.int_rows)
+
+    def aggregate_fwd_boundary(self, x_inner, msg: Messages, out):
+        """a3 on the boundary rows only, halo rows dequantised from msg."""
+        lay = msg.layout or self.layout
+        B.dequant_aggregate_fwd(self.bnd_ptr, self.bnd_idx, self.bnd_w, self.plan_bnd, x_inner, self.n_in, msg.codes,
+                                lay.word_offset, lay.bits, lay.classes, msg.meta, self.n_h, 0, out,
+                                workspace=self.agg_ws, row_ids=self.bnd_rows)
+
     def aggregate_bwd_halo(self, grad_out, dx_halo):
         """a6 (halo range): gradients of the halo columns."""
         B.aggregate_bwd(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out, self.n_in, 0,
@@ -243,11 +290,15 @@ class LayerStack:
     """
 
     def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False,
-                 pipelined: bool = False, max_bits: int = 0, fold_received: bool = False):
+                 pipelined: bool = False, max_bits: int = 0, fold_received: bool = False,
+                 split_interior: bool = False):
         self.gp = gp
         self.seed = seed
         self.fused_halo_bwd = fused_halo_bwd
         self.fold_received = fold_received
+        self.split_interior = split_interior
+        if split_interior:
+            gp.split_interior()
         self.pipelined = pipelined
         dev = gp.device
         n_in, d = gp.n_in, gp.d
@@ -287,7 +338,7 @@ class LayerStack:
         self.msg_f = [[gp.new_messages(cap) for _ in range(n_slots)] for _ in range(self.L)]
         self.msg_b = [[gp.new_messages(cap) for _ in range(n_slots)] for _ in range(self.L)]
         self.msg_epoch = [None] * n_slots          # epoch whose messages each slot holds
-        self.comm = torch.cuda.Stream(device=dev) if pipelined else None
+        self.comm = torch.cuda.Stream(device=dev) if (pipelined or split_interior) else None
         # split-row partials of the gather that runs on the second stream (the compute stream's
         # gathers keep using the partition's workspace meanwhile)
         self.comm_ws = torch.empty_like(gp.agg_ws) if (pipelined and fused_halo_bwd) else None
@@ -306,7 +357,14 @@ class LayerStack:
         x = self.X[l]
         agg_out = self.A[l][:, d:] if self.sage else self.A[l]
         msg = self.msg_f[l][slot]
-        if sync:
+        if sync and self.split_interior:
+            # interior rows on the second stream while the messages are quantised, then the rest
+            self._on_comm(lambda: gp.aggregate_fwd_interior(x, agg_out))
+            gp.quantize_send(x, gp.mirror, msg, epoch, 2 * l, self.seed)
+            if hook: hook("quantize_fwd", l)
+            gp.aggregate_fwd_boundary(x, msg, agg_out)
+            torch.cuda.current_stream().wait_stream(self.comm)
+        elif sync:
             gp.quantize_send(x, gp.mirror, msg, epoch, 2 * l, self.seed)
             if hook: hook("quantize_fwd", l)
             gp.aggregate_fwd(x, msg, agg_out)

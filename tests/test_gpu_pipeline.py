@@ -164,3 +164,28 @@ def test_adaptive_epochs_follow_the_coordinator():
         H.assert_close(H.host(st.A[0]), OA.gcn_aggregate(ptr, idx, deg, x_cols),
                        what=f"epoch {t} aggregate (halos of epoch {src} at base {used[src]})")
         run.report([loss], 1.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_interior_split_gives_the_unsplit_result(d):
+    """The interior / boundary split (interior rows aggregated on the second stream while the messages
+    are quantised) changes no row's arithmetic: every output of a synchronous step equals the unsplit
+    step's bit for bit, and the interior rows really have no halo neighbour."""
+    H.require_gpu()
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
+    part = synth.make_partition(synth.small_workload(4000, 150, 24000, d, bits=("top", 4, 8, 0.1), index=91))
+    n_in = part.n_in
+    outs = []
+    for split in (False, True):
+        gp = GpuPartition(part, chunk=64)
+        st = LayerStack(gp, part.weights, part.x, part.grad_top, split_interior=split)
+        H.note(f"interior split={split} d={d}")
+        st.step(epoch=2)
+        outs.append([H.host(t).copy() for t in (st.A[0], st.H[0], st.dX[0], st.dW[0])])
+        if split:
+            rows = H.host(gp.int_rows).astype(np.int64)
+            assert gp.n_interior == rows.size and 0.2 * n_in < rows.size < n_in
+            for r in rows[:200]:
+                assert np.all(part.nbr_idx[part.nbr_ptr[r]:part.nbr_ptr[r + 1]] < n_in)
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
