@@ -25,6 +25,9 @@
 // rate of unpacked float32 ones, so in this memory-bound loop the wider sum is free) and rounded
 // to float32 once.  Chunks of a heavy row write float64 partial sums that a second kernel adds in
 // chunk order, so results do not depend on scheduling.
+// Gathers whose every column is a plain float row (the transposed passes, and forward calls
+// without halo columns) run a leaner kernel: column indices and weights come by scalar loads, and
+// rows by range-checked buffer loads at 32-bit offsets, whenever x spans less than 4 GiB.
 #include "../../include/qha.h"
 #include "qha_internal.hpp"
 #include "quant_common.hpp"
@@ -50,6 +53,13 @@ constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
 #ifndef QHA_HALO_BATCH
 #define QHA_HALO_BATCH 8    // edges per batch when halo rows are dequantised too
 #endif
+#ifndef QHA_ROWS_KERNEL
+#define QHA_ROWS_KERNEL 1
+#endif
+#ifndef QHA_ROWS_BATCH
+#define QHA_ROWS_BATCH 16   // edges per batch of the plain-row gather at d <= 128 (8 KB in flight)
+#endif
+constexpr int rows_batch_of(int D) { return D >= 512 ? QHA_ROWS_BATCH / 4 : (D >= 256 ? QHA_ROWS_BATCH / 2 : QHA_ROWS_BATCH); }
 constexpr int batch_of(int D, bool halo) { return D >= 512 ? 8 : (halo ? QHA_HALO_BATCH : QHA_BATCH); }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 
@@ -58,8 +68,12 @@ __device__ __forceinline__ float rdlanef(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// scale * q + min with two roundings.  Written with plain operators under this file's contract(off):
+// the header forms of __fmul_rn / __fadd_rn are plain operators compiled with contraction allowed,
+// and once inlined their product and sum may be fused into one FMA.
 __device__ __forceinline__ float dequant(float sc, uint32_t q, float zp) {
-  return __fadd_rn(__fmul_rn(sc, static_cast<float>(q)), zp);
+  const float t = sc * static_cast<float>(q);
+  return t + zp;
 }
 
 template <int VEC>
@@ -474,6 +488,146 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
 }
 
+// VEC floats of one row by a range-checked buffer load (a lane past the buffer's end reads 0).
+template <int VEC>
+__device__ __forceinline__ void buffer_row(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&xv)[VEC]) {
+  const int o = static_cast<int>(off);
+  if constexpr (VEC == 1) {
+    xv[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+  } else if constexpr (VEC == 2) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+    xv[0] = __uint_as_float(t[0]);
+    xv[1] = __uint_as_float(t[1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, o + 16 * q, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[4 * q + c] = __uint_as_float(t[c]);
+    }
+  }
+}
+
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit buffer, range-checked against num_records
+
+// Gather of plain float rows (every column is a row of x: the transposed gathers, and forward
+// gathers without halo columns).  A batch's B column indices and edge weights are read by scalar
+// loads straight into scalar registers, so no lane-to-scalar moves are needed and the wait for them
+// does not include the wavefront's earlier row stores; each row load is a buffer load whose offset
+// (column * row pitch + the lane's features) is 32-bit and range-checked by the hardware.
+template <int D, bool BETA>
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
+  constexpr int VEC = vec_of(D);
+  constexpr int G = D / VEC;
+  constexpr int B = rows_batch_of(D);
+  const int lane = threadIdx.x & 63;
+  const int j0 = (G == 64 ? lane : (lane < G ? lane : 0)) * VEC;
+  const bool owner = (G == 64) || lane < G;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (item >= a.n_items) return;
+
+  int32_t row0, nrows, e0, e1;
+  if (a.items != nullptr) {
+    cptr<int32_t> it = cst(a.items) + 4 * item;
+    row0 = it[0];
+    nrows = it[1];
+    e0 = it[2];
+    e1 = it[3];
+  } else {
+    row0 = static_cast<int32_t>(item);
+    nrows = 1;
+    e0 = cst(a.rowptr)[item];
+    e1 = cst(a.rowptr)[item + 1];
+  }
+  const bool split = item < a.n_split_items;
+  const int li = lane < nrows ? lane : nrows - 1;
+  const int32_t v_end = split ? 0x7FFFFFFF : a.rowptr[row0 + li + 1];
+  const int32_t v_out = (a.row_ids != nullptr) ? a.row_ids[row0 + li] : row0 + li;
+
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.x), static_cast<short>(0), static_cast<int>(a.x_bytes),
+                                        static_cast<int>(kBufferWord3));
+  const uint32_t pitch = static_cast<uint32_t>(a.ldx) * 4u;
+  const uint32_t lane_off = static_cast<uint32_t>(j0) * 4u;
+  cptr<int32_t> ci = cst(a.colidx);
+  cptr<float> cw = cst(a.w);
+  const bool weighted = a.w != nullptr;
+
+  double acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+  int cur = 0;
+  int32_t cur_end = rdlane(v_end, 0);
+  auto flush = [&]() {
+    const int64_t orow = rdlane(v_out, cur);
+    if (owner) {
+      float* dst = a.out + orow * a.ldo + j0;
+      float res[VEC];
+      if constexpr (BETA) {
+        float old[VEC];
+        load_row<VEC>(dst, old);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+      }
+      store_row<VEC>(dst, res);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+    ++cur;
+    cur_end = rdlane(v_end, cur < nrows ? cur : nrows - 1);
+  };
+
+  for (int32_t e = e0; e < e1; e += B) {
+    int32_t u[B];
+    float ww[B];
+    if (e + B <= e1) {
+#pragma unroll
+      for (int i = 0; i < B; ++i) u[i] = ci[e + i];
+      if (weighted) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) ww[i] = cw[e + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < B; ++i) ww[i] = 1.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int32_t ei = min(e + i, e1 - 1);
+        u[i] = ci[ei];
+        ww[i] = weighted ? cw[ei] : 1.0f;
+      }
+    }
+    float xv[B][VEC];
+#pragma unroll
+    for (int i = 0; i < B; ++i) buffer_row<VEC>(xr, static_cast<uint32_t>(u[i]) * pitch + lane_off, xv[i]);
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int32_t p = e + i;
+      if (p < e1) {
+        const double wt = static_cast<double>(ww[i]);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
+        if (p + 1 == cur_end) flush();
+      }
+    }
+  }
+
+  if (split) {
+    double* p = a.partial + item * D + j0;
+    if (owner) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) p[v] = acc[v];
+    }
+  } else if (e0 == e1) {
+    flush();
+  }
+}
+
 // Adds the partial sums of every split row in chunk order and writes (or quantises) the row.
 template <int D, bool QUANT>
 __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
@@ -532,6 +686,10 @@ void launch_variant(const GatherArgs& a, dim3 grid, hipStream_t s) {
 
 template <int D>
 hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_out, hipStream_t s) {
+  // the plain-row kernel addresses x with 32-bit byte offsets
+  const int64_t x_bytes = a.n_inner > 0 ? ((a.n_inner - 1) * a.ldx + D) * 4 : 0;
+  const bool rows_ok = x_bytes <= static_cast<int64_t>(0xFFFFFFFFu) && QHA_ROWS_KERNEL;
+
   if (a.n_items > 0) {
     const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
     if (quantize_out) {
@@ -539,6 +697,11 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_ou
     } else if (with_halo) {
       if (a.beta) launch_variant<D, true, true>(a, grid, s);
       else launch_variant<D, true, false>(a, grid, s);
+    } else if (rows_ok) {
+      GatherArgs r = a;
+      r.x_bytes = static_cast<uint32_t>(x_bytes);
+      if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true>), grid, dim3(256), 0, s, r);
+      else hipLaunchKernelGGL((gather_rows_kernel<D, false>), grid, dim3(256), 0, s, r);
     } else {
       if (a.beta) launch_variant<D, false, true>(a, grid, s);
       else launch_variant<D, false, false>(a, grid, s);

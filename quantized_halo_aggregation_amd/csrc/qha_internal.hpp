@@ -66,7 +66,9 @@ struct GatherArgs {
   const float* x;
   int64_t ldx;
   int64_t n_inner;
+  uint32_t x_bytes;           // readable bytes of x (set by the launcher for range-checked loads)
   const uint32_t* codes;
+  uint32_t codes_bytes;       // bound on the readable bytes of codes (set by the launcher)
   const uint32_t* word_offset;
   const uint8_t* bits;
   Classes cls;

@@ -229,3 +229,69 @@ def test_plain_rows_and_degenerate_inputs():
     ref2 = np.zeros((25, d))
     np.add.at(ref2, rows[keep], x[idx[keep]].astype(np.float64))
     H.assert_close(H.host(out2), ref2, what="inner-only rows, unit weights")
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("grouped", [True, False], ids=["width-classes", "offset-table"])
+@pytest.mark.parametrize("beta", [0, 1])
+def test_dequantised_halo_rows_are_exact(d, grouped, beta):
+    """A row whose one neighbour is a halo node, at unit weight, is that node's received row: the
+    message format's scale * q + min with both roundings in float32 (not one fused multiply-add),
+    raw floats at b = 32, bit for bit (beta = 1 adds it to zeros)."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(31 + d)
+    n_h, n_inner = 300, 7
+    bits = rng.choice(np.array([1, 2, 4, 8, 32], np.uint8), size=n_h)
+    if grouped:
+        bits = np.sort(bits)[::-1].copy()
+    hx = (rng.standard_normal((n_h, d)) * rng.uniform(0.01, 100.0, size=(n_h, 1))).astype(np.float32)
+    msg = H.oracle_messages(hx, bits, 77, 3, 1, n_inner)
+    off, _ = B.pack_layout(bits, d)
+    classes = B.pack_classes(bits, d) if grouped else None
+    assert (classes is not None) == grouped
+    ptr = np.arange(n_h + 1, dtype=np.int32)
+    idx = (n_inner + rng.permutation(n_h)).astype(np.int32)
+    x = rng.standard_normal((n_inner, d)).astype(np.float32)
+    meta = np.stack([msg["zero_point"], msg["scale"]], 1).astype(np.float32)
+    words = msg["words"] if msg["words"].size else np.zeros(1, np.uint32)
+    H.note(f"exact dequantisation d={d} grouped={grouped} beta={beta}")
+    out = torch.zeros((n_h, d), dtype=torch.float32, device="cuda") if beta else \
+        torch.full((n_h, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dequant_aggregate_fwd(H.dev(ptr), H.dev(idx), None, B.AggPlan(ptr), H.dev(x), n_inner,
+                            H.dev(words.view(np.int32)), H.dev(off.view(np.int32)), H.dev(bits), classes, H.dev(meta),
+                            n_h, beta, out)
+    H.assert_bits_equal(H.host(out), msg["received"][idx - n_inner], "dequantised rows")
+
+
+def test_plain_gather_beyond_32bit_offsets():
+    """Rows of x more than 4 GiB apart (a row pitch of 2^24 floats): the gather takes its 64-bit
+    addressing path and still sums the right rows."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    d, n_x, pitch = 128, 65, 1 << 24
+    rng = np.random.default_rng(12)
+    big = torch.empty(n_x * pitch, dtype=torch.float32, device="cuda")
+    xv = rng.standard_normal((n_x, d)).astype(np.float32)
+    xs = big.view(n_x, pitch)[:, :d]
+    xs.copy_(H.dev(xv))
+    lens = rng.integers(1, 12, size=40)
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    idx = rng.integers(0, n_x, size=int(ptr[-1])).astype(np.int32)
+    idx[:3] = n_x - 1                                      # the last row, past 4 GiB
+    w = rng.random(idx.size).astype(np.float32)
+    rows = np.repeat(np.arange(40), lens)
+    ref = np.zeros((40, d))
+    np.add.at(ref, rows, w.astype(np.float64)[:, None] * xv[idx].astype(np.float64))
+    H.note("plain gather, 64-bit offsets")
+    out = torch.full((40, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dequant_aggregate_fwd(H.dev(ptr), H.dev(idx), H.dev(w), B.AggPlan(ptr), xs, n_x, None, None, None, None, None,
+                            0, 0, out)
+    H.assert_close(H.host(out), ref, what="gather over a 4.3 GB row pitch")
+    ga = torch.full((40, d), np.nan, dtype=torch.float32, device="cuda")
+    B.aggregate_bwd(H.dev(ptr), H.dev(idx), H.dev(w), B.AggPlan(ptr), xs, n_x, 0, ga)
+    H.assert_close(H.host(ga), ref, what="transposed-call form, same rows")
+    del big
+    torch.cuda.empty_cache()
