@@ -117,6 +117,15 @@ def main():
                     split_interior=args.split_interior)
     torch.cuda.synchronize()
     print("[bench] device set-up done", file=sys.stderr, flush=True)
+    # the forward halo gather addresses the inner rows, codes and (min, scale) pairs from one base
+    # when they lie within 4 GiB of each other
+    m0 = st.msg_f[0][0]
+    spans = [(st.X[0].data_ptr(), st.X[0].data_ptr() + st.X[0].stride(0) * st.X[0].shape[0] * 4),
+             (m0.codes.data_ptr(), m0.codes.data_ptr() + m0.codes.numel() * 4),
+             (m0.meta.data_ptr(), m0.meta.data_ptr() + m0.meta.numel() * 4)]
+    span = max(h for _, h in spans) - min(l for l, _ in spans)
+    print(f"[bench] forward gather buffers span {span / 2**20:.0f} MiB "
+          f"({'one base' if span < 2**32 else 'separate bases'})", file=sys.stderr, flush=True)
 
     n_in, n_h, d = part.n_in, part.n_h, part.d
     if args.sweep_bits:

@@ -209,7 +209,10 @@ int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int
  * aligned) must hold qha_agg_workspace_bytes(plan, d) bytes.  beta is 0 or 1.  Each product
  * w[e] * x~_u (exact in float64) is summed in float64 in edge order (chunks of a split row
  * separately, then in chunk order), added to the old value when beta = 1 and rounded to float32
- * once; results are deterministic.  Errors: INVALID_ARG, UNSUPPORTED (d), WORKSPACE, HIP. */
+ * once; results are deterministic.  With `classes` alone (bits and word_offset NULL), x_inner's
+ * rows and the packed codes must each span less than 4 GiB; otherwise the call fails with HIP
+ * (invalid value) and the per-row arrays are needed.  Errors: INVALID_ARG, UNSUPPORTED (d),
+ * WORKSPACE, HIP. */
 int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
                               const float* w, const int32_t* row_ids, const qha_agg_plan* plan,
                               const float* x_inner, int64_t ldx, int64_t n_inner,

@@ -25,12 +25,18 @@
 // rate of unpacked float32 ones, so in this memory-bound loop the wider sum is free) and rounded
 // to float32 once.  Chunks of a heavy row write float64 partial sums that a second kernel adds in
 // chunk order, so results do not depend on scheduling.
-// Gathers whose every column is a plain float row (the transposed passes, and forward calls
-// without halo columns) run a leaner kernel: column indices and weights come by scalar loads, and
-// rows by range-checked buffer loads at 32-bit offsets, whenever x spans less than 4 GiB.
+// Three kernels share this scheme.  gather_rows_kernel serves gathers whose every column is a
+// plain float row (the transposed passes, forward calls without halo columns): column indices and
+// weights come by scalar loads, rows by range-checked buffer loads at 32-bit offsets.
+// gather_grouped_kernel serves halo gathers over a width-grouped message: per-edge set-up is
+// lane-parallel, and when x, the codes and the (min, scale) pairs lie within 4 GiB of one base
+// every load is that base plus a 32-bit offset, so an edge costs no scalar selects.  gather_kernel
+// is the general form: per-row offset tables, 64-bit addresses, and the fused quantising epilogue.
 #include "../../include/qha.h"
 #include "qha_internal.hpp"
 #include "quant_common.hpp"
+
+#include <type_traits>
 
 // the dequantisation scale * q + min is two roundings, as the message format defines it
 #pragma clang fp contract(off)
@@ -52,6 +58,12 @@ constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
 #endif
 #ifndef QHA_HALO_BATCH
 #define QHA_HALO_BATCH 8    // edges per batch when halo rows are dequantised too
+#endif
+#ifndef QHA_SINGLE_BASE
+#define QHA_SINGLE_BASE 1
+#endif
+#ifndef QHA_GROUPED_KERNEL
+#define QHA_GROUPED_KERNEL 1
 #endif
 #ifndef QHA_ROWS_KERNEL
 #define QHA_ROWS_KERNEL 1
@@ -123,18 +135,6 @@ __device__ __forceinline__ void load_row(const float* p, float (&xv)[VEC]) {
       xv[4 * q + 0] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
     }
   }
-}
-
-// Width and first code word of halo row k of a width-grouped buffer; the class table is held one
-// class per lane (v_cstart: first row, INT_MAX past the last class), so the class is the number of
-// lanes whose class starts at or before k, minus one.
-template <int D>
-__device__ __forceinline__ void class_of(int32_t v_cstart, int32_t v_cbits, uint32_t v_cbase, int32_t k, uint32_t& b,
-                                         uint32_t& off) {
-  const int c = __popcll(__ballot(v_cstart <= k)) - 1;
-  b = static_cast<uint32_t>(rdlane(v_cbits, c));
-  const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (((b << log2i(D)) + 31u) >> 5);
-  off = static_cast<uint32_t>(rdlane(static_cast<int>(v_cbase), c)) + static_cast<uint32_t>(k - rdlane(v_cstart, c)) * words;
 }
 
 // Quantises output row k of a gather, held VEC features per lane (lane l owns features l*VEC ..,
@@ -213,7 +213,7 @@ __device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, c
   if (lane == 0) *reinterpret_cast<float2*>(q.meta + 2 * k) = make_float2(rs.zp, rs.sc);
 }
 
-template <int D, bool HALO, bool BETA, bool GROUPED, bool QUANT>
+template <int D, bool HALO, bool BETA, bool QUANT>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;           // lanes that own features
@@ -246,20 +246,6 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int li = lane < nrows ? lane : nrows - 1;
   const int32_t v_end = split ? 0x7FFFFFFF : a.rowptr[row0 + li + 1];
   const int32_t v_out = (a.row_ids != nullptr) ? a.row_ids[row0 + li] : row0 + li;
-
-  // width classes of a grouped halo buffer, class i in lane i
-  int32_t v_cstart = 0x7FFFFFFF, v_cbits = 0;
-  uint32_t v_cbase = 0;
-  if constexpr (HALO && GROUPED) {
-#pragma unroll
-    for (int c = 0; c < kMaxClasses; ++c) {
-      if (lane == c && c < a.cls.n) {
-        v_cstart = a.cls.start[c];
-        v_cbits = a.cls.bits[c];
-        v_cbase = a.cls.base[c];
-      }
-    }
-  }
 
   double acc[VEC];
 #pragma unroll
@@ -315,164 +301,76 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       ww[i] = rdlanef(v_w, i);
     }
 
-    if constexpr (HALO && GROUPED) {
-      // batch set-up, vectorised over the batch's edges (edge i in lane i): each edge's class,
-      // width and code offset, and the two addresses its loads will use -- the value (an inner
-      // row, the raw floats of a 32-bit halo row, or for a quantised halo row its (min, scale) pair
-      // when each lane holds two features) and the code word row (the first word of the buffer for
-      // edges without codes).
-      constexpr bool META_IN_XV = VEC == 2;
-      const int32_t vk = v_u - static_cast<int32_t>(a.n_inner);
-      const bool vh = vk >= 0;
-      uint32_t vb = 0, vst = 0, vcb = 0;
+    // phase 1: inner rows (and with a per-row offset table: the halo rows' widths, offsets and
+    // (min, scale) pairs)
+    float xv[B][VEC];
+    float2 ms[B];
+    uint32_t cwd[B][CW];
+    uint32_t woff[B], bw[B];
 #pragma unroll
-      for (int c = 0; c < kMaxClasses; ++c) {
-        if (c < a.cls.n && vk >= a.cls.start[c]) {
-          vb = static_cast<uint32_t>(a.cls.bits[c]);
-          vst = static_cast<uint32_t>(a.cls.start[c]);
-          vcb = a.cls.base[c];
+    for (int i = 0; i < B; ++i) {
+      if (HALO && u[i] >= a.n_inner) {
+        const int32_t k = u[i] - static_cast<int32_t>(a.n_inner);
+        woff[i] = cst(a.word_offset)[k];
+        if constexpr (D >= 32) {
+          // the width follows from the row's word count (unique for d >= 32)
+          bw[i] = ((cst(a.word_offset)[k + 1] - woff[i]) << 5) >> log2i(D);
+        } else {
+          bw[i] = cst(a.bits)[k];
         }
+        ms[i] = *reinterpret_cast<const float2*>(a.meta + 2 * static_cast<int64_t>(k));
+      } else {
+        load_row<VEC>(a.x + static_cast<int64_t>(u[i]) * a.ldx + j0, xv[i]);
       }
-      const bool vq = vh && vb != 32u;                           // a quantised halo row
-      const uint32_t vlgb = vq ? static_cast<uint32_t>(__builtin_ctz(vb)) : 0u;
-      // words per row, a power of two: ceil(d*b/32) for codes (d = 16 with 1-bit codes fills half a
-      // word), d for raw rows
-      const uint32_t vlgdb = static_cast<uint32_t>(log2i(D)) + vlgb;
-      const uint32_t vlgw = (vb == 32u) ? static_cast<uint32_t>(log2i(D)) : (vlgdb > 5u ? vlgdb - 5u : 0u);
-      const uint32_t voff = vh ? vcb + ((static_cast<uint32_t>(vk) - vst) << vlgw) : 0u;
-      const uint64_t vval = !vh ? reinterpret_cast<uint64_t>(a.x + static_cast<int64_t>(v_u) * a.ldx)
-                          : (vq && META_IN_XV) ? reinterpret_cast<uint64_t>(a.meta + 2 * static_cast<int64_t>(vk))
-                                               : reinterpret_cast<uint64_t>(a.codes + voff);
-      const uint64_t vcode = reinterpret_cast<uint64_t>(a.codes + (vq ? voff : 0u));
-      const uint64_t vmeta = reinterpret_cast<uint64_t>(a.meta + 2 * static_cast<int64_t>(vq ? vk : 0));
-      const uint32_t vkind = vq ? vb : (vh ? 32u : 0u);          // 0: inner, 32: raw halo, else width
-
-      // phase 1: per edge, two (three when d >= 256) loads from the prepared addresses
-      float xv[B][VEC];
-      float2 mp[B];
-      uint32_t cwd[B][CW];
-      uint32_t kind[B];
+    }
+    if (e + B < e1) fetch(e + B);
+    // phase 2: the code words of the halo rows, once their offsets are in
+    if constexpr (HALO) {
 #pragma unroll
       for (int i = 0; i < B; ++i) {
-        kind[i] = static_cast<uint32_t>(rdlane(static_cast<int>(vkind), i));
-        const bool q = kind[i] != 0u && kind[i] != 32u;
-        const uint64_t va = (static_cast<uint64_t>(static_cast<uint32_t>(rdlane(static_cast<int>(vval >> 32), i))) << 32) |
-                            static_cast<uint32_t>(rdlane(static_cast<int>(vval), i));
-        load_row_unaligned<VEC>(reinterpret_cast<const float*>(va) + (q ? 0 : j0), xv[i]);
-        if constexpr (!META_IN_XV) {
-          const uint64_t ma = (static_cast<uint64_t>(static_cast<uint32_t>(rdlane(static_cast<int>(vmeta >> 32), i))) << 32) |
-                              static_cast<uint32_t>(rdlane(static_cast<int>(vmeta), i));
-          mp[i] = *reinterpret_cast<const float2*>(ma);
-        }
-        const uint64_t ca = (static_cast<uint64_t>(static_cast<uint32_t>(rdlane(static_cast<int>(vcode >> 32), i))) << 32) |
-                            static_cast<uint32_t>(rdlane(static_cast<int>(vcode), i));
-        const uint32_t lgb = static_cast<uint32_t>(rdlane(static_cast<int>(vlgb), i));
-        const uint32_t* crow = reinterpret_cast<const uint32_t*>(ca);
-        const uint32_t cw0 = q ? ((static_cast<uint32_t>(j0) << lgb) >> 5) : 0u;
-        cwd[i][0] = crow[cw0];
-        if (CW == 2) cwd[i][CW - 1] = crow[cw0 + ((q && kind[i] * VEC > 32u) ? 1u : 0u)];
-      }
-      if (e + B < e1) fetch(e + B);
-      // phase 2: dequantise and sum, closing the row whose last edge this is
+        if (u[i] >= a.n_inner) {
+          const uint32_t b = bw[i];
+          const uint32_t* row = a.codes + woff[i];
+          if (b == 32u) {
 #pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int32_t p = e + i;
-        if (p < e1) {
-          const double wt = static_cast<double>(ww[i]);
-          const uint32_t b = kind[i];
-          float val[VEC];
-          if (b != 0u && b != 32u) {
-            const float mn = META_IN_XV ? xv[i][0] : mp[i].x;
-            const float sc = META_IN_XV ? xv[i][1 % VEC] : mp[i].y;
+            for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
+          } else if (width_valid(b)) {
+            const uint32_t pos = static_cast<uint32_t>(j0) * b;
+            cwd[i][0] = row[pos >> 5];
+            if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
+          }
+        }
+      }
+    }
+    // phase 3: dequantise and sum, closing the row whose last edge this is
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int32_t p = e + i;
+      if (p < e1) {
+        const double wt = static_cast<double>(ww[i]);
+        if (HALO && u[i] >= a.n_inner && bw[i] != 32u) {
+          const uint32_t b = bw[i];
+          float q[VEC];
+          if (width_valid(b)) {
             const uint32_t mask = (1u << b) - 1u;
-            const uint32_t sh = (static_cast<uint32_t>(j0) << __builtin_ctz(b)) & 31u;
+            const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
               const uint32_t bitpos = sh + static_cast<uint32_t>(v) * b;
               const uint32_t wd = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
-              val[v] = dequant(sc, wd & mask, mn);
+              q[v] = dequant(ms[i].y, wd & mask, ms[i].x);
             }
           } else {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) val[v] = xv[i][v];
+            for (int v = 0; v < VEC; ++v) q[v] = 0.0f;
           }
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(val[v]), acc[v]);
-          if (p + 1 == cur_end) flush();
-        }
-      }
-    } else {
-      // phase 1: inner rows (and with a per-row offset table: the halo rows' widths, offsets and
-      // (min, scale) pairs)
-      float xv[B][VEC];
-      float2 ms[B];
-      uint32_t cwd[B][CW];
-      uint32_t woff[B], bw[B];
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        if (HALO && u[i] >= a.n_inner) {
-          const int32_t k = u[i] - static_cast<int32_t>(a.n_inner);
-          woff[i] = cst(a.word_offset)[k];
-          if constexpr (D >= 32) {
-            // the width follows from the row's word count (unique for d >= 32)
-            bw[i] = ((cst(a.word_offset)[k + 1] - woff[i]) << 5) >> log2i(D);
-          } else {
-            bw[i] = cst(a.bits)[k];
-          }
-          ms[i] = *reinterpret_cast<const float2*>(a.meta + 2 * static_cast<int64_t>(k));
+          for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(q[v]), acc[v]);
         } else {
-          load_row<VEC>(a.x + static_cast<int64_t>(u[i]) * a.ldx + j0, xv[i]);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
         }
-      }
-      if (e + B < e1) fetch(e + B);
-      // phase 2: the code words of the halo rows, once their offsets are in
-      if constexpr (HALO) {
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-          if (u[i] >= a.n_inner) {
-            const uint32_t b = bw[i];
-            const uint32_t* row = a.codes + woff[i];
-            if (b == 32u) {
-#pragma unroll
-              for (int v = 0; v < VEC; ++v) xv[i][v] = __uint_as_float(row[j0 + v]);
-            } else if (width_valid(b)) {
-              const uint32_t pos = static_cast<uint32_t>(j0) * b;
-              cwd[i][0] = row[pos >> 5];
-              if (CW == 2) cwd[i][CW - 1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
-            }
-          }
-        }
-      }
-      // phase 3: dequantise and sum, closing the row whose last edge this is
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int32_t p = e + i;
-        if (p < e1) {
-          const double wt = static_cast<double>(ww[i]);
-          if (HALO && u[i] >= a.n_inner && bw[i] != 32u) {
-            const uint32_t b = bw[i];
-            float q[VEC];
-            if (width_valid(b)) {
-              const uint32_t mask = (1u << b) - 1u;
-              const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
-#pragma unroll
-              for (int v = 0; v < VEC; ++v) {
-                const uint32_t bitpos = sh + static_cast<uint32_t>(v) * b;
-                const uint32_t wd = (CW == 2 && bitpos >= 32u) ? (cwd[i][CW - 1] >> (bitpos - 32u)) : (cwd[i][0] >> bitpos);
-                q[v] = dequant(ms[i].y, wd & mask, ms[i].x);
-              }
-            } else {
-#pragma unroll
-              for (int v = 0; v < VEC; ++v) q[v] = 0.0f;
-            }
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(q[v]), acc[v]);
-          } else {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
-          }
-          if (p + 1 == cur_end) flush();
-        }
+        if (p + 1 == cur_end) flush();
       }
     }
   }
@@ -628,6 +526,275 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
   }
 }
 
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+
+// VEC floats at byte offset off (32-bit, the same register in every lane or a per-lane one) from a
+// global base held in scalar registers: one global load in its scalar-base form.
+template <int VEC>
+__device__ __forceinline__ void global_row(gptr<char> base, uint32_t off, float (&xv)[VEC]) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  gptr<char> p = base + off;
+  if constexpr (VEC == 1) {
+    xv[0] = *reinterpret_cast<gptr<float>>(p);
+  } else if constexpr (VEC == 2) {
+    const v2f t = *reinterpret_cast<gptr<v2f>>(p);
+    xv[0] = t.x; xv[1] = t.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const v4f t = reinterpret_cast<gptr<v4f>>(p)[q];
+      xv[4 * q + 0] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+    }
+  }
+}
+
+// Halo gather over a width-grouped message (rows ordered by width, the guide's section 9 packing).
+// A batch's set-up runs one edge per lane: the column's class (a scan of the few class starts),
+// width, code-row offset, and the 32-bit byte offset of the edge's value load -- the inner row,
+// the raw row of a 32-bit halo, or the (min, scale) pair of a quantised one.  Each edge then moves
+// three words to scalar registers (kind and width, value offset, code offset) and issues exactly
+// two loads, with the value's base chosen by scalar selects: the value, and the code word that
+// holds the lane's features (a word of the buffer's first row for edges without codes), so every
+// edge's loads are counted alike and the sums can consume them one edge at a time.  Dequantisation
+// branches once per edge on its width, with that width's lane shifts precomputed.
+template <int D, bool BETA, bool SB>
+__global__ __launch_bounds__(256) void gather_grouped_kernel(GatherArgs a) {
+  constexpr int VEC = vec_of(D);
+  constexpr int G = D / VEC;
+  constexpr int B = batch_of(D, true);
+  constexpr int CW = (VEC * 8 > 32) ? 2 : 1;
+  constexpr int LGD = log2i(D);
+  constexpr uint32_t LGV = static_cast<uint32_t>(log2i(VEC));
+  const int lane = threadIdx.x & 63;
+  const int j0 = (G == 64 ? lane : (lane < G ? lane : 0)) * VEC;
+  const bool owner = (G == 64) || lane < G;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (item >= a.n_items) return;
+
+  int32_t row0, nrows, e0, e1;
+  if (a.items != nullptr) {
+    cptr<int32_t> it = cst(a.items) + 4 * item;
+    row0 = it[0];
+    nrows = it[1];
+    e0 = it[2];
+    e1 = it[3];
+  } else {
+    row0 = static_cast<int32_t>(item);
+    nrows = 1;
+    e0 = cst(a.rowptr)[item];
+    e1 = cst(a.rowptr)[item + 1];
+  }
+  const bool split = item < a.n_split_items;
+  const int li = lane < nrows ? lane : nrows - 1;
+  const int32_t v_end = split ? 0x7FFFFFFF : a.rowptr[row0 + li + 1];
+  const int32_t v_out = (a.row_ids != nullptr) ? a.row_ids[row0 + li] : row0 + li;
+
+  // the class table, class c in lane c
+  int32_t v_cstart = 0x7FFFFFFF, v_cbits = 0;
+  uint32_t v_cbase = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxClasses; ++c) {
+    if (lane == c && c < a.cls.n) {
+      v_cstart = a.cls.start[c];
+      v_cbits = a.cls.bits[c];
+      v_cbase = a.cls.base[c];
+    }
+  }
+  const int ncls = a.cls.n;
+  // per width b = 2^lgb: the lane's first code bit within its word
+  uint32_t v_sh[4];
+#pragma unroll
+  for (int lgb = 0; lgb < 4; ++lgb) v_sh[lgb] = (static_cast<uint32_t>(j0) << lgb) & 31u;
+  const uint32_t lane_eff = static_cast<uint32_t>(j0) >> LGV;
+
+  // with one base (SB) every load is that base plus a 32-bit offset, and offsets carry the
+  // buffers' own distances from it
+  gptr<char> xb = SB ? (gptr<char>)(a.base) : (gptr<char>)(a.x);
+  gptr<char> cb = SB ? (gptr<char>)(a.base) : (gptr<char>)(a.codes);
+  gptr<char> mb = SB ? (gptr<char>)(a.base) : (gptr<char>)(a.meta);
+  const uint32_t x_off = SB ? a.x_off : 0u;
+  const uint32_t codes_off = SB ? a.codes_off : 0u;
+  const uint32_t meta_off = SB ? a.meta_off : 0u;
+  const uint32_t pitch = static_cast<uint32_t>(a.ldx) * 4u;
+  const uint32_t lane_off = static_cast<uint32_t>(j0) * 4u;
+  const int32_t n_inner = static_cast<int32_t>(a.n_inner);
+
+  double acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+  int cur = 0;
+  int32_t cur_end = rdlane(v_end, 0);
+  auto flush = [&]() {
+    const int64_t orow = rdlane(v_out, cur);
+    if (owner) {
+      float* dst = a.out + orow * a.ldo + j0;
+      float res[VEC];
+      if constexpr (BETA) {
+        float old[VEC];
+        load_row<VEC>(dst, old);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+      }
+      store_row<VEC>(dst, res);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+    ++cur;
+    cur_end = rdlane(v_end, cur < nrows ? cur : nrows - 1);
+  };
+
+  int32_t v_u = 0;
+  float v_w = 1.0f;
+  const bool weighted = a.w != nullptr;
+  auto fetch = [&](int32_t eb) {
+    const int32_t ei = min(eb + lane, e1 - 1);
+    v_u = a.colidx[ei];
+    if (weighted) v_w = a.w[ei];
+  };
+  if (e0 < e1) fetch(e0);
+
+  for (int32_t e = e0; e < e1; e += B) {
+    // set-up, edge i in lane i
+    const int32_t vk = v_u - n_inner;
+    const bool vh = vk >= 0;
+    int32_t vst = rdlane(v_cstart, 0);
+    uint32_t vb = static_cast<uint32_t>(rdlane(v_cbits, 0));
+    uint32_t vcb = static_cast<uint32_t>(rdlane(static_cast<int>(v_cbase), 0));
+    for (int c = 1; c < ncls; ++c) {
+      const int32_t st = rdlane(v_cstart, c);
+      const uint32_t bc = static_cast<uint32_t>(rdlane(v_cbits, c));
+      const uint32_t cbc = static_cast<uint32_t>(rdlane(static_cast<int>(v_cbase), c));
+      const bool ge = vk >= st;
+      vst = ge ? st : vst;
+      vb = ge ? bc : vb;
+      vcb = ge ? cbc : vcb;
+    }
+    const bool vq = vh && vb != 32u;
+    const uint32_t vlgb = static_cast<uint32_t>(__builtin_ctz(vb));             // 5 for raw rows
+    const uint32_t vlgw = vb == 32u ? static_cast<uint32_t>(LGD) : (LGD + vlgb > 5u ? LGD + vlgb - 5u : 0u);
+    const uint32_t vrow = vcb + (static_cast<uint32_t>(vk - vst) << vlgw);     // code-row word offset
+    const uint32_t vvo = !vh ? x_off + static_cast<uint32_t>(v_u) * pitch
+                             : (vq ? meta_off + static_cast<uint32_t>(vk) * 8u : codes_off + vrow * 4u);
+    const uint32_t vco = codes_off + (vq ? vrow * 4u : 0u);
+    // kind (0 inner, 32 raw halo, else the code width) | lane shift of the code word << 8: the word
+    // holding a lane's first code is lane * VEC * b / 32, i.e. lane >> (5 - log2(VEC * b)); edges
+    // without codes take shift 6, so every lane reads the buffer's first word
+    const uint32_t vsh = vq ? (LGV + vlgb <= 5u ? 5u - LGV - vlgb : 0u) : 6u;
+    const uint32_t vpk = (vh ? (vq ? vb : 32u) : 0u) | (vsh << 8) | ((vq ? vlgb : 0u) << 16);
+
+    // phase 1: two loads per edge
+    float xv[B][VEC];
+    float mp[B][2];                    // (min, scale) when a lane holds one feature
+    uint32_t cwd[B][CW];
+    uint32_t pk[B];
+    float ww[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      pk[i] = static_cast<uint32_t>(rdlane(static_cast<int>(vpk), i));
+      ww[i] = rdlanef(v_w, i);
+      const uint32_t kind = pk[i] & 0xFFu;
+      const uint32_t wsh = (pk[i] >> 8) & 0xFFu;
+      const uint32_t vo = static_cast<uint32_t>(rdlane(static_cast<int>(vvo), i));
+      const uint32_t co = static_cast<uint32_t>(rdlane(static_cast<int>(vco), i));
+      const bool q = kind != 0u && kind != 32u;
+      if (SB && VEC == 2) {
+        // one load form for every edge: a quantised row's (min, scale) pair is read by all lanes
+        global_row<VEC>(xb, vo + (lane_off & (q ? 0u : 0xFFFFFFFFu)), xv[i]);
+      } else if (q) {
+        float pr[2];
+        global_row<2>(mb, vo, pr);
+        if constexpr (VEC >= 2) {
+          xv[i][0] = pr[0];
+          xv[i][1] = pr[1];
+        } else {
+          mp[i][0] = pr[0];
+          mp[i][1] = pr[1];
+        }
+      } else {
+        global_row<VEC>(kind == 0u ? xb : cb, vo + lane_off, xv[i]);
+      }
+      // the byte offset of the word holding the lane's first code (8-bit codes at VEC = 8 take two
+      // words a lane: lane * 2)
+      uint32_t wofs = (lane_eff >> wsh) << 2;
+      if constexpr (LGV + 3 > 5) {
+        if (kind == 8u) wofs = lane_eff << 3;
+      }
+      gptr<uint32_t> crow = reinterpret_cast<gptr<uint32_t>>(cb + (co + wofs));
+      cwd[i][0] = crow[0];
+      if constexpr (CW == 2) cwd[i][1] = crow[kind * VEC > 32u && q ? 1 : 0];
+    }
+    if (e + B < e1) fetch(e + B);
+
+    // phase 2: dequantise and sum, closing the row whose last edge this is
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int32_t p = e + i;
+      if (p < e1) {
+        const double wt = static_cast<double>(ww[i]);
+        const uint32_t kind = pk[i] & 0xFFu;
+        if (kind == 0u || kind == 32u) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(xv[i][v]), acc[v]);
+        } else if constexpr (SB) {
+          // the width as a run-time field: one branch per edge
+          const float mn = VEC >= 2 ? xv[i][0] : mp[i][0];
+          const float sc = VEC >= 2 ? xv[i][1 % VEC] : mp[i][1];
+          const uint32_t b = kind;
+          const uint32_t lgb = pk[i] >> 16;
+          const uint32_t bit0 = (static_cast<uint32_t>(j0) << lgb) & 31u;
+          float qv[VEC];
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const uint32_t vb_ = static_cast<uint32_t>(v) * b;
+            const uint32_t word = (CW == 2 && vb_ >= 32u) ? cwd[i][CW - 1] : cwd[i][0];
+            const uint32_t code = __builtin_amdgcn_ubfe(word, (bit0 + vb_) & 31u, b);
+            qv[v] = dequant(sc, code, mn);
+          }
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(qv[v]), acc[v]);
+        } else {
+          const float mn = VEC >= 2 ? xv[i][0] : mp[i][0];
+          const float sc = VEC >= 2 ? xv[i][1 % VEC] : mp[i][1];
+          auto body = [&](auto bc) {
+            constexpr uint32_t b = decltype(bc)::value;
+            constexpr uint32_t lg = static_cast<uint32_t>(log2i(static_cast<int>(b)));
+            float q[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const uint32_t word = (CW == 2 && (static_cast<uint32_t>(v) * b) >= 32u) ? cwd[i][CW - 1] : cwd[i][0];
+              const uint32_t bit = (v_sh[lg] + static_cast<uint32_t>(v) * b) & 31u;
+              q[v] = dequant(sc, (word >> bit) & ((1u << b) - 1u), mn);
+            }
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(q[v]), acc[v]);
+          };
+          if (kind == 4u) body(std::integral_constant<uint32_t, 4>{});
+          else if (kind == 8u) body(std::integral_constant<uint32_t, 8>{});
+          else if (kind == 2u) body(std::integral_constant<uint32_t, 2>{});
+          else body(std::integral_constant<uint32_t, 1>{});
+        }
+        if (p + 1 == cur_end) flush();
+      }
+    }
+  }
+
+  if (split) {
+    double* p = a.partial + item * D + j0;
+    if (owner) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) p[v] = acc[v];
+    }
+  } else if (e0 == e1) {
+    flush();
+  }
+}
+
 // Adds the partial sums of every split row in chunk order and writes (or quantises) the row.
 template <int D, bool QUANT>
 __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
@@ -676,35 +843,66 @@ __global__ __launch_bounds__(256) void edge_weights_kernel(int64_t n_rows, const
     w[e] = __fmul_rn(rf, c ? c[colidx[e]] : 1.0f);
 }
 
-template <int D, bool HALO, bool BETA>
-void launch_variant(const GatherArgs& a, dim3 grid, hipStream_t s) {
-  if (HALO && a.cls.n > 0)
-    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, true, false>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((gather_kernel<D, HALO, BETA, false, false>), grid, dim3(256), 0, s, a);
-}
-
 template <int D>
 hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_out, hipStream_t s) {
   // the plain-row kernel addresses x with 32-bit byte offsets
   const int64_t x_bytes = a.n_inner > 0 ? ((a.n_inner - 1) * a.ldx + D) * 4 : 0;
   const bool rows_ok = x_bytes <= static_cast<int64_t>(0xFFFFFFFFu) && QHA_ROWS_KERNEL;
+  // the grouped halo kernel addresses x, the codes and the (min, scale) pairs with 32-bit offsets
+  bool grouped_ok = false, single_base = false;
+  uintptr_t lo = 0;
+  if (with_halo && a.cls.n > 0 && QHA_GROUPED_KERNEL) {
+    const int c = a.cls.n - 1;
+    const int64_t b = a.cls.bits[c];
+    const int64_t words = b == 32 ? D : (D * b + 31) / 32;
+    const int64_t code_bytes = (static_cast<int64_t>(a.cls.base[c]) + (a.cls.start[c + 1] - a.cls.start[c]) * words) * 4;
+    grouped_ok = x_bytes <= static_cast<int64_t>(0xFFFFFFFFu) && code_bytes <= static_cast<int64_t>(0xFFFFFFFFu) &&
+                 a.n_halo * 8 <= static_cast<int64_t>(0xFFFFFFFFu);
+    // the span from the lowest to the highest byte of x, codes and meta
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(a.codes), m0 = reinterpret_cast<uintptr_t>(a.meta);
+    lo = c0 < m0 ? c0 : m0;
+    uintptr_t hi = c0 + static_cast<uintptr_t>(code_bytes);
+    const uintptr_t mh = m0 + static_cast<uintptr_t>(a.n_halo * 8);
+    hi = mh > hi ? mh : hi;
+    if (a.x != nullptr && x_bytes > 0) {
+      const uintptr_t x0 = reinterpret_cast<uintptr_t>(a.x);
+      lo = x0 < lo ? x0 : lo;
+      const uintptr_t xh = x0 + static_cast<uintptr_t>(x_bytes);
+      hi = xh > hi ? xh : hi;
+    }
+    single_base = QHA_SINGLE_BASE && hi - lo <= 0xFFFFFFFFull;
+  }
 
   if (a.n_items > 0) {
     const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
     if (quantize_out) {
-      hipLaunchKernelGGL((gather_kernel<D, false, false, false, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gather_kernel<D, false, false, true>), grid, dim3(256), 0, s, a);
+    } else if (with_halo && grouped_ok) {
+      GatherArgs r = a;
+      if (single_base) {
+        r.base = reinterpret_cast<const char*>(lo);
+        r.x_off = a.x ? static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a.x) - lo) : 0u;
+        r.codes_off = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a.codes) - lo);
+        r.meta_off = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a.meta) - lo);
+        if (a.beta) hipLaunchKernelGGL((gather_grouped_kernel<D, true, true>), grid, dim3(256), 0, s, r);
+        else hipLaunchKernelGGL((gather_grouped_kernel<D, false, true>), grid, dim3(256), 0, s, r);
+      } else {
+        if (a.beta) hipLaunchKernelGGL((gather_grouped_kernel<D, true, false>), grid, dim3(256), 0, s, r);
+        else hipLaunchKernelGGL((gather_grouped_kernel<D, false, false>), grid, dim3(256), 0, s, r);
+      }
     } else if (with_halo) {
-      if (a.beta) launch_variant<D, true, true>(a, grid, s);
-      else launch_variant<D, true, false>(a, grid, s);
+      // the per-row offset table (also the way for width classes beyond 32-bit offsets)
+      if (a.word_offset == nullptr || (D < 32 && a.bits == nullptr)) return hipErrorInvalidValue;
+      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, true, true, false>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gather_kernel<D, true, false, false>), grid, dim3(256), 0, s, a);
     } else if (rows_ok) {
       GatherArgs r = a;
       r.x_bytes = static_cast<uint32_t>(x_bytes);
       if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true>), grid, dim3(256), 0, s, r);
       else hipLaunchKernelGGL((gather_rows_kernel<D, false>), grid, dim3(256), 0, s, r);
     } else {
-      if (a.beta) launch_variant<D, false, true>(a, grid, s);
-      else launch_variant<D, false, false>(a, grid, s);
+      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true, false>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gather_kernel<D, false, false, false>), grid, dim3(256), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

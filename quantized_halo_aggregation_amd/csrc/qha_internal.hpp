@@ -69,6 +69,10 @@ struct GatherArgs {
   uint32_t x_bytes;           // readable bytes of x (set by the launcher for range-checked loads)
   const uint32_t* codes;
   uint32_t codes_bytes;       // bound on the readable bytes of codes (set by the launcher)
+  // one base under x, codes and meta with every byte of them within 4 GiB of it (set by the
+  // launcher when that holds): the grouped halo gather then addresses all three from one register
+  const char* base;
+  uint32_t x_off, codes_off, meta_off;
   const uint32_t* word_offset;
   const uint8_t* bits;
   Classes cls;

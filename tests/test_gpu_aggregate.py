@@ -295,3 +295,38 @@ def test_plain_gather_beyond_32bit_offsets():
     H.assert_close(H.host(ga), ref, what="transposed-call form, same rows")
     del big
     torch.cuda.empty_cache()
+
+
+def test_grouped_gather_with_buffers_far_apart():
+    """Inner rows and the received message more than 4 GiB apart: the grouped gather cannot address
+    them from one base and takes its per-buffer path, with the same result as when they are close."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    part, gp = _setup(CASES[3])
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    msg = H.oracle_messages(part.x[part.mirror], part.bits, SEED, 0, 0, n_in)
+    x_cols = np.concatenate([part.x, msg["received"]])
+    ref = OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, x_cols)
+    words = msg["words"].view(np.int32)
+    meta = np.stack([msg["zero_point"], msg["scale"]], 1).astype(np.float32).reshape(-1)
+    gap = (5 << 30) // 4                                    # 5 GiB of float32 between them
+    big = torch.empty(gap + words.size + meta.size + 64, dtype=torch.float32, device="cuda")
+    xs = big[:n_in * d].view(n_in, d)
+    xs.copy_(H.dev(part.x))
+    codes = big[gap:gap + words.size].view(torch.int32)
+    codes.copy_(H.dev(words))
+    mt = big[gap + words.size + 16:gap + words.size + 16 + meta.size]
+    mt.copy_(H.dev(meta))
+    assert gp.classes is not None
+    H.note("grouped gather, buffers 5 GiB apart")
+    out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dequant_aggregate_fwd(gp.rowptr, gp.colidx, gp.w_fwd, gp.plan_fwd, xs, n_in, codes, gp.word_offset, gp.bits,
+                            gp.classes, mt.view(-1, 2), n_h, 0, out, workspace=gp.agg_ws)
+    got = H.host(out)
+    H.assert_close(got, ref, what="grouped gather, far buffers")
+    near = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_fwd(H.dev(part.x), H.upload_messages(gp, msg), near)
+    H.assert_bits_equal(got, H.host(near), "far and near buffers give the same bits")
+    del big, xs, codes, mt
+    torch.cuda.empty_cache()
