@@ -140,3 +140,32 @@ def test_dense_backward_of_no_rows_writes_zero_weight_gradient():
     H.note("dense_backward m=0")
     B.dense_backward(e, e, e, w, e, dw)
     assert not H.host(dw).any()
+
+
+@pytest.mark.parametrize("dist", ["normal", "wide-range", "cancelling"])
+def test_forward_error_is_float32_class(dist):
+    """The width-128 forward's error against float64, relative to sum_k |a_k w_k| per element, stays
+    within 8 units of float32 rounding (2^-24) on well-scaled, wide-range (e^+-8 per element) and
+    cancelling rows: the products are formed at float32 accuracy whatever units compute them."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng({"normal": 1, "wide-range": 2, "cancelling": 3}[dist])
+    m, d = 3001, 128
+    if dist == "normal":
+        a = rng.standard_normal((m, d))
+    elif dist == "wide-range":
+        a = rng.standard_normal((m, d)) * np.exp(rng.uniform(-8, 8, (m, d)))
+    else:
+        a = np.repeat(rng.standard_normal((m, 1)), d, 1) * np.where(np.arange(d) % 2, 1, -1) + \
+            1e-3 * rng.standard_normal((m, d))
+    a = a.astype(np.float32)
+    w = (rng.standard_normal((d, d)) / 11.3).astype(np.float32)
+    H.note(f"forward error bound, {dist}")
+    h = torch.full((m, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, H.dev(a), H.dev(w), 0, h)
+    got = H.host(h).astype(np.float64)
+    ref = a.astype(np.float64) @ w.astype(np.float64).T
+    scale = np.abs(a.astype(np.float64)) @ np.abs(w.astype(np.float64)).T
+    err = np.abs(got - ref) / scale
+    assert err.max() <= 8 * 2.0 ** -24, f"max error {err.max() * 2**24:.2f} units of 2^-24"
