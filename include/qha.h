@@ -12,7 +12,7 @@
  *   qha_dequant_aggregate_fwd dequantisation fused into the normalised neighbour gather (SpMM)
  *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
  *   qha_aggregate_bwd_quantize the same over the halo columns, quantising each gradient row
- *   qha_dense_project         the dense projection (fp32 MFMA) with ReLU
+ *   qha_dense_project         the dense projection (float32 products on matrix cores) with ReLU
  *   qha_dense_backward        its gradients dA and dW in one pass
  *
  * plus small set-up helpers.  Conventions shared by every entry point:
@@ -262,7 +262,12 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
  * Products are accumulated by the fp32 matrix cores over 32 values of k at a time and those
  * partial sums are added in float64; the result is rounded to float32 once (after adding C when
  * beta = 1, before the epilogue).  The forward shape n = k = 128 (trans_b = 1, no prologue,
- * beta = 0) runs as a row-panel kernel that keeps B in on-chip memory.  When m*n is small and k large the reduction is split over k
+ * beta = 0) runs as a row-panel kernel on the bf16 matrix cores instead: each float32 operand is
+ * split exactly into three bf16 parts and each product is rebuilt from the six part products of
+ * weight >= 2^-16 of it (the dropped ones total below 2^-23 of the product), accumulated in
+ * float32 over 32 values of k and in float64 across them; its error against float64 is of the
+ * same size as the fp32 matrix cores' (at most 8 units of 2^-24 of sum_k |a_k b_k| per element
+ * in the tests).  When m*n is small and k large the reduction is split over k
  * into float64 partials in the workspace (device, 16-byte aligned, qha_dense_project_workspace
  * bytes) and summed in a fixed order; results are deterministic.  beta is 0 or 1.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */

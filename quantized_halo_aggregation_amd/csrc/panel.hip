@@ -5,24 +5,27 @@
 // gradient sums (dL/dh_v * sigma'(z_v)) a_v^T over the rows).
 //
 // Mapping to gfx950: the tall operands have m rows (a partition's nodes, 10^5..10^6) and 128
-// columns; W is 128 x 128 (64 KB).  One 1024-thread block per compute unit keeps W in LDS for the
-// whole launch and streams 64-row panels of the tall operands through LDS, loading the next
-// panel into registers while the matrix cores work on the current one; sixteen wavefronts (four
-// per SIMD) hide each other's LDS latency.  Each wavefront owns two 16 x 16 tiles of a panel's
-// product (v_mfma_f32_16x16x4f32); in the backward it also owns one 32 x 32 tile of dW
-// (v_mfma_f32_32x32x2f32), which stays in registers across all of the block's panels, so dH, H
-// and A are each read once and dZ is formed once.  Operand reads: a lane that walks a row along
-// the contraction takes four consecutive values with one 16-byte LDS read and feeds them to four
-// consecutive MFMAs (the lane groups take interleaved k ranges); a lane that walks a column reads
-// one float per MFMA, the lane groups far enough apart in rows that the 64 reads hit 64 banks
-// (row strides of 136 and 132 floats, measured free of bank conflicts for these patterns).
-// Precision: for the forward and dA each MFMA chain adds 32 products in fp32 and those partial
-// sums are added in float64.  A block's dW tiles are fp32 MFMA sums over its panels' rows (about
-// m/256 rows); a second kernel adds the blocks' partials in float64 in a fixed order, so results
-// are deterministic.
+// columns; W is 128 x 128 (64 KB).
+// Forward (panel_fwd_x3_kernel): float32 products on the bf16 matrix cores.  Each operand is split
+// into three bf16 parts and each product is rebuilt from the six part products that matter (the
+// split and the error bound are at split3); W's parts stay in registers, A is streamed through LDS
+// as three bf16 planes of 64-row panels, double-buffered, with v_mfma_f32_32x32x16_bf16.
+// Backward (panel_bwd_kernel): one 1024-thread block per compute unit keeps W in LDS for the whole
+// launch and streams 64-row panels of dH, H and A through LDS, loading the next panel into
+// registers while the matrix cores work on the current one; sixteen wavefronts (four per SIMD)
+// hide each other's LDS latency.  Each wavefront owns two 16 x 16 tiles of dA
+// (v_mfma_f32_16x16x4f32) and one 32 x 32 tile of dW (v_mfma_f32_32x32x2f32), which stays in
+// registers across all of the block's panels, so dH, H and A are each read once and dZ is formed
+// once.  Operand reads: a lane that walks a row along the contraction takes four consecutive
+// values with one 16-byte LDS read and feeds them to four consecutive MFMAs (the lane groups take
+// interleaved k ranges); a lane that walks a column reads one float per MFMA, the lane groups far
+// enough apart in rows that the reads hit distinct banks (row strides of 136 and 132 floats,
+// measured free of bank conflicts for these patterns).
+// Precision: for the forward and dA each MFMA chain adds 32 k-steps in float32 and those partial
+// sums are added in float64.  A block's dW tiles are float32 MFMA sums over its panels' rows
+// (about m/256 rows); a second kernel adds the blocks' partials in float64 in a fixed order, so
+// results are deterministic.
 #include "qha_internal.hpp"
-
-#include <type_traits>
 
 namespace qha {
 namespace {
@@ -65,18 +68,6 @@ __device__ __forceinline__ void load_panel(const float* p, int64_t ld, int64_t m
   }
 }
 
-// The same rows, every lane loading: a row at or past m re-reads row m - 1 (for products whose
-// rows are independent and whose rows past m are never stored).  The number of loads in flight
-// is then the same on every path, so waits can count them.
-__device__ __forceinline__ void load_panel_all(const float* p, int64_t ld, int64_t m, int64_t r0, float4 (&v)[SV]) {
-#pragma unroll
-  for (int s = 0; s < SV; ++s) {
-    const int f = static_cast<int>(threadIdx.x) + NT * s;
-    const int64_t r = r0 + (f >> 5);
-    v[s] = *reinterpret_cast<const float4*>(p + (r < m ? r : m - 1) * ld + 4 * (f & 31));
-  }
-}
-
 __device__ __forceinline__ void store_panel(float* lds, const float4 (&v)[SV]) {
 #pragma unroll
   for (int s = 0; s < SV; ++s) {
@@ -95,134 +86,6 @@ __device__ __forceinline__ void load_w(float* lds, const float* w, int64_t ldw) 
   }
 }
 
-// One panel of the forward: stage it from registers (s0, s1) into LDS, start loading the panel
-// `ahead` into the same registers, then multiply and store.  FULL: every row of the panel exists,
-// so the stores are unconditional and every step issues the same number of memory operations.
-template <bool FULL>
-__device__ __forceinline__ void panel_fwd_step(const PanelArgs& p, float* As, const float* arow, const float* brow0,
-                                               const float* brow1, int64_t panel, int64_t ahead, float4& s0,
-                                               float4& s1, int rt, int cp, int g, int i) {
-  static_assert(SV == 2, "two staged float4 per thread");
-  __syncthreads();                       // the previous panel's reads are done
-  {
-    const float4 v[SV] = {s0, s1};
-    store_panel(As, v);
-  }
-  __syncthreads();
-  {
-    float4 v[SV];
-    load_panel_all(p.a, p.lda, p.m, ahead * PR, v);
-    s0 = v[0];
-    s1 = v[1];
-  }
-
-  double sum0[4], sum1[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sum0[r] = sum1[r] = 0.0;
-#pragma unroll
-  for (int kc = 0; kc < PD / 32; ++kc) {
-    floatx4 acc0, acc1;
-    zero<4>(acc0);
-    zero<4>(acc1);
-#pragma unroll
-    for (int q = 2 * kc; q < 2 * kc + 2; ++q) {
-      const float4 av = *reinterpret_cast<const float4*>(arow + 16 * q);
-      const float4 b0 = *reinterpret_cast<const float4*>(brow0 + 16 * q);
-      const float4 b1 = *reinterpret_cast<const float4*>(brow1 + 16 * q);
-      acc0 = mfma16(av.x, b0.x, acc0);
-      acc1 = mfma16(av.x, b1.x, acc1);
-      acc0 = mfma16(av.y, b0.y, acc0);
-      acc1 = mfma16(av.y, b1.y, acc1);
-      acc0 = mfma16(av.z, b0.z, acc0);
-      acc1 = mfma16(av.z, b1.z, acc1);
-      acc0 = mfma16(av.w, b0.w, acc0);
-      acc1 = mfma16(av.w, b1.w, acc1);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sum0[r] += static_cast<double>(acc0[r]);
-      sum1[r] += static_cast<double>(acc1[r]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t row = panel * PR + 16 * rt + 4 * g + r;
-    if (FULL || row < p.m) {
-      float v0 = static_cast<float>(sum0[r]);
-      float v1 = static_cast<float>(sum1[r]);
-      if (p.relu) {
-        v0 = v0 > 0.0f ? v0 : 0.0f;
-        v1 = v1 > 0.0f ? v1 : 0.0f;
-      }
-      float* dst = p.out + row * p.ldo + 32 * cp + i;
-      dst[0] = v0;
-      dst[16] = v1;
-    }
-  }
-}
-
-// H = epi(A W^T): A [m x 128], W [128 x 128], H [m x 128].  Wavefront w owns panel rows
-// 16*(w/4) .. +15 and output columns 32*(w%4) .. +31 as two 16 x 16 tiles (v_mfma_f32_16x16x4f32:
-// lane (g, i) = (lane/16, lane%16) supplies row i of A and row i of W^T's column block at
-// k = 16q + 4g + c for MFMA c of step q; its four accumulators are C[4g + r][i]).  A block walks
-// its panels with two register sets of staged rows taken in turn, so each panel's load has two
-// panels of work to arrive in.
-__global__ __launch_bounds__(NT) void panel_fwd_kernel(PanelArgs p) {
-  __shared__ __attribute__((aligned(16))) float Ws[PD * LS];
-  __shared__ __attribute__((aligned(16))) float As[PR * LS];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int g = lane >> 4;
-  const int i = lane & 15;
-  const int rt = wid >> 2;      // 16-row block of the panel
-  const int cp = wid & 3;       // 32-column block of the output
-  const int64_t n_panels = (p.m + PR - 1) / PR;
-  const int64_t n_full = p.m / PR;
-  const int64_t stride = gridDim.x;
-  const int64_t first = blockIdx.x;
-  if (first >= n_panels) return;
-
-  load_w<LS>(Ws, p.w, p.ldw);
-  const float* arow = &As[(16 * rt + i) * LS + 4 * g];
-  const float* brow0 = &Ws[(32 * cp + i) * LS + 4 * g];
-  const float* brow1 = brow0 + 16 * LS;
-  auto clampp = [&](int64_t q) { return q < n_panels ? q : n_panels - 1; };
-
-  float4 a0, a1, b0, b1;
-  {
-    float4 v[SV];
-    load_panel_all(p.a, p.lda, p.m, first * PR, v);
-    a0 = v[0];
-    a1 = v[1];
-    load_panel_all(p.a, p.lda, p.m, clampp(first + stride) * PR, v);
-    b0 = v[0];
-    b1 = v[1];
-  }
-  // the ragged last panel of the matrix, if it is this block's, ends the walk (past the last
-  // panel the prefetch re-reads it, keeping the loads in flight path-independent)
-  int64_t panel = first;
-  for (;;) {
-    if (panel >= n_full) {
-      if (panel < n_panels)
-        panel_fwd_step<false>(p, As, arow, brow0, brow1, panel, clampp(panel + 2 * stride), a0, a1, rt, cp, g, i);
-      break;
-    }
-    panel_fwd_step<true>(p, As, arow, brow0, brow1, panel, clampp(panel + 2 * stride), a0, a1, rt, cp, g, i);
-    panel += stride;
-    if (panel >= n_full) {
-      if (panel < n_panels)
-        panel_fwd_step<false>(p, As, arow, brow0, brow1, panel, clampp(panel + 2 * stride), b0, b1, rt, cp, g, i);
-      break;
-    }
-    panel_fwd_step<true>(p, As, arow, brow0, brow1, panel, clampp(panel + 2 * stride), b0, b1, rt, cp, g, i);
-    panel += stride;
-  }
-}
-
-#ifndef QHA_PANEL_X3
-#define QHA_PANEL_X3 1             // the forward on bf16 matrix cores with a three-way split
-#endif
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int X3_NT = 512;          // 8 wavefronts: 2 row blocks x 4 column blocks of 32 x 32
 constexpr int X3_PR = 64;           // rows per panel
@@ -368,86 +231,6 @@ __global__ __launch_bounds__(X3_NT) void panel_fwd_x3_kernel(PanelArgs p) {
       }
     }
     __syncthreads();
-  }
-}
-
-#ifndef QHA_PANEL_FWD_RB
-#define QHA_PANEL_FWD_RB 0          // the row-block forward (0: the panel forward)
-#endif
-constexpr int F2_NT = 512;          // 8 wavefronts: 4 row slots x 2 column halves
-constexpr int F2_BLOCKS = 512;      // two blocks per compute unit
-
-// H = epi(A W^T) without per-panel barriers: W stays in LDS (loaded once per block) and every
-// wavefront then works alone on 16-row blocks.  It loads its rows' A fragments from global memory
-// straight into registers (lane (g, i): row i, columns 16q + 4g .. +3 for q = 0..7, the operand
-// layout of v_mfma_f32_16x16x4f32) and computes one half of the output columns, four 16 x 16
-// tiles, folding each 32-k MFMA chain into float64.  The two wavefronts of a row slot take the two
-// halves of the same rows, so the second read of A is served by the compute unit's cache.
-__global__ __launch_bounds__(F2_NT, 4) void panel_fwd_rb_kernel(PanelArgs p) {
-  __shared__ __attribute__((aligned(16))) float Ws[PD * LS];
-#pragma unroll
-  for (int s = 0; s < PD * PD / 4 / F2_NT; ++s) {
-    const int f = static_cast<int>(threadIdx.x) + F2_NT * s;
-    *reinterpret_cast<float4*>(&Ws[(f >> 5) * LS + 4 * (f & 31)]) =
-        *reinterpret_cast<const float4*>(p.w + static_cast<int64_t>(f >> 5) * p.ldw + 4 * (f & 31));
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int g = lane >> 4;
-  const int i = lane & 15;
-  const int ch = wid & 1;
-  const int rs = wid >> 1;
-  const int64_t n_rb = (p.m + 15) / 16;
-  const float* wrow = &Ws[(64 * ch + i) * LS + 4 * g];
-  for (int64_t rb = static_cast<int64_t>(blockIdx.x) * 4 + rs; rb < n_rb; rb += static_cast<int64_t>(gridDim.x) * 4) {
-    const int64_t arow = rb * 16 + i;
-    float4 a[PD / 16];
-#pragma unroll
-    for (int q = 0; q < PD / 16; ++q)
-      a[q] = arow < p.m ? *reinterpret_cast<const float4*>(p.a + arow * p.lda + 16 * q + 4 * g)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    double sum[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sum[t][r] = 0.0;
-#pragma unroll
-    for (int kc = 0; kc < PD / 32; ++kc) {
-      // keeps each 32-k step's W reads within the step, so their registers are reused
-      __builtin_amdgcn_sched_barrier(0);
-      floatx4 acc[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) zero<4>(acc[t]);
-#pragma unroll
-      for (int q = 2 * kc; q < 2 * kc + 2; ++q) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float4 b = *reinterpret_cast<const float4*>(wrow + 16 * t * LS + 16 * q);
-          acc[t] = mfma16(a[q].x, b.x, acc[t]);
-          acc[t] = mfma16(a[q].y, b.y, acc[t]);
-          acc[t] = mfma16(a[q].z, b.z, acc[t]);
-          acc[t] = mfma16(a[q].w, b.w, acc[t]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sum[t][r] += static_cast<double>(acc[t][r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = rb * 16 + 4 * g + r;
-      if (row < p.m) {
-        float* dst = p.out + row * p.ldo + 64 * ch + i;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float v = static_cast<float>(sum[t][r]);
-          if (p.relu) v = v > 0.0f ? v : 0.0f;
-          dst[16 * t] = v;
-        }
-      }
-    }
   }
 }
 
@@ -607,17 +390,9 @@ size_t panel_bwd_workspace(int64_t m) {
 
 hipError_t launch_panel_fwd(const PanelArgs& p, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
-  if (QHA_PANEL_X3) {
-    const int64_t n_panels = (p.m + X3_PR - 1) / X3_PR;
-    const unsigned grid = static_cast<unsigned>(n_panels < kPanelBlocks ? n_panels : kPanelBlocks);
-    hipLaunchKernelGGL(panel_fwd_x3_kernel, dim3(grid), dim3(X3_NT), 0, s, p);
-  } else if (QHA_PANEL_FWD_RB) {
-    const int64_t slots = ((p.m + 15) / 16 + 3) / 4;
-    const unsigned grid = static_cast<unsigned>(slots < F2_BLOCKS ? slots : F2_BLOCKS);
-    hipLaunchKernelGGL(panel_fwd_rb_kernel, dim3(grid), dim3(F2_NT), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(panel_fwd_kernel, dim3(static_cast<unsigned>(panel_grid(p.m))), dim3(NT), 0, s, p);
-  }
+  const int64_t n_panels = (p.m + X3_PR - 1) / X3_PR;
+  const unsigned grid = static_cast<unsigned>(n_panels < kPanelBlocks ? n_panels : kPanelBlocks);
+  hipLaunchKernelGGL(panel_fwd_x3_kernel, dim3(grid), dim3(X3_NT), 0, s, p);
   return hipGetLastError();
 }
 
