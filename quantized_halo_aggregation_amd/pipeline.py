@@ -128,10 +128,11 @@ class GpuPartition:
         self.plan_fwd = mk(ptr)
         self.plan_bwd_halo = mk(colptr[n_in:])
         self.plan_bwd_inner = mk(colptr[:n_in + 1])
+        self.plan_bwd_all = mk(colptr)
         self.plan_mirror = mk(mc_ptr)
         self.plan_recv = mk(self.h_r_ptr)
         ws = max(p.workspace_bytes(d) for p in (self.plan_fwd, self.plan_bwd_halo, self.plan_bwd_inner,
-                                                 self.plan_mirror, self.plan_recv))
+                                                 self.plan_bwd_all, self.plan_mirror, self.plan_recv))
         self.agg_ws = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
         self.dense_ws = None
 
@@ -240,6 +241,13 @@ class GpuPartition:
                                 lay.word_offset, lay.bits, lay.classes, msg.meta, self.n_h, 0, out,
                                 workspace=self.agg_ws, row_ids=self.bnd_rows)
 
+    def aggregate_bwd_all(self, grad_out, dx_cols):
+        """a6 over every column in one launch: dx_cols [n_in + n_h, d] gets the inner columns'
+        gradients in rows 0 .. n_in - 1 and the halo columns' after them (no tail between two
+        launches; each row's sum is the same as in the two range calls)."""
+        B.aggregate_bwd(self.colptr, self.rowidx, self.w_bwd, self.plan_bwd_all, grad_out, self.n_in, 0, dx_cols,
+                        workspace=self.agg_ws)
+
     def aggregate_bwd_halo(self, grad_out, dx_halo):
         """a6 (halo range): gradients of the halo columns."""
         B.aggregate_bwd(self.colptr[self.n_in:], self.rowidx, self.w_bwd, self.plan_bwd_halo, grad_out, self.n_in, 0,
@@ -322,16 +330,28 @@ class LayerStack:
             self.X = [torch.from_numpy(x).to(dev)] + self.H[:-1]
         self.grad_top = torch.from_numpy(grad_top).to(dev)
         self.dA = [torch.empty(n_in, k_in, dtype=torch.float32, device=dev) for _ in range(self.L)]
+        # GCN without the fused or folded halo paths runs its transposed aggregation as one launch
+        # over all columns into [n_in + n_h, d]: the inner rows are dX, the halo rows the gradients
+        # to quantise (one buffer per layer, since layer l's may still be quantised on the second
+        # stream while layer l - 1 gathers)
+        self.one_bwd_gather = not sage and not fused_halo_bwd and not fold_received
+        self.dX_cols = []
         if sage:
             # dL/dh of layer l's input rows = the self half of dA, plus the transposed mean (added
             # in place), plus the received halo gradients
             self.dX = [self.dA[l][:, :d] for l in range(self.L)]
+        elif self.one_bwd_gather:
+            self.dX_cols = [torch.empty(n_in + gp.n_h, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
+            self.dX = [c[:n_in] for c in self.dX_cols]
         else:
             self.dX = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
         # halo gradient rows before quantisation: one buffer, or one per layer when the quantisation
         # of layer l may still run on the second stream while layer l-1 gathers
-        n_halo_bufs = 0 if fused_halo_bwd else (self.L if pipelined else 1)
-        self.dX_halo = [torch.empty(gp.n_h, d, dtype=torch.float32, device=dev) for _ in range(n_halo_bufs)]
+        if self.one_bwd_gather:
+            self.dX_halo = [c[n_in:] for c in self.dX_cols]
+        else:
+            n_halo_bufs = 0 if fused_halo_bwd else (self.L if pipelined else 1)
+            self.dX_halo = [torch.empty(gp.n_h, d, dtype=torch.float32, device=dev) for _ in range(n_halo_bufs)]
         n_slots = 2 if pipelined else 1
         # message buffers sized for the current widths, or for any widths up to max_bits
         cap = gp.words_at(max_bits) if max_bits else 0
@@ -393,8 +413,12 @@ class LayerStack:
                 self._on_comm(send)
         else:
             buf = self.dX_halo[l if len(self.dX_halo) > 1 else 0]
-            gp.aggregate_bwd_halo(g, buf)
-            if hook: hook("aggregate_bwd_halo", l)
+            if self.one_bwd_gather:
+                gp.aggregate_bwd_all(g, self.dX_cols[l])
+                if hook: hook("aggregate_bwd", l)
+            else:
+                gp.aggregate_bwd_halo(g, buf)
+                if hook: hook("aggregate_bwd_halo", l)
             send = lambda: gp.quantize_send(buf, None, msg, epoch, stream_id, self.seed)
             if sync:
                 send()
@@ -403,7 +427,10 @@ class LayerStack:
                 self._on_comm(send)
         received = msg if sync else self.msg_b[l][1 - slot]
         beta = 1 if self.sage else 0
-        if self.fold_received:
+        if self.one_bwd_gather:
+            gp.add_received(received, self.dX[l])
+            if hook: hook("add_received", l)
+        elif self.fold_received:
             gp.aggregate_bwd_inner_received(g, received, self.dX[l], beta)
             if hook: hook("aggregate_bwd_inner_received", l)
         else:
