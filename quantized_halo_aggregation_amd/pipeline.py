@@ -316,18 +316,34 @@ class LayerStack:
         sage = gp.model == "sage"
         self.sage = sage
         k_in = 2 * d if sage else d
+        n_slots = 2 if pipelined else 1
+        # message buffers sized for the current widths, or for any widths up to max_bits
+        cap = gp.words_at(max_bits) if max_bits else 0
+        words = max(gp.total_words, cap, 1)
+        # Layer l's input rows and its forward messages share one allocation (and each layer's
+        # backward messages another), so that the forward gather finds x, the codes and the
+        # (min, scale) pairs within 4 GiB of one base and addresses them from it.
+        xs = n_in * (k_in if sage else d)
+        fwd = [self._arena([("x", xs)] + [(f"c{t}", words) for t in range(n_slots)] +
+                           [(f"m{t}", 2 * gp.n_h) for t in range(n_slots)]) for _ in range(self.L)]
+        bwd = [self._arena([(f"c{t}", words) for t in range(n_slots)] +
+                           [(f"m{t}", 2 * gp.n_h) for t in range(n_slots)]) for _ in range(self.L)]
+        msgs = lambda ar, t: Messages(ar[f"c{t}"].view(torch.int32), ar[f"m{t}"].view(gp.n_h, 2))
+        self.msg_f = [[msgs(fwd[l], t) for t in range(n_slots)] for l in range(self.L)]
+        self.msg_b = [[msgs(bwd[l], t) for t in range(n_slots)] for l in range(self.L)]
         # activations: A_l is layer l's aggregated input ([n, 2d] for SAGE with the self half
         # first), H_l its output.  For SAGE, H_{l-1} is the left half of A_l.
         if sage:
-            self.A = [torch.empty(n_in, k_in, dtype=torch.float32, device=dev) for _ in range(self.L)]
+            self.A = [fwd[l]["x"].view(n_in, k_in) for l in range(self.L)]
             self.A[0][:, :d].copy_(torch.from_numpy(x).to(dev))
             self.H = [self.A[l + 1][:, :d] for l in range(self.L - 1)] + \
                      [torch.empty(n_in, d, dtype=torch.float32, device=dev)]
             self.X = [self.A[0][:, :d]] + self.H[:-1]
         else:
             self.A = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
-            self.H = [torch.empty(n_in, d, dtype=torch.float32, device=dev) for _ in range(self.L)]
-            self.X = [torch.from_numpy(x).to(dev)] + self.H[:-1]
+            self.X = [fwd[l]["x"].view(n_in, d) for l in range(self.L)]
+            self.X[0].copy_(torch.from_numpy(x).to(dev))
+            self.H = self.X[1:] + [torch.empty(n_in, d, dtype=torch.float32, device=dev)]
         self.grad_top = torch.from_numpy(grad_top).to(dev)
         self.dA = [torch.empty(n_in, k_in, dtype=torch.float32, device=dev) for _ in range(self.L)]
         # GCN without the fused or folded halo paths runs its transposed aggregation as one launch
@@ -352,17 +368,21 @@ class LayerStack:
         else:
             n_halo_bufs = 0 if fused_halo_bwd else (self.L if pipelined else 1)
             self.dX_halo = [torch.empty(gp.n_h, d, dtype=torch.float32, device=dev) for _ in range(n_halo_bufs)]
-        n_slots = 2 if pipelined else 1
-        # message buffers sized for the current widths, or for any widths up to max_bits
-        cap = gp.words_at(max_bits) if max_bits else 0
-        self.msg_f = [[gp.new_messages(cap) for _ in range(n_slots)] for _ in range(self.L)]
-        self.msg_b = [[gp.new_messages(cap) for _ in range(n_slots)] for _ in range(self.L)]
         self.msg_epoch = [None] * n_slots          # epoch whose messages each slot holds
         self.comm = torch.cuda.Stream(device=dev) if (pipelined or split_interior) else None
         # split-row partials of the gather that runs on the second stream (the compute stream's
         # gathers keep using the partition's workspace meanwhile)
         self.comm_ws = torch.empty_like(gp.agg_ws) if (pipelined and fused_halo_bwd) else None
         self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), backward=(n_in, d, k_in))
+
+    def _arena(self, parts):
+        """One float32 allocation cut into named 1-D views (each at a 256-byte boundary)."""
+        offs, total = [], 0
+        for _, n in parts:
+            offs.append(total)
+            total += -(-n // 64) * 64
+        buf = torch.empty(max(total, 64), dtype=torch.float32, device=self.gp.device)
+        return {name: buf[o:o + n] for (name, n), o in zip(parts, offs)}
 
     def _on_comm(self, fn):
         """Runs fn on the second stream once the compute stream's work so far is done."""
