@@ -16,15 +16,16 @@
 
 namespace qha {
 
-// Philox4x32-10: ten rounds of the 4x32 S-box with the Weyl key schedule.
+// Philox4x32-10: ten rounds of the 4x32 S-box with the Weyl key schedule.  Each round's two
+// three-way xors are one gfx950 three-input bit operation each (truth table 0x96 = a ^ b ^ c).
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
                                               uint32_t k1) {
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
     const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
     const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
-    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3, k1, 0x96);
     c1 = static_cast<uint32_t>(p1);
     c3 = static_cast<uint32_t>(p0);
     c0 = n0;
@@ -61,14 +62,14 @@ __device__ __forceinline__ RowScale row_scale(float mn, float mx, uint32_t b) {
 }
 
 // The code of one value: floor of y = (v - min) * inv, plus one when the 16-bit draw is below the
-// fractional part of y (times 2^16), clamped to L.
+// fractional part of y (times 2^16), clamped to L.  y >= +0 (v >= min, inv >= 0), so truncation
+// is its floor and the hardware fraction y - floor(y) is exact.
 __device__ __forceinline__ uint32_t code_of(float v, float mn, const RowScale& r, uint32_t u16) {
   const float t = v - mn;
   const float y = t * r.inv;
-  const float f = floorf(y);
-  const float fr = y - f;
+  const float fr = __builtin_amdgcn_fractf(y);
   const uint32_t up = (static_cast<float>(u16) < fr * 65536.0f) ? 1u : 0u;
-  uint32_t q = static_cast<uint32_t>(f) + up;
+  uint32_t q = static_cast<uint32_t>(y) + up;
   q = q > r.levels ? r.levels : q;
   return r.flat ? 0u : q;
 }

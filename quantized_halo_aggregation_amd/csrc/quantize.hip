@@ -4,12 +4,14 @@
 // (h - min) / scale, min travels as the zero-point).  Layout of a packed row: ceil(d*b/32)
 // words, code j at bit j*b, LSB first (raw float32 words for b = 32).
 //
-// Mapping to gfx950: a row of d features is owned by d/8 lanes, each holding 8 consecutive
-// features (two 16-byte loads).  One Philox4x32-10 call per lane yields the eight 16-bit rounding
-// thresholds of its features, so the generator is paid once per 8 elements.  Row min/max come
-// from a butterfly over the row's lanes; codes are packed in registers and neighbouring lanes'
-// pieces are merged with lane shuffles (1- and 2-bit rows), so every word is written once.
-// d = 128 gives 16 lanes per row and four rows per wavefront.
+// Mapping to gfx950: a row of d features is owned by d/16 lanes, each holding 16 consecutive
+// features (four 16-byte loads).  Two Philox4x32-10 calls per lane yield the sixteen 16-bit
+// rounding thresholds of its features, so the generator is paid once per 8 elements, and the
+// per-row work every lane of a row repeats (the min / max butterfly, the scale's two rounded
+// divisions, the width lookup) is shared by 16 features.  Codes are packed in registers (16 b
+// bits a lane, whole words for b >= 2) and pairs of lanes' halves are merged with a lane shuffle
+// for 1-bit rows, so every word is written once.  d = 128 gives 8 lanes per row and eight rows
+// per wavefront.
 #include "qha_internal.hpp"
 #include "quant_common.hpp"
 
@@ -18,114 +20,154 @@
 namespace qha {
 namespace {
 
+// min / max over the G lanes of a row (G = 1, 2, 4, 8, 16, 32; rows start at lanes that are
+// multiples of G).  Lanes 1 and 2 apart through DPP quad permutes, then the mirrored lane of the
+// half row (8 lanes) and of the row (16 lanes): after the quad steps every lane of a quad holds
+// its quad's value, so the mirror pairs each lane with the other quad (half).  32 lanes: a swap
+// of the two 16-lane halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+template <int G>
+__device__ __forceinline__ void row_min_max(float& mn, float& mx) {
+  constexpr int kXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+  constexpr int kXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+  constexpr int kHalfMirror = 0x141;
+  constexpr int kMirror = 0x140;
+  if constexpr (G >= 2) { mn = fminf(mn, dpp_f<kXor1>(mn)); mx = fmaxf(mx, dpp_f<kXor1>(mx)); }
+  if constexpr (G >= 4) { mn = fminf(mn, dpp_f<kXor2>(mn)); mx = fmaxf(mx, dpp_f<kXor2>(mx)); }
+  if constexpr (G >= 8) { mn = fminf(mn, dpp_f<kHalfMirror>(mn)); mx = fmaxf(mx, dpp_f<kHalfMirror>(mx)); }
+  if constexpr (G >= 16) { mn = fminf(mn, dpp_f<kMirror>(mn)); mx = fmaxf(mx, dpp_f<kMirror>(mx)); }
+  if constexpr (G >= 32) { mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16)); }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
-  constexpr int G = D / 8;      // lanes per row
-  constexpr int RPW = 64 / G;   // rows per wavefront
+  constexpr int F = 16;          // features per lane: two Philox calls
+  static_assert(D % F == 0 && D / F <= 32, "d = 16 .. 512");
+  constexpr int G = D / F;       // lanes per row
+  constexpr int RPW = 64 / G;    // rows per wavefront
   const int lane = threadIdx.x & 63;
   const int gl = lane % G;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t r = wave * RPW + lane / G;
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wib) * RPW;   // wave's first row
+  const int64_t r = r0 + lane / G;
   const bool valid = r < a.n_rows;
 
-  float v[8];
-  uint32_t b = 0;
-  uint32_t row_off = 0;
-  if (valid) {
-    const int64_t src = a.row_index ? static_cast<int64_t>(a.row_index[r]) : r;
-    const float4* p = reinterpret_cast<const float4*>(a.x + src * a.ldx + gl * 8);
-    const float4 lo = p[0];
-    const float4 hi = p[1];
-    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    if (a.cls.n > 0) {
-      // width-grouped buffer: the row's class, width and first word by arithmetic
-      int32_t st = a.cls.start[0];
-      uint32_t base = a.cls.base[0];
-      b = static_cast<uint32_t>(a.cls.bits[0]);
+  // lanes past the last row work on the last row and store nothing
+  const int64_t rc = valid ? r : a.n_rows - 1;
+  float v[F];
+  {
+    const int64_t src = a.row_index ? static_cast<int64_t>(a.row_index[rc]) : rc;
+    const float4* p = reinterpret_cast<const float4*>(a.x + src * a.ldx + gl * F);
 #pragma unroll
-      for (int c = 1; c < kMaxClasses; ++c) {
-        if (c < a.cls.n && r >= a.cls.start[c]) {
+    for (int q = 0; q < F / 4; ++q) {
+      const float4 t = p[q];
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+  }
+  uint32_t b, row_off;
+  if (a.cls.n > 0) {
+    // width-grouped buffer (fewer than 2^31 rows): the class of the wave's first row from scalar
+    // compares; a wave whose rows cross into the next class looks its rows up one by one
+    const int32_t w0 = static_cast<int32_t>(r0);
+    const int32_t wl = w0 + (RPW - 1);
+    int32_t st = a.cls.start[0];
+    uint32_t base = a.cls.base[0];
+    int32_t bb = a.cls.bits[0];
+    bool straddle = false;
+#pragma unroll
+    for (int c = 1; c < kMaxClasses; ++c) {
+      if (c < a.cls.n) {
+        if (w0 >= a.cls.start[c]) {
           st = a.cls.start[c];
           base = a.cls.base[c];
-          b = static_cast<uint32_t>(a.cls.bits[c]);
+          bb = a.cls.bits[c];
+        } else if (wl >= a.cls.start[c]) {
+          straddle = true;
         }
       }
-      const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (b * static_cast<uint32_t>(D) + 31u) >> 5;
-      row_off = base + static_cast<uint32_t>(r - st) * words;
-    } else {
-      b = a.bits[r];
-      row_off = a.word_offset[r];
     }
-  } else {
+    const int32_t r32 = static_cast<int32_t>(rc);
+    if (straddle) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      for (int c = 1; c < kMaxClasses; ++c) {
+        if (c < a.cls.n && r32 >= a.cls.start[c]) {
+          st = a.cls.start[c];
+          base = a.cls.base[c];
+          bb = a.cls.bits[c];
+        }
+      }
+    }
+    b = static_cast<uint32_t>(bb);
+    const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (b * static_cast<uint32_t>(D) + 31u) >> 5;
+    row_off = base + static_cast<uint32_t>(r32 - st) * words;
+  } else {
+    b = a.bits[rc];
+    row_off = a.word_offset[rc];
   }
 
-  // exact min / max of the row: in-lane, then a butterfly over the row's G lanes
+  // exact min / max of the row: in-lane, then across the row's G lanes
   float mn = v[0], mx = v[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
+  for (int i = 1; i < F; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off));
-    mx = fmaxf(mx, __shfl_xor(mx, off));
-  }
+  row_min_max<G>(mn, mx);
 
   const bool active = valid && width_valid(b);
   const bool raw = b == 32u;
-  uint32_t lo_w = 0, hi_w = 0;
+  // the lane's 16 codes in four groups: code 4k + i at bit i b of acc[k]
+  uint32_t acc[4] = {0u, 0u, 0u, 0u};
   float sc = 0.0f, zp = 0.0f;
   if (active && !raw) {
     const RowScale rs = row_scale(mn, mx, b);
     zp = rs.zp;
     sc = rs.sc;
-    uint32_t c0 = a.node_base + static_cast<uint32_t>(r);
-    uint32_t c1 = static_cast<uint32_t>(gl);          // this lane's 8 features are group gl
-    uint32_t c2 = a.epoch;
-    uint32_t c3 = a.stream_id;
-    philox4x32_10(c0, c1, c2, c3, a.seed_lo, a.seed_hi);
-    const uint32_t w[4] = {c0, c1, c2, c3};
+    const uint32_t sh[4] = {0u, b, 2u * b, 3u * b};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t q = code_of(v[i], mn, rs, draw16(w, i));
-      const uint32_t pos = static_cast<uint32_t>(i) * b;       // < 64
-      if (pos < 32u) lo_w |= q << pos;
-      else hi_w |= q << (pos - 32u);
+    for (int h = 0; h < 2; ++h) {
+      // features 16 gl + 8 h .. +7 are group 2 gl + h
+      uint32_t c0 = a.node_base + static_cast<uint32_t>(r);
+      uint32_t c1 = static_cast<uint32_t>(2 * gl + h);
+      uint32_t c2 = a.epoch;
+      uint32_t c3 = a.stream_id;
+      philox4x32_10(c0, c1, c2, c3, a.seed_lo, a.seed_hi);
+      const uint32_t w[4] = {c0, c1, c2, c3};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = 8 * h + i;
+        const uint32_t q = code_of(v[j], mn, rs, draw16(w, i));
+        acc[j >> 2] |= q << sh[j & 3];
+      }
     }
   }
-
-  // merge 8- and 16-bit lane pieces into whole words (all lanes take part in the shuffles)
-  const uint32_t n1 = __shfl_down(lo_w, 1);
-  const uint32_t n2 = __shfl_down(lo_w, 2);
-  const uint32_t n3 = __shfl_down(lo_w, 3);
+  // b = 4: words lo, hi; b <= 2: one word of 16 b bits (shifts wrap where the result is unused)
+  const uint32_t t4 = (4u * b) & 31u;
+  const uint32_t lo = acc[0] | (acc[1] << t4);
+  const uint32_t hi = acc[2] | (acc[3] << t4);
+  const uint32_t one = lo | (hi << ((2u * t4) & 31u));
+  // 1-bit rows: a lane's codes fill half a word; the even lane takes its odd neighbour's half
+  const uint32_t nb = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(one), 0xB1, 0xF, 0xF, true));
   if (!active) return;
 
   uint32_t* row_codes = a.codes + row_off;
   if (raw) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) row_codes[gl * 8 + i] = __float_as_uint(v[i]);
+    for (int i = 0; i < F; ++i) row_codes[gl * F + i] = __float_as_uint(v[i]);
   } else if (b == 8u) {
-    row_codes[2 * gl] = lo_w;
-    row_codes[2 * gl + 1] = hi_w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) row_codes[4 * gl + k] = acc[k];
   } else if (b == 4u) {
-    row_codes[gl] = lo_w;
+    row_codes[2 * gl] = lo;
+    row_codes[2 * gl + 1] = hi;
   } else if (b == 2u) {
-    if ((gl & 1) == 0) {
-      const uint32_t up1 = (gl + 1 < G) ? n1 : 0u;
-      row_codes[gl >> 1] = lo_w | (up1 << 16);
-    }
+    row_codes[gl] = one;
   } else {  // b == 1
-    if ((gl & 3) == 0) {
-      uint32_t word = lo_w;
-      if (gl + 1 < G) word |= n1 << 8;
-      if (gl + 2 < G) word |= n2 << 16;
-      if (gl + 3 < G) word |= n3 << 24;
-      row_codes[gl >> 2] = word;
-    }
+    if ((gl & 1) == 0) row_codes[gl >> 1] = one | ((gl + 1 < G) ? nb << 16 : 0u);
   }
   if (gl == 0) *reinterpret_cast<float2*>(a.meta + 2 * r) = make_float2(zp, sc);   // (min, scale)
 }
@@ -146,7 +188,7 @@ __global__ __launch_bounds__(256) void degree_norm_kernel(const int32_t* deg, in
 
 template <int D>
 hipError_t launch_quantize_d(const QuantArgs& a, hipStream_t s) {
-  constexpr int RPB = 4 * (64 / (D / 8));   // rows per 256-thread block
+  constexpr int RPB = 4 * (64 / (D / 16));  // rows per 256-thread block
   const int64_t blocks = (a.n_rows + RPB - 1) / RPB;
   hipLaunchKernelGGL(quantize_pack_kernel<D>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -156,6 +198,7 @@ hipError_t launch_quantize_d(const QuantArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize(const QuantArgs& a, int32_t d, hipStream_t s) {
   if (a.n_rows == 0) return hipSuccess;
+  if (a.cls.n > 0 && a.n_rows > INT32_MAX) return hipErrorInvalidValue;   // class rows are 32-bit
   switch (d) {
     case 16: return launch_quantize_d<16>(a, s);
     case 32: return launch_quantize_d<32>(a, s);
