@@ -13,7 +13,7 @@
  *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
  *   qha_aggregate_bwd_quantize the same over the halo columns, quantising each gradient row
  *   qha_dense_project         the dense projection (float32 products on matrix cores) with ReLU
- *   qha_dense_backward        its gradients dA and dW in one pass
+ *   qha_dense_backward        its gradients dA and dW in one pass (float32 products on matrix cores)
  *
  * plus small set-up helpers.  Conventions shared by every entry point:
  *   - Array arguments are caller-owned.  Pointers documented as "device" must be HIP device
@@ -286,11 +286,13 @@ size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, 
  * (ldw); dA: device [m x k] (ldda), overwritten; dW: device [n x k] (lddw), overwritten (zeros
  * when m = 0).  Leading dimensions are multiples of 4 and at least the row width; dH, H, A and W
  * are 16-byte aligned.  dA must not overlap dH, H, A or W.  For n = k = 128 the operands are read
- * once: W stays in on-chip memory while 64-row panels stream through, dZ is formed once and used
- * for both products, and per-block dW partials (workspace) are added in a fixed order.  Other
- * widths run as the two qha_dense_project products.  dA sums are fp32 matrix-core chains of 32
- * products added in float64; dW adds fp32 chains over each block's rows in float64.  workspace:
- * device, 16-byte aligned, qha_dense_backward_workspace bytes.  Results are deterministic.
+ * once: 32-row panels stream through on-chip memory, dZ is formed once and used for both
+ * products, both products run on the bf16 matrix cores with the three-way split of
+ * qha_dense_project's width-128 forward (W's parts held on chip), and per-block dW partials
+ * (workspace) are added in a fixed order.  Other widths run as the two qha_dense_project
+ * products.  dA sums are chains of 32 products accumulated in float32 and added in float64; dW
+ * adds float32 sums over each block's rows in float64.  workspace: device, 16-byte aligned,
+ * qha_dense_backward_workspace bytes.  Results are deterministic.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */
 int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t ldg, const float* h, int64_t ldh,
                        const float* a, int64_t lda, const float* w, int64_t ldw, float* da, int64_t ldda,

@@ -5,22 +5,15 @@
 // gradient sums (dL/dh_v * sigma'(z_v)) a_v^T over the rows).
 //
 // Mapping to gfx950: the tall operands have m rows (a partition's nodes, 10^5..10^6) and 128
-// columns; W is 128 x 128 (64 KB).
-// Forward (panel_fwd_x3_kernel): float32 products on the bf16 matrix cores.  Each operand is split
-// into three bf16 parts and each product is rebuilt from the six part products that matter (the
-// split and the error bound are at split3); W's parts stay in registers, A is streamed through LDS
-// as three bf16 planes of 64-row panels, double-buffered, with v_mfma_f32_32x32x16_bf16.
-// Backward (panel_bwd_kernel): one 1024-thread block per compute unit keeps W in LDS for the whole
-// launch and streams 64-row panels of dH, H and A through LDS, loading the next panel into
-// registers while the matrix cores work on the current one; sixteen wavefronts (four per SIMD)
-// hide each other's LDS latency.  Each wavefront owns two 16 x 16 tiles of dA
-// (v_mfma_f32_16x16x4f32) and one 32 x 32 tile of dW (v_mfma_f32_32x32x2f32), which stays in
-// registers across all of the block's panels, so dH, H and A are each read once and dZ is formed
-// once.  Operand reads: a lane that walks a row along the contraction takes four consecutive
-// values with one 16-byte LDS read and feeds them to four consecutive MFMAs (the lane groups take
-// interleaved k ranges); a lane that walks a column reads one float per MFMA, the lane groups far
-// enough apart in rows that the reads hit distinct banks (row strides of 136 and 132 floats,
-// measured free of bank conflicts for these patterns).
+// columns; W is 128 x 128 (64 KB).  Both kernels compute float32 products on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16): each float32 operand is split exactly into three bf16 parts
+// and each product is rebuilt from the six part products that matter (the split and the error
+// bound are at split3).  One block per compute unit, persistent over row panels staged in LDS.
+// Forward (panel_fwd_x3_kernel): W's parts stay in registers; A is streamed through LDS as three
+// bf16 planes of 64-row panels, double-buffered.
+// Backward (panel_bwd_x3_kernel): dZ and A are staged per 32-row panel; four wavefronts form dA
+// (W's parts in registers, as in the forward) while four form the block's dW partial, so dH, H
+// and A are each read once and dZ is formed once.
 // Precision: for the forward and dA each MFMA chain adds 32 k-steps in float32 and those partial
 // sums are added in float64.  A block's dW tiles are float32 MFMA sums over its panels' rows
 // (about m/256 rows); a second kernel adds the blocks' partials in float64 in a fixed order, so
@@ -31,59 +24,13 @@ namespace qha {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-constexpr int PR = 64;             // rows per panel
+constexpr int PR = 64;             // rows per grid unit: the backward's grid is min(ceil(m / 64), 256)
 constexpr int PD = 128;            // n = k = 128
-// LDS row strides (floats), chosen by bank: a 16-byte read by lane (g, i) at row i, column 4g is
-// conflict-free at a stride of 136; a 4-byte read whose lane groups sit 4 rows apart at column i
-// (W in the backward) needs 132
-constexpr int LS = PD + 8;
-constexpr int LSW = PD + 4;
-constexpr int NT = 1024;           // threads per block: 16 wavefronts, four per SIMD
-constexpr int SV = PR * PD / 4 / NT;   // float4 per thread per staged panel array (2)
-constexpr int WV = PD * PD / 4 / NT;   // float4 per thread for W (4)
-
-__device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <int N>
 __device__ __forceinline__ void zero(float __attribute__((ext_vector_type(N)))& v) {
 #pragma unroll
   for (int r = 0; r < N; ++r) v[r] = 0.0f;
-}
-
-// Rows [r0, r0 + PR) of a [m x 128] row-major matrix, float4 f = tid + NT*s at (row f/32, col 4*(f%32));
-// rows at or past m read as zero.
-__device__ __forceinline__ void load_panel(const float* p, int64_t ld, int64_t m, int64_t r0, float4 (&v)[SV]) {
-#pragma unroll
-  for (int s = 0; s < SV; ++s) {
-    const int f = static_cast<int>(threadIdx.x) + NT * s;
-    const int64_t r = r0 + (f >> 5);
-    v[s] = r < m ? *reinterpret_cast<const float4*>(p + r * ld + 4 * (f & 31)) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-__device__ __forceinline__ void store_panel(float* lds, const float4 (&v)[SV]) {
-#pragma unroll
-  for (int s = 0; s < SV; ++s) {
-    const int f = static_cast<int>(threadIdx.x) + NT * s;
-    *reinterpret_cast<float4*>(&lds[(f >> 5) * LS + 4 * (f & 31)]) = v[s];
-  }
-}
-
-template <int STRIDE>
-__device__ __forceinline__ void load_w(float* lds, const float* w, int64_t ldw) {
-#pragma unroll
-  for (int s = 0; s < WV; ++s) {
-    const int f = static_cast<int>(threadIdx.x) + NT * s;
-    *reinterpret_cast<float4*>(&lds[(f >> 5) * STRIDE + 4 * (f & 31)]) =
-        *reinterpret_cast<const float4*>(w + static_cast<int64_t>(f >> 5) * ldw + 4 * (f & 31));
-  }
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -100,27 +47,35 @@ __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16&
   lo = static_cast<__bf16>(r - static_cast<float>(mid));
 }
 
+// split3 of a pair (a, b), as packed words (a in the low half): one packed conversion rounds the
+// pair to bf16, and the pair's float values come back by a shift and a mask of the packed word.
+// Bit for bit the same parts as split3.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& ph, uint32_t& pm, uint32_t& pl) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  ph = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){a, b}, bf16x2));
+  const float ra = a - __uint_as_float(ph << 16);
+  const float rb = b - __uint_as_float(ph & 0xFFFF0000u);
+  pm = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){ra, rb}, bf16x2));
+  const float la = ra - __uint_as_float(pm << 16);
+  const float lb = rb - __uint_as_float(pm & 0xFFFF0000u);
+  pl = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){la, lb}, bf16x2));
+}
+
 __device__ __forceinline__ floatx16 mfma32b(const bf16x8& a, const bf16x8& b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Stages 4 floats of a panel row (row r, columns c .. c + 3) as the three bf16 planes.
+// Stages 4 floats of a panel row (row r, columns c .. c + 3) as the three bf16 planes of ROWS rows.
+template <int ROWS = 64>
 __device__ __forceinline__ void stage4(__bf16* planes, int r, int c, const float4& v) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 h, m, l;
-  const float x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __bf16 a, b, d;
-    split3(x[j], a, b, d);
-    h[j] = a;
-    m[j] = b;
-    l[j] = d;
-  }
+  uint2 h, m, l;
+  split_pair(v.x, v.y, h.x, m.x, l.x);
+  split_pair(v.z, v.w, h.y, m.y, l.y);
   const int o = r * X3_LS + c;
-  *reinterpret_cast<bf16x4*>(planes + o) = h;
-  *reinterpret_cast<bf16x4*>(planes + X3_PR * X3_LS + o) = m;
-  *reinterpret_cast<bf16x4*>(planes + 2 * X3_PR * X3_LS + o) = l;
+  *reinterpret_cast<uint2*>(planes + o) = h;
+  *reinterpret_cast<uint2*>(planes + ROWS * X3_LS + o) = m;
+  *reinterpret_cast<uint2*>(planes + 2 * ROWS * X3_LS + o) = l;
 }
 
 // H = epi(A W^T) on the bf16 matrix cores.  Every float32 operand is split into three bf16 parts
@@ -234,117 +189,228 @@ __global__ __launch_bounds__(X3_NT) void panel_fwd_x3_kernel(PanelArgs p) {
   }
 }
 
-// dZ = dH * [H > 0]; dA = dZ W; per-block dW partial = dZ^T A to ws[block][128][128].
-// Wavefront w: dA rows 16*(w/4) .. +15, columns 32*(w%4) .. +31 as two 16 x 16 tiles (contraction
-// over n = 16q + 4g + c); dW tile rows 32*(w/4) .., columns 32*(w%4) .. (32 x 32, contraction over
-// the panel's rows p = 16s + 8h + c, lane halves eight rows apart).
-__global__ __launch_bounds__(NT) void panel_bwd_kernel(PanelArgs p) {
-  __shared__ __attribute__((aligned(16))) float Ws[PD * LSW];
-  __shared__ __attribute__((aligned(16))) float Zs[PR * LS];
-  __shared__ __attribute__((aligned(16))) float As[PR * LS];
+// Backward on the bf16 matrix cores (same split and the same six part products as the forward).
+// One 512-thread block per compute unit, persistent over 32-row panels staged in double-buffered
+// LDS: dZ = dH [H > 0] and A in float32 (row stride 140 floats, so that the 4-byte column reads
+// of the dW operands hit distinct banks) and dZ's three bf16 planes for the dA operand.  Every
+// thread loads its share of the next panel (dH, H, A) into registers during the products and
+// stages it after the panel's one barrier.  The wavefronts split the products by role, one of
+// each per SIMD:
+//  - wavefronts 0-3 form dA = dZ W for 32 output columns each: W's parts for those columns stay
+//    in registers (lane (h, l) holds W[16 s + 8 h + j][32 c + l]) and each 32-k chain is folded
+//    into float64;
+//  - wavefronts 4-7 form a 64 x 64 quarter of the block's dW partial = dZ^T A (four 32 x 32
+//    tiles; operands read down the panel's float32 columns and split as they are read),
+//    accumulated in float32 across the block's panels like the float32 kernel's.
+constexpr int BX_PR = 32;           // rows per panel
+constexpr int BX_LS = 140;          // floats per staged row
+constexpr int BX_NT = 512;
+constexpr int kBxBufferWord3 = 0x00020000;   // raw buffer, 32-bit data: out-of-range stores dropped
+constexpr int BX_SV = BX_PR * PD / 4 / BX_NT;   // float4 per thread per staged array (2)
+
+// split3 of eight values, two at a time
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 wh, wm, wl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t a, b, d;
+    split_pair(x[2 * k], x[2 * k + 1], a, b, d);
+    wh[k] = a;
+    wm[k] = b;
+    wl[k] = d;
+  }
+  hi = __builtin_bit_cast(bf16x8, wh);
+  mid = __builtin_bit_cast(bf16x8, wm);
+  lo = __builtin_bit_cast(bf16x8, wl);
+}
+
+// c += a b over the six part products, smallest first
+__device__ __forceinline__ floatx16 mfma6(const bf16x8& ah, const bf16x8& am, const bf16x8& al, const bf16x8& bh,
+                                          const bf16x8& bm, const bf16x8& bl, floatx16 c) {
+  c = mfma32b(am, bm, c);
+  c = mfma32b(al, bh, c);
+  c = mfma32b(ah, bl, c);
+  c = mfma32b(am, bh, c);
+  c = mfma32b(ah, bm, c);
+  return mfma32b(ah, bh, c);
+}
+
+// Thread tid's share of panel pn: float4 f = tid + 512 s at (row f / 32, column 4 (f % 32)).  Rows
+// at or past m are read from row m - 1 (no branches around the loads) and staged as zero.
+__device__ __forceinline__ void bx_load(const float* dh, int64_t lddh, const float* hp, int64_t ldh, const float* ap,
+                                        int64_t lda, int64_t m, int64_t pn, int tid, float4 (&g)[BX_SV],
+                                        float4 (&hh)[BX_SV], float4 (&a)[BX_SV]) {
+#pragma unroll
+  for (int sv = 0; sv < BX_SV; ++sv) {
+    const int f = tid + BX_NT * sv;
+    int64_t r = pn * BX_PR + (f >> 5);
+    r = r < m ? r : m - 1;
+    const int c = 4 * (f & 31);
+    g[sv] = *reinterpret_cast<const float4*>(dh + r * lddh + c);
+    hh[sv] = *reinterpret_cast<const float4*>(hp + r * ldh + c);
+    a[sv] = *reinterpret_cast<const float4*>(ap + r * lda + c);
+  }
+}
+
+__device__ __forceinline__ void bx_stage(float* zs, float* as, __bf16* zp, int64_t m, int64_t pn, int tid, const float4 (&g)[BX_SV],
+                                         const float4 (&hh)[BX_SV], const float4 (&a)[BX_SV]) {
+#pragma unroll
+  for (int sv = 0; sv < BX_SV; ++sv) {
+    const int f = tid + BX_NT * sv;
+    const int o = (f >> 5) * BX_LS + 4 * (f & 31);
+    const bool in = pn * BX_PR + (f >> 5) < m;
+    float4 z, x;
+    z.x = in && hh[sv].x > 0.0f ? g[sv].x : 0.0f;
+    z.y = in && hh[sv].y > 0.0f ? g[sv].y : 0.0f;
+    z.z = in && hh[sv].z > 0.0f ? g[sv].z : 0.0f;
+    z.w = in && hh[sv].w > 0.0f ? g[sv].w : 0.0f;
+    x.x = in ? a[sv].x : 0.0f;
+    x.y = in ? a[sv].y : 0.0f;
+    x.z = in ? a[sv].z : 0.0f;
+    x.w = in ? a[sv].w : 0.0f;
+    *reinterpret_cast<float4*>(zs + o) = z;
+    *reinterpret_cast<float4*>(as + o) = x;
+    stage4<BX_PR>(zp, f >> 5, 4 * (f & 31), z);
+  }
+}
+
+__global__ __launch_bounds__(BX_NT) void panel_bwd_x3_kernel(PanelArgs p) {
+  __shared__ __attribute__((aligned(16))) float Zs[2][BX_PR * BX_LS];
+  __shared__ __attribute__((aligned(16))) float As[2][BX_PR * BX_LS];
+  __shared__ __attribute__((aligned(16))) __bf16 Zp[2][3 * BX_PR * X3_LS];   // dZ's bf16 planes
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int g = lane >> 4;
-  const int i = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
-  const int l32 = lane & 31;
-  const int rt = wid >> 2;
-  const int cp = wid & 3;
-  const int64_t n_panels = (p.m + PR - 1) / PR;
-
-  load_w<LSW>(Ws, p.w, p.ldw);
-  floatx16 wacc;                 // the block's dW tile, over all of its panels
-  zero<16>(wacc);
-
-  float4 sg[SV], sh[SV], sa[SV];
+  const int l = lane & 31;
+  const int64_t n_panels = (p.m + BX_PR - 1) / BX_PR;
+  const int64_t grid = gridDim.x;
   int64_t panel = blockIdx.x;
-  if (panel < n_panels) {
-    load_panel(p.dh, p.lddh, p.m, panel * PR, sg);
-    load_panel(p.h, p.ldh, p.m, panel * PR, sh);
-    load_panel(p.a, p.lda, p.m, panel * PR, sa);
-  }
-  const float* zrow = &Zs[(16 * rt + i) * LS + 4 * g];
-  const float* wcol = &Ws[(4 * g) * LSW + 32 * cp + i];
-  const float* zcol = &Zs[(4 * h) * LS + 32 * rt + l32];
-  const float* acol = &As[(4 * h) * LS + 32 * cp + l32];
-  for (; panel < n_panels; panel += gridDim.x) {
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < SV; ++s) {
-      float4 z;
-      z.x = sh[s].x > 0.0f ? sg[s].x : 0.0f;
-      z.y = sh[s].y > 0.0f ? sg[s].y : 0.0f;
-      z.z = sh[s].z > 0.0f ? sg[s].z : 0.0f;
-      z.w = sh[s].w > 0.0f ? sg[s].w : 0.0f;
-      sg[s] = z;
-    }
-    store_panel(Zs, sg);
-    store_panel(As, sa);
-    __syncthreads();
-    const int64_t next = panel + gridDim.x;
-    if (next < n_panels) {
-      load_panel(p.dh, p.lddh, p.m, next * PR, sg);
-      load_panel(p.h, p.ldh, p.m, next * PR, sh);
-      load_panel(p.a, p.lda, p.m, next * PR, sa);
-    }
+  if (panel >= n_panels) return;
 
-    // dA tiles
-    double as0[4], as1[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) as0[r] = as1[r] = 0.0;
-#pragma unroll
-    for (int nc = 0; nc < PD / 32; ++nc) {
-      floatx4 acc0, acc1;
-      zero<4>(acc0);
-      zero<4>(acc1);
-#pragma unroll
-      for (int q = 2 * nc; q < 2 * nc + 2; ++q) {
-        const float4 z = *reinterpret_cast<const float4*>(zrow + 16 * q);
-        const float* wq = wcol + 16 * q * LSW;
-        acc0 = mfma16(z.x, wq[0 * LSW], acc0);
-        acc1 = mfma16(z.x, wq[0 * LSW + 16], acc1);
-        acc0 = mfma16(z.y, wq[1 * LSW], acc0);
-        acc1 = mfma16(z.y, wq[1 * LSW + 16], acc1);
-        acc0 = mfma16(z.z, wq[2 * LSW], acc0);
-        acc1 = mfma16(z.z, wq[2 * LSW + 16], acc1);
-        acc0 = mfma16(z.w, wq[3 * LSW], acc0);
-        acc1 = mfma16(z.w, wq[3 * LSW + 16], acc1);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        as0[r] += static_cast<double>(acc0[r]);
-        as1[r] += static_cast<double>(acc1[r]);
-      }
-    }
-    // stored before the dW work, which leaves that work to cover the stores' completion
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = panel * PR + 16 * rt + 4 * g + r;
-      if (row < p.m) {
-        float* dst = p.da + row * p.ldda + 32 * cp + i;
-        dst[0] = static_cast<float>(as0[r]);
-        dst[16] = static_cast<float>(as1[r]);
-      }
-    }
+  // the first panel staged, the second in flight
+  float4 pg[BX_SV], ph[BX_SV], pa[BX_SV];
+  bx_load(p.dh, p.lddh, p.h, p.ldh, p.a, p.lda, p.m, panel, tid, pg, ph, pa);
+  bx_stage(Zs[0], As[0], Zp[0], p.m, panel, tid, pg, ph, pa);
+  if (panel + grid < n_panels) bx_load(p.dh, p.lddh, p.h, p.ldh, p.a, p.lda, p.m, panel + grid, tid, pg, ph, pa);
+  int buf = 0;
 
-    // dW tile: lane half h takes the panel rows p = 8s + 4h + c
+  if (wid < 4) {
+    // ---- dA role: output columns 32 cb .. 32 cb + 31
+    const int cb = wid;
+    bf16x8 wh[PD / 16], wm[PD / 16], wl[PD / 16];
 #pragma unroll
-    for (int s = 0; s < PR / 8; ++s) {
+    for (int st = 0; st < PD / 16; ++st) {
+      float x[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int off = (8 * s + c) * LS;
-        wacc = mfma32(zcol[off], acol[off], wacc);
-      }
+      for (int j = 0; j < 8; ++j) x[j] = p.w[static_cast<int64_t>(16 * st + 8 * h + j) * p.ldw + 32 * cb + l];
+      split8(x, wh[st], wm[st], wl[st]);
     }
+    for (; panel < n_panels; panel += grid) {
+      __syncthreads();
+      const int64_t nxt = panel + grid;
+      if (nxt < n_panels) {
+        bx_stage(Zs[buf ^ 1], As[buf ^ 1], Zp[buf ^ 1], p.m, nxt, tid, pg, ph, pa);
+        if (nxt + grid < n_panels) bx_load(p.dh, p.lddh, p.h, p.ldh, p.a, p.lda, p.m, nxt + grid, tid, pg, ph, pa);
+      }
+      const __bf16* zp = Zp[buf];
+#pragma unroll
+      for (int rb = 0; rb < BX_PR / 32; ++rb) {
+        double sum[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] = 0.0;
+#pragma unroll
+        for (int kc = 0; kc < PD / 32; ++kc) {
+          floatx16 acc;
+          zero<16>(acc);
+#pragma unroll
+          for (int st = 2 * kc; st < 2 * kc + 2; ++st) {
+            const __bf16* zr = zp + (32 * rb + l) * X3_LS + 16 * st + 8 * h;
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(zr);
+            const bf16x8 xm = *reinterpret_cast<const bf16x8*>(zr + BX_PR * X3_LS);
+            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(zr + 2 * BX_PR * X3_LS);
+            acc = mfma6(xh, xm, xl, wh[st], wm[st], wl[st], acc);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum[r] += static_cast<double>(acc[r]);
+        }
+        // range-checked buffer stores: rows at or past m are dropped by the hardware, so the
+        // stores need no branches (and the next panel's load waits need not cover them)
+        const int64_t row0 = panel * BX_PR + 32 * rb;
+        const int64_t rows = p.m - row0 < 32 ? p.m - row0 : 32;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            p.da + row0 * p.ldda, 0, static_cast<int32_t>(rows * p.ldda * 4), kBxBufferWord3);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pr = 8 * (r >> 2) + 4 * h + (r & 3);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(static_cast<float>(sum[r])), rs,
+                                                static_cast<uint32_t>((pr * p.ldda + 32 * cb + l) * 4), 0, 0);
+        }
+      }
+      buf ^= 1;
+    }
+    return;
   }
 
+  // ---- dW role: wavefront q forms the tiles (o-block 2 (q / 2) + ot, i-block 2 (q % 2) + it)
+  const int q = wid - 4;
+  const int ob0 = 2 * (q >> 1);
+  const int ib0 = 2 * (q & 1);
+  floatx16 wacc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) zero<16>(wacc[k]);
+  for (; panel < n_panels; panel += grid) {
+    __syncthreads();
+    const int64_t nxt = panel + grid;
+    if (nxt < n_panels) {
+      bx_stage(Zs[buf ^ 1], As[buf ^ 1], Zp[buf ^ 1], p.m, nxt, tid, pg, ph, pa);
+      if (nxt + grid < n_panels) bx_load(p.dh, p.lddh, p.h, p.ldh, p.a, p.lda, p.m, nxt + grid, tid, pg, ph, pa);
+    }
+    const float* zb = Zs[buf];
+    const float* ab = As[buf];
+#pragma unroll
+    for (int ks = 0; ks < BX_PR / 16; ++ks) {
+      // lane half h takes the panel rows 16 ks + 8 h .. + 7
+      bf16x8 zh[2], zm[2], zl[2], ah[2], am[2], al[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float xz[8], xa[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int o = (16 * ks + 8 * h + j) * BX_LS + l;
+          xz[j] = zb[o + 32 * (ob0 + u)];
+          xa[j] = ab[o + 32 * (ib0 + u)];
+        }
+        split8(xz, zh[u], zm[u], zl[u]);
+        split8(xa, ah[u], am[u], al[u]);
+      }
+      // the four tiles' products interleaved, so that consecutive MFMAs are independent (each
+      // tile still takes its six products smallest first)
+#define QHA_DW_STEP(ZA, AB)                                                         \
+  _Pragma("unroll") for (int ot = 0; ot < 2; ++ot)                                  \
+  _Pragma("unroll") for (int it = 0; it < 2; ++it)                                  \
+      wacc[2 * ot + it] = mfma32b(ZA[ot], AB[it], wacc[2 * ot + it]);
+      QHA_DW_STEP(zm, am)
+      QHA_DW_STEP(zl, ah)
+      QHA_DW_STEP(zh, al)
+      QHA_DW_STEP(zm, ah)
+      QHA_DW_STEP(zh, am)
+      QHA_DW_STEP(zh, ah)
+#undef QHA_DW_STEP
+    }
+    buf ^= 1;
+  }
   float* part = p.ws + static_cast<int64_t>(blockIdx.x) * PD * PD;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int n = 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
-    part[n * PD + 32 * cp + l32] = wacc[r];
-  }
+  for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = 32 * (ob0 + ot) + 8 * (r >> 2) + 4 * h + (r & 3);
+        part[o * PD + 32 * (ib0 + it) + l] = wacc[2 * ot + it][r];
+      }
 }
 
 // dW = sum over blocks of the per-block partials in float64, in block order within four fixed
@@ -399,7 +465,7 @@ hipError_t launch_panel_fwd(const PanelArgs& p, hipStream_t s) {
 hipError_t launch_panel_bwd(const PanelArgs& p, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
   const int32_t grid = panel_grid(p.m);
-  hipLaunchKernelGGL(panel_bwd_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL(panel_bwd_x3_kernel, dim3(static_cast<unsigned>(grid)), dim3(BX_NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(panel_dw_reduce_kernel, dim3(PD * PD / 64), dim3(256), 0, s, static_cast<const float*>(p.ws),

@@ -169,3 +169,44 @@ def test_forward_error_is_float32_class(dist):
     scale = np.abs(a.astype(np.float64)) @ np.abs(w.astype(np.float64)).T
     err = np.abs(got - ref) / scale
     assert err.max() <= 8 * 2.0 ** -24, f"max error {err.max() * 2**24:.2f} units of 2^-24"
+
+
+@pytest.mark.parametrize("dist", ["normal", "wide-range", "cancelling"])
+def test_backward_error_is_float32_class(dist):
+    """The width-128 backward's error against float64, relative to the sum of |terms| per element:
+    dA within 8 units of 2^-24 (chains of 32 products folded into float64, as in the forward), dW
+    within 16 units (float32 sums over each block's rows, at most 64 rows per block at m = 3001,
+    then float64 across blocks; measured at most 2.7)."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng({"normal": 11, "wide-range": 12, "cancelling": 13}[dist])
+    m, d = 3001, 128
+    if dist == "normal":
+        a = rng.standard_normal((m, d))
+        dh = rng.standard_normal((m, d))
+    elif dist == "wide-range":
+        a = rng.standard_normal((m, d)) * np.exp(rng.uniform(-8, 8, (m, d)))
+        dh = rng.standard_normal((m, d)) * np.exp(rng.uniform(-8, 8, (m, d)))
+    else:
+        a = np.repeat(rng.standard_normal((m, 1)), d, 1) * np.where(np.arange(d) % 2, 1, -1) + \
+            1e-3 * rng.standard_normal((m, d))
+        dh = np.repeat(rng.standard_normal((1, d)), m, 0) * np.where(np.arange(m) % 2, 1, -1)[:, None] + \
+            1e-3 * rng.standard_normal((m, d))
+    a = a.astype(np.float32)
+    dh = dh.astype(np.float32)
+    w = (rng.standard_normal((d, d)) / 11.3).astype(np.float32)
+    h = np.where(rng.random((m, d)) < 0.5, 0.0, 1.0).astype(np.float32)     # the ReLU mask's pattern
+    H.note(f"backward error bound, {dist}")
+    ws = torch.empty(B.dense_backward_workspace(m, d, d) // 4 + 1, dtype=torch.float32, device="cuda")
+    da = torch.full((m, d), np.nan, dtype=torch.float32, device="cuda")
+    dw = torch.full((d, d), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_backward(H.dev(dh), H.dev(h), H.dev(a), H.dev(w), da, dw, workspace=ws)
+    z = np.where(h > 0, dh, 0.0).astype(np.float64)
+    ref_da, sc_da = z @ w.astype(np.float64), np.abs(z) @ np.abs(w.astype(np.float64))
+    ref_dw, sc_dw = z.T @ a.astype(np.float64), np.abs(z).T @ np.abs(a.astype(np.float64))
+    e_da = np.abs(H.host(da).astype(np.float64) - ref_da) / np.maximum(sc_da, 1e-300)
+    e_dw = np.abs(H.host(dw).astype(np.float64) - ref_dw) / np.maximum(sc_dw, 1e-300)
+    H.note(f"  dA max {e_da.max() * 2**24:.2f}, dW max {e_dw.max() * 2**24:.2f} units of 2^-24")
+    assert e_da.max() <= 8 * 2.0 ** -24, f"dA: max error {e_da.max() * 2**24:.2f} units of 2^-24"
+    assert e_dw.max() <= 16 * 2.0 ** -24, f"dW: max error {e_dw.max() * 2**24:.2f} units of 2^-24"
