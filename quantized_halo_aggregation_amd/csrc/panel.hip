@@ -34,6 +34,7 @@ __device__ __forceinline__ void zero(float __attribute__((ext_vector_type(N)))& 
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data: out-of-range stores dropped
 constexpr int X3_NT = 512;          // 8 wavefronts: 2 row blocks x 4 column blocks of 32 x 32
 constexpr int X3_PR = 64;           // rows per panel
 constexpr int X3_LS = 136;          // bf16 per staged row: the 32 x 32 operand reads hit distinct banks
@@ -78,6 +79,16 @@ __device__ __forceinline__ void stage4(__bf16* planes, int r, int c, const float
   *reinterpret_cast<uint2*>(planes + 2 * ROWS * X3_LS + o) = l;
 }
 
+// Sixteen stores that the hardware drops (a buffer of no records).  Issued after the loads that
+// enter a panel loop, they give the loop's entry the same order of pending memory operations as
+// its back edge (the next panel's loads, then the sixteen output stores), so the compiler's wait
+// before staging a panel counts the stores as still in flight instead of waiting for them.
+__device__ __forceinline__ void dropped_stores16(const float* base) {
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0, kBufferWord3);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) __builtin_amdgcn_raw_buffer_store_b32(0u, none, static_cast<uint32_t>(64 * r), 0, 0);
+}
+
 // H = epi(A W^T) on the bf16 matrix cores.  Every float32 operand is split into three bf16 parts
 // (split3) and each product a * w is formed from the six part products whose weight is at least
 // 2^-16 of it, hi*hi + hi*mid + mid*hi + hi*lo + lo*hi + mid*mid (smallest first); the three
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(X3_NT) void panel_fwd_x3_kernel(PanelArgs p) {
   __shared__ __attribute__((aligned(16))) __bf16 Ap[2][3 * X3_PR * X3_LS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int l = lane & 31;
   const int cb = wid & 3;       // 32-column block of the output
@@ -142,6 +153,7 @@ __global__ __launch_bounds__(X3_NT) void panel_fwd_x3_kernel(PanelArgs p) {
   stage(0);
   __syncthreads();
   if (panel + stride < n_panels) load(panel + stride);
+  dropped_stores16(p.out);
 
   for (int buf = 0; panel < n_panels; panel += stride, buf ^= 1) {
     const __bf16* ah = Ap[buf] + (32 * rb + l) * X3_LS + 8 * h;
@@ -176,13 +188,20 @@ __global__ __launch_bounds__(X3_NT) void panel_fwd_x3_kernel(PanelArgs p) {
       stage(buf ^ 1);
       if (next + stride < n_panels) load(next + stride);
     }
+    // range-checked buffer stores (rows past m dropped by the hardware): no branches, so the
+    // next panel's load wait need not cover them
+    {
+      const int64_t row0 = panel * X3_PR + 32 * rb;
+      const int64_t rows = p.m - row0 < 32 ? (p.m - row0 > 0 ? p.m - row0 : 0) : 32;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          p.out + row0 * p.ldo, 0, static_cast<int32_t>(rows * p.ldo * 4), kBufferWord3);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = panel * X3_PR + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < p.m) {
+      for (int r = 0; r < 16; ++r) {
         float v = static_cast<float>(sum[r]);
         if (p.relu) v = v > 0.0f ? v : 0.0f;
-        p.out[row * p.ldo + 32 * cb + l] = v;
+        const int pr = 8 * (r >> 2) + 4 * h + (r & 3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs,
+                                              static_cast<uint32_t>((pr * p.ldo + 32 * cb + l) * 4), 0, 0);
       }
     }
     __syncthreads();
@@ -205,7 +224,6 @@ __global__ __launch_bounds__(X3_NT) void panel_fwd_x3_kernel(PanelArgs p) {
 constexpr int BX_PR = 32;           // rows per panel
 constexpr int BX_LS = 140;          // floats per staged row
 constexpr int BX_NT = 512;
-constexpr int kBxBufferWord3 = 0x00020000;   // raw buffer, 32-bit data: out-of-range stores dropped
 constexpr int BX_SV = BX_PR * PD / 4 / BX_NT;   // float4 per thread per staged array (2)
 
 // split3 of eight values, two at a time
@@ -307,6 +325,7 @@ __global__ __launch_bounds__(BX_NT) void panel_bwd_x3_kernel(PanelArgs p) {
       for (int j = 0; j < 8; ++j) x[j] = p.w[static_cast<int64_t>(16 * st + 8 * h + j) * p.ldw + 32 * cb + l];
       split8(x, wh[st], wm[st], wl[st]);
     }
+    dropped_stores16(p.da);
     for (; panel < n_panels; panel += grid) {
       __syncthreads();
       const int64_t nxt = panel + grid;
@@ -340,7 +359,7 @@ __global__ __launch_bounds__(BX_NT) void panel_bwd_x3_kernel(PanelArgs p) {
         const int64_t row0 = panel * BX_PR + 32 * rb;
         const int64_t rows = p.m - row0 < 32 ? p.m - row0 : 32;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            p.da + row0 * p.ldda, 0, static_cast<int32_t>(rows * p.ldda * 4), kBxBufferWord3);
+            p.da + row0 * p.ldda, 0, static_cast<int32_t>(rows * p.ldda * 4), kBufferWord3);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int pr = 8 * (r >> 2) + 4 * h + (r & 3);
@@ -456,6 +475,7 @@ size_t panel_bwd_workspace(int64_t m) {
 
 hipError_t launch_panel_fwd(const PanelArgs& p, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
+  if (p.ldo >= (int64_t{1} << 24)) return hipErrorInvalidValue;   // 32-row store ranges in 32 bits
   const int64_t n_panels = (p.m + X3_PR - 1) / X3_PR;
   const unsigned grid = static_cast<unsigned>(n_panels < kPanelBlocks ? n_panels : kPanelBlocks);
   hipLaunchKernelGGL(panel_fwd_x3_kernel, dim3(grid), dim3(X3_NT), 0, s, p);
@@ -464,6 +484,7 @@ hipError_t launch_panel_fwd(const PanelArgs& p, hipStream_t s) {
 
 hipError_t launch_panel_bwd(const PanelArgs& p, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
+  if (p.ldda >= (int64_t{1} << 24)) return hipErrorInvalidValue;  // 32-row store ranges in 32 bits
   const int32_t grid = panel_grid(p.m);
   hipLaunchKernelGGL(panel_bwd_x3_kernel, dim3(static_cast<unsigned>(grid)), dim3(BX_NT), 0, s, p);
   hipError_t e = hipGetLastError();
