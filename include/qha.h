@@ -253,21 +253,21 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
                                size_t workspace_bytes, void* stream);
 
 /* Dense projection and its gradients (guide section 2: z_v = W a_v, h_v = sigma(z_v); section 7:
- * dL/dW = sum_v (dL/dh_v * sigma'(z_v)) a_v^T) on fp32 matrix cores (MFMA):
+ * dL/dW = sum_v (dL/dh_v * sigma'(z_v)) a_v^T), float32 products on the matrix cores (MFMA):
  *   C[m x n] = (beta ? C : 0) + op(A)[m x k] * op(B)[k x n]
  * op(X) = X (row-major, leading dimension ld) or X^T when trans_x = 1.  The forward is
  * trans_b = 1 with B = W [d_out x d_in] and epilogue RELU; the backward's dA is dZ * W and its
  * dW is dZ^T * A (trans_a = 1), both with prologue RELU_MASK and aux = the forward output H, so
  * that dZ = dH * [H > 0] is formed while A is loaded (aux has op(A)'s storage layout).
- * Products are accumulated by the fp32 matrix cores over 32 values of k at a time and those
- * partial sums are added in float64; the result is rounded to float32 once (after adding C when
- * beta = 1, before the epilogue).  The forward shape n = k = 128 (trans_b = 1, no prologue,
- * beta = 0) runs as a row-panel kernel on the bf16 matrix cores instead: each float32 operand is
- * split exactly into three bf16 parts and each product is rebuilt from the six part products of
- * weight >= 2^-16 of it (the dropped ones total below 2^-23 of the product), accumulated in
- * float32 over 32 values of k and in float64 across them; its error against float64 is of the
- * same size as the fp32 matrix cores' (at most 8 units of 2^-24 of sum_k |a_k b_k| per element
- * in the tests).  When m*n is small and k large the reduction is split over k
+ * Each float32 operand is split exactly into three bf16 parts and each product is rebuilt on the
+ * bf16 matrix cores from the six part products of weight >= 2^-16 of it (the dropped ones total
+ * below 2^-23 of the product); products are accumulated in float32 over 32 values of k at a time
+ * and those partial sums are added in float64; the result is rounded to float32 once (after adding
+ * C when beta = 1, before the epilogue).  The error against float64 is of the size of float32
+ * matrix-core products (at most 8 units of 2^-24 of sum_k |a_k b_k| per element for the
+ * width-128 forward in the tests).  The width-128 forward (n = k = 128, trans_b = 1, no prologue,
+ * beta = 0) runs as a row-panel kernel with W's parts held on chip; other shapes as tiled
+ * products.  When m*n is small and k large the reduction is split over k
  * into float64 partials in the workspace (device, 16-byte aligned, qha_dense_project_workspace
  * bytes) and summed in a fixed order; results are deterministic.  beta is 0 or 1.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */

@@ -1,15 +1,18 @@
-// Dense projection C = op(A) op(B) on fp32 matrix cores, with the ReLU epilogue of the forward
-// and the ReLU-mask prologue of the backward.
+// Dense projection C = op(A) op(B) with float32 products on the bf16 matrix cores, with the ReLU
+// epilogue of the forward and the ReLU-mask prologue of the backward.
 //
 // Method: SYLVIE guide, section 2 (z_v = W a_v, h_v = sigma(z_v)) and section 7 (the weight
 // gradient sum_v (dL/dh_v * sigma'(z_v)) a_v^T).
 //
 // Mapping to gfx950: a 256-thread block owns a 64x128 tile of C; its four wavefronts own 32x64
-// pieces, each held as two v_mfma_f32_32x32x2f32 accumulators (32 fp32 per lane) plus their
-// float64 running sums.  K advances 32 at a time through LDS tiles that keep the operand's global layout
-// (k-contiguous tiles are read with 16-byte LDS reads, the others with 4-byte reads), padded so
-// neither the stores nor the fragment reads conflict on banks.  Within an 8-wide k slab, MFMA c
-// of a lane in half h consumes k = 4h + c, which lets a single 16-byte read feed four MFMAs.
+// pieces, each two 32x32 accumulators (32 fp32 per lane) plus their float64 running sums.  The
+// float32 products run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16): every operand value is
+// split exactly into three bf16 parts as its tile is staged in LDS (once per block), and each
+// product is rebuilt from the six part products of weight >= 2^-16 of it (the dropped ones total
+// below 2^-23 of the product, about one float32 rounding).  K advances 32 at a time; the tiles are
+// staged k-contiguous ([row][k] for A, [column][k] for B, 40 bf16 per row so that the 16-byte
+// operand reads and the 8-byte staging writes hit distinct banks); operands stored k-major are
+// read four k at a time with coalesced 4-byte loads, which transposes them on the way in.
 // The next tile's global loads are issued before the current tile is consumed.  Each 32-wide k
 // step accumulates into fresh fp32 MFMA accumulators that are then added into float64 running
 // sums, so a long dot product is rounded in float32 only over 32 terms at a time (for K = 512 this
@@ -22,24 +25,128 @@ namespace qha {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 64;
 constexpr int BN = 128;
 constexpr int BK = 32;
-constexpr int PAD = 4;
+constexpr int KS = BK + 8;     // bf16 per staged row
 constexpr int A_LOADS = BM * BK / 4 / 256;   // float4 loads per thread per k step
 constexpr int B_LOADS = BN * BK / 4 / 256;
 
+// x = hi + mid + lo exactly for a pair of values, as packed bf16 words (first value in the low
+// half): each part is rounded to nearest even, and the remainders x - hi and (x - hi) - mid are
+// exact in float32.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& ph, uint32_t& pm, uint32_t& pl) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  ph = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){a, b}, bf16x2));
+  const float ra = a - __uint_as_float(ph << 16);
+  const float rb = b - __uint_as_float(ph & 0xFFFF0000u);
+  pm = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){ra, rb}, bf16x2));
+  const float la = ra - __uint_as_float(pm << 16);
+  const float lb = rb - __uint_as_float(pm & 0xFFFF0000u);
+  pl = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){la, lb}, bf16x2));
+}
+
+// Stages a float4 that runs along k (4 consecutive k of one row) into the three planes.
+template <int ROWS>
+__device__ __forceinline__ void stage_k4(__bf16* planes, int row, int k, const float4& v) {
+  uint2 h, m, l;
+  split_pair(v.x, v.y, h.x, m.x, l.x);
+  split_pair(v.z, v.w, h.y, m.y, l.y);
+  const int o = row * KS + k;
+  *reinterpret_cast<uint2*>(planes + o) = h;
+  *reinterpret_cast<uint2*>(planes + ROWS * KS + o) = m;
+  *reinterpret_cast<uint2*>(planes + 2 * ROWS * KS + o) = l;
+}
+
+__device__ __forceinline__ floatx16 mfma6(const bf16x8& ah, const bf16x8& am, const bf16x8& al, const bf16x8& bh,
+                                          const bf16x8& bm, const bf16x8& bl, floatx16 c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bm, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bm, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c, 0, 0, 0);
+}
+
+// global -> registers for the tiles starting at k0, as float4s that run along k: float4 s of a
+// thread is (row, k0 + 4 kq .. + 3) of A (rows m0 + row) and B (columns n0 + row).  An operand
+// stored k-contiguous is read with one 16-byte load per float4 (eight lanes per row); one stored
+// k-major with four 4-byte loads whose lanes run along the rows (coalesced), which transposes it on
+// the way in.  Values outside the operands (rows, columns, k) are zero; out-of-range loads read the
+// operand's first element instead (no branch around the loads).
+template <bool TRANS, int ROWS, int NL>
+__device__ __forceinline__ void load_k4(const float* x, int64_t ld, const float* aux, int64_t ld_aux, bool mask,
+                                        int64_t r0, int64_t rows, int64_t k0, int64_t kend, int tid, float4 (&v)[NL]) {
+#pragma unroll
+  for (int s = 0; s < NL; ++s) {
+    const int f = tid + 256 * s;
+    const int row = TRANS ? f % ROWS : f / (BK / 4);
+    const int kq = TRANS ? f / ROWS : f % (BK / 4);
+    const int64_t gr = r0 + row, gk = k0 + 4 * kq;
+    float e[4];
+    if (!TRANS) {         // stored [row][k]
+      const bool ok = gr < rows && gk < kend;
+      const int64_t off = ok ? gr * ld + gk : 0;
+      const float4 t = *reinterpret_cast<const float4*>(x + off);
+      e[0] = t.x; e[1] = t.y; e[2] = t.z; e[3] = t.w;
+      if (mask) {
+        const float4 a = *reinterpret_cast<const float4*>(aux + (ok ? gr * ld_aux + gk : 0));
+        e[0] = a.x > 0.0f ? e[0] : 0.0f;
+        e[1] = a.y > 0.0f ? e[1] : 0.0f;
+        e[2] = a.z > 0.0f ? e[2] : 0.0f;
+        e[3] = a.w > 0.0f ? e[3] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = ok ? e[j] : 0.0f;
+    } else {              // stored [k][row]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = gr < rows && gk + j < kend;
+        float t = x[ok ? (gk + j) * ld + gr : 0];
+        if (mask) t = aux[ok ? (gk + j) * ld_aux + gr : 0] > 0.0f ? t : 0.0f;
+        e[j] = ok ? t : 0.0f;
+      }
+    }
+    v[s] = make_float4(e[0], e[1], e[2], e[3]);
+  }
+}
+
+template <bool TA, bool TB, bool MASK>
+__device__ __forceinline__ void load_tiles(const GemmArgs& p, int tid, int64_t m0, int64_t n0, int64_t k0, int64_t kend,
+                                           float4 (&ra)[A_LOADS], float4 (&rb)[B_LOADS]) {
+  load_k4<TA, BM, A_LOADS>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra);
+  load_k4<!TB, BN, B_LOADS>(p.b, p.ldb, nullptr, 0, false, n0, p.n, k0, kend, tid, rb);
+}
+
+// registers -> the k-contiguous bf16 planes of the tiles
+template <bool TA, bool TB>
+__device__ __forceinline__ void store_tiles(__bf16* As, __bf16* Bs, int tid, const float4 (&ra)[A_LOADS],
+                                            const float4 (&rb)[B_LOADS]) {
+#pragma unroll
+  for (int s = 0; s < A_LOADS; ++s) {
+    const int f = tid + 256 * s;
+    if (!TA) stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), ra[s]);
+    else stage_k4<BM>(As, f % BM, 4 * (f / BM), ra[s]);
+  }
+#pragma unroll
+  for (int s = 0; s < B_LOADS; ++s) {
+    const int f = tid + 256 * s;
+    if (TB) stage_k4<BN>(Bs, f / (BK / 4), 4 * (f % (BK / 4)), rb[s]);
+    else stage_k4<BN>(Bs, f % BN, 4 * (f / BN), rb[s]);
+  }
+}
+
 template <bool TA, bool TB, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
-  constexpr int A_ELEMS = TA ? BK * (BM + PAD) : BM * (BK + PAD);
-  constexpr int B_ELEMS = TB ? BN * (BK + PAD) : BK * (BN + PAD);
-  __shared__ __attribute__((aligned(16))) float As[A_ELEMS];
-  __shared__ __attribute__((aligned(16))) float Bs[B_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 As[3 * BM * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * BN * KS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1;        // 32-row half of the block tile
   const int wn = wid & 1;         // 64-column half
   const int h = lane >> 5;
@@ -56,125 +163,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     for (int r = 0; r < 16; ++r) sum[j][r] = 0.0;
 
   float4 ra[A_LOADS], rb[B_LOADS];
-  const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-
-  // global -> registers for the tile starting at k0
-  auto load_tiles = [&](int64_t k0) {
-#pragma unroll
-    for (int s = 0; s < A_LOADS; ++s) {
-      const int f = tid + 256 * s;
-      int64_t gr, gc;     // storage row / column of the float4's first element
-      bool ok;
-      if (!TA) {          // A stored [m][k]
-        const int row = f / (BK / 4), kq = f % (BK / 4);
-        gr = m0 + row;
-        gc = k0 + 4 * kq;
-        ok = gr < p.m && gc < kend;
-      } else {            // A stored [k][m]
-        const int kr = f / (BM / 4), mq = f % (BM / 4);
-        gr = k0 + kr;
-        gc = m0 + 4 * mq;
-        ok = gr < kend && gc < p.m;
-      }
-      float4 v = zero4;
-      if (ok) {
-        v = *reinterpret_cast<const float4*>(p.a + gr * p.lda + gc);
-        if (MASK) {
-          const float4 x = *reinterpret_cast<const float4*>(p.aux + gr * p.ld_aux + gc);
-          v.x = x.x > 0.0f ? v.x : 0.0f;
-          v.y = x.y > 0.0f ? v.y : 0.0f;
-          v.z = x.z > 0.0f ? v.z : 0.0f;
-          v.w = x.w > 0.0f ? v.w : 0.0f;
-        }
-      }
-      ra[s] = v;
-    }
-#pragma unroll
-    for (int s = 0; s < B_LOADS; ++s) {
-      const int f = tid + 256 * s;
-      int64_t gr, gc;
-      bool ok;
-      if (TB) {           // B stored [n][k]
-        const int row = f / (BK / 4), kq = f % (BK / 4);
-        gr = n0 + row;
-        gc = k0 + 4 * kq;
-        ok = gr < p.n && gc < kend;
-      } else {            // B stored [k][n]
-        const int kr = f / (BN / 4), nq = f % (BN / 4);
-        gr = k0 + kr;
-        gc = n0 + 4 * nq;
-        ok = gr < kend && gc < p.n;
-      }
-      rb[s] = ok ? *reinterpret_cast<const float4*>(p.b + gr * p.ldb + gc) : zero4;
-    }
-  };
-
-  auto store_tiles = [&]() {
-#pragma unroll
-    for (int s = 0; s < A_LOADS; ++s) {
-      const int f = tid + 256 * s;
-      if (!TA) {
-        const int row = f / (BK / 4), kq = f % (BK / 4);
-        *reinterpret_cast<float4*>(&As[row * (BK + PAD) + 4 * kq]) = ra[s];
-      } else {
-        const int kr = f / (BM / 4), mq = f % (BM / 4);
-        *reinterpret_cast<float4*>(&As[kr * (BM + PAD) + 4 * mq]) = ra[s];
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < B_LOADS; ++s) {
-      const int f = tid + 256 * s;
-      if (TB) {
-        const int row = f / (BK / 4), kq = f % (BK / 4);
-        *reinterpret_cast<float4*>(&Bs[row * (BK + PAD) + 4 * kq]) = rb[s];
-      } else {
-        const int kr = f / (BN / 4), nq = f % (BN / 4);
-        *reinterpret_cast<float4*>(&Bs[kr * (BN + PAD) + 4 * nq]) = rb[s];
-      }
-    }
-  };
 
   if (kbeg < kend) {
-    load_tiles(kbeg);
-    store_tiles();
+    load_tiles<TA, TB, MASK>(p, tid, m0, n0, kbeg, kend, ra, rb);
+    store_tiles<TA, TB>(As, Bs, tid, ra, rb);
     __syncthreads();
   }
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
-    if (more) load_tiles(k0 + BK);
+    if (more) load_tiles<TA, TB, MASK>(p, tid, m0, n0, k0 + BK, kend, ra, rb);
     floatx16 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 #pragma unroll
-    for (int slab = 0; slab < BK / 8; ++slab) {
-      const int kk = slab * 8 + 4 * h;
-      float af[4], bf[2][4];
-      const int row = wm * 32 + l32;
-      if (!TA) {
-        const float4 t = *reinterpret_cast<const float4*>(&As[row * (BK + PAD) + kk]);
-        af[0] = t.x; af[1] = t.y; af[2] = t.z; af[3] = t.w;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) af[c] = As[(kk + c) * (BM + PAD) + row];
-      }
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      // lane (h, l32) takes k = 16 ks + 8 h .. + 7 of row l32 (A) and of column l32 (B)
+      const __bf16* ap = As + (wm * 32 + l32) * KS + 16 * ks + 8 * h;
+      const bf16x8 xh = *reinterpret_cast<const bf16x8*>(ap);
+      const bf16x8 xm = *reinterpret_cast<const bf16x8*>(ap + BM * KS);
+      const bf16x8 xl = *reinterpret_cast<const bf16x8*>(ap + 2 * BM * KS);
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const int col = wn * 64 + ni * 32 + l32;
-        if (TB) {
-          const float4 t = *reinterpret_cast<const float4*>(&Bs[col * (BK + PAD) + kk]);
-          bf[ni][0] = t.x; bf[ni][1] = t.y; bf[ni][2] = t.z; bf[ni][3] = t.w;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) bf[ni][c] = Bs[(kk + c) * (BN + PAD) + col];
-        }
+        const __bf16* bp = Bs + (wn * 64 + ni * 32 + l32) * KS + 16 * ks + 8 * h;
+        const bf16x8 yh = *reinterpret_cast<const bf16x8*>(bp);
+        const bf16x8 ym = *reinterpret_cast<const bf16x8*>(bp + BN * KS);
+        const bf16x8 yl = *reinterpret_cast<const bf16x8*>(bp + 2 * BN * KS);
+        acc[ni] = mfma6(xh, xm, xl, yh, ym, yl, acc[ni]);
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[c], bf[ni][c], acc[ni], 0, 0, 0);
     }
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) sum[ni][r] += static_cast<double>(acc[ni][r]);
     __syncthreads();
     if (more) {
-      store_tiles();
+      store_tiles<TA, TB>(As, Bs, tid, ra, rb);
       __syncthreads();
     }
   }
