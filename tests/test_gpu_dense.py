@@ -210,3 +210,35 @@ def test_backward_error_is_float32_class(dist):
     H.note(f"  dA max {e_da.max() * 2**24:.2f}, dW max {e_dw.max() * 2**24:.2f} units of 2^-24")
     assert e_da.max() <= 8 * 2.0 ** -24, f"dA: max error {e_da.max() * 2**24:.2f} units of 2^-24"
     assert e_dw.max() <= 16 * 2.0 ** -24, f"dW: max error {e_dw.max() * 2**24:.2f} units of 2^-24"
+
+
+@pytest.mark.parametrize("m,d_in,d_out", [(3001, 256, 256), (2000, 512, 256), (1001, 16, 16)])
+def test_general_width_error_is_float32_class(m, d_in, d_out):
+    """The tiled products at widths other than 128 (split parts on the bf16 matrix cores, 32-k
+    chains folded into float64): the forward and dA within 8 units of 2^-24 of the sum of |terms|
+    per element, dW within 16 units, on wide-range operands (e^+-8 per element)."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(m + d_in)
+    a = (rng.standard_normal((m, d_in)) * np.exp(rng.uniform(-8, 8, (m, d_in)))).astype(np.float32)
+    w = (rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).astype(np.float32)
+    dh = (rng.standard_normal((m, d_out)) * np.exp(rng.uniform(-8, 8, (m, d_out)))).astype(np.float32)
+    h = np.where(rng.random((m, d_out)) < 0.5, 0.0, 1.0).astype(np.float32)
+    H.note(f"general-width error bound m={m} {d_in}->{d_out}")
+    out = torch.full((m, d_out), np.nan, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(B.dense_project_workspace(0, 1, m, d_out, d_in), 4) // 4, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 1, H.dev(a), H.dev(w), 0, out, workspace=ws)
+    a64, w64 = a.astype(np.float64), w.astype(np.float64)
+    e_f = np.abs(H.host(out).astype(np.float64) - a64 @ w64.T) / np.maximum(np.abs(a64) @ np.abs(w64).T, 1e-300)
+    wsb = torch.empty(B.dense_backward_workspace(m, d_out, d_in) // 4 + 1, dtype=torch.float32, device="cuda")
+    da = torch.full((m, d_in), np.nan, dtype=torch.float32, device="cuda")
+    dw = torch.full((d_out, d_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_backward(H.dev(dh), H.dev(h), H.dev(a), H.dev(w), da, dw, workspace=wsb)
+    z = np.where(h > 0, dh, 0.0).astype(np.float64)
+    e_da = np.abs(H.host(da).astype(np.float64) - z @ w64) / np.maximum(np.abs(z) @ np.abs(w64), 1e-300)
+    e_dw = np.abs(H.host(dw).astype(np.float64) - z.T @ a64) / np.maximum(np.abs(z).T @ np.abs(a64), 1e-300)
+    H.note(f"  forward {e_f.max() * 2**24:.2f}, dA {e_da.max() * 2**24:.2f}, dW {e_dw.max() * 2**24:.2f} units")
+    assert e_f.max() <= 8 * 2.0 ** -24, f"forward: {e_f.max() * 2**24:.2f} units of 2^-24"
+    assert e_da.max() <= 8 * 2.0 ** -24, f"dA: {e_da.max() * 2**24:.2f} units of 2^-24"
+    assert e_dw.max() <= 16 * 2.0 ** -24, f"dW: {e_dw.max() * 2**24:.2f} units of 2^-24"
