@@ -4,8 +4,9 @@
 // Method: SYLVIE guide, section 2 (z_v = W a_v, h_v = sigma(z_v)) and section 7 (the weight
 // gradient sum_v (dL/dh_v * sigma'(z_v)) a_v^T).
 //
-// Mapping to gfx950: a 256-thread block owns a 64x128 tile of C; its four wavefronts own 32x64
-// pieces, each two 32x32 accumulators (32 fp32 per lane) plus their float64 running sums.  The
+// Mapping to gfx950: a block owns a 64x128 tile of C (256 threads), or 64x256 for outputs at least
+// 512 wide (512 threads, so each A tile is staged once for twice the columns); its wavefronts own
+// 32x64 pieces, each two 32x32 accumulators (32 fp32 per lane) plus their float64 running sums.  The
 // float32 products run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16): every operand value is
 // split exactly into three bf16 parts as its tile is staged in LDS (once per block), and each
 // product is rebuilt from the six part products of weight >= 2^-16 of it (the dropped ones total
@@ -28,11 +29,18 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 64;
-constexpr int BN = 128;
 constexpr int BK = 32;
 constexpr int KS = BK + 8;     // bf16 per staged row
-constexpr int A_LOADS = BM * BK / 4 / 256;   // float4 loads per thread per k step
-constexpr int B_LOADS = BN * BK / 4 / 256;
+// Block tile BM x BN with two wavefronts along m and BN / 64 along n (2 BN threads): BN = 256 for
+// outputs at least 512 wide (each A tile is then staged once for twice the columns; measured
+// faster there, slower at 256), else 128.
+template <int BN>
+struct Tile {
+  static constexpr int NT = 2 * BN;
+  static constexpr int A_LOADS = BM * BK / 4 / NT;   // float4 loads per thread per k step
+  static constexpr int B_LOADS = BN * BK / 4 / NT;
+};
+int tile_n(int64_t n) { return n >= 512 ? 256 : 128; }
 
 // x = hi + mid + lo exactly for a pair of values, as packed bf16 words (first value in the low
 // half): each part is rounded to nearest even, and the remainders x - hi and (x - hi) - mid are
@@ -77,12 +85,12 @@ __device__ __forceinline__ floatx16 mfma6(const bf16x8& ah, const bf16x8& am, co
 // k-major with four 4-byte loads whose lanes run along the rows (coalesced), which transposes it on
 // the way in.  Values outside the operands (rows, columns, k) are zero; out-of-range loads read the
 // operand's first element instead (no branch around the loads).
-template <bool TRANS, int ROWS, int NL>
+template <bool TRANS, int ROWS, int NL, int NT>
 __device__ __forceinline__ void load_k4(const float* x, int64_t ld, const float* aux, int64_t ld_aux, bool mask,
                                         int64_t r0, int64_t rows, int64_t k0, int64_t kend, int tid, float4 (&v)[NL]) {
 #pragma unroll
   for (int s = 0; s < NL; ++s) {
-    const int f = tid + 256 * s;
+    const int f = tid + NT * s;
     const int row = TRANS ? f % ROWS : f / (BK / 4);
     const int kq = TRANS ? f / ROWS : f % (BK / 4);
     const int64_t gr = r0 + row, gk = k0 + 4 * kq;
@@ -114,41 +122,41 @@ __device__ __forceinline__ void load_k4(const float* x, int64_t ld, const float*
   }
 }
 
-template <bool TA, bool TB, bool MASK>
+template <int BN, bool TA, bool TB, bool MASK>
 __device__ __forceinline__ void load_tiles(const GemmArgs& p, int tid, int64_t m0, int64_t n0, int64_t k0, int64_t kend,
-                                           float4 (&ra)[A_LOADS], float4 (&rb)[B_LOADS]) {
-  load_k4<TA, BM, A_LOADS>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra);
-  load_k4<!TB, BN, B_LOADS>(p.b, p.ldb, nullptr, 0, false, n0, p.n, k0, kend, tid, rb);
+                                           float4 (&ra)[Tile<BN>::A_LOADS], float4 (&rb)[Tile<BN>::B_LOADS]) {
+  load_k4<TA, BM, Tile<BN>::A_LOADS, Tile<BN>::NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra);
+  load_k4<!TB, BN, Tile<BN>::B_LOADS, Tile<BN>::NT>(p.b, p.ldb, nullptr, 0, false, n0, p.n, k0, kend, tid, rb);
 }
 
 // registers -> the k-contiguous bf16 planes of the tiles
-template <bool TA, bool TB>
-__device__ __forceinline__ void store_tiles(__bf16* As, __bf16* Bs, int tid, const float4 (&ra)[A_LOADS],
-                                            const float4 (&rb)[B_LOADS]) {
+template <int BN, bool TA, bool TB>
+__device__ __forceinline__ void store_tiles(__bf16* As, __bf16* Bs, int tid, const float4 (&ra)[Tile<BN>::A_LOADS],
+                                            const float4 (&rb)[Tile<BN>::B_LOADS]) {
 #pragma unroll
-  for (int s = 0; s < A_LOADS; ++s) {
-    const int f = tid + 256 * s;
+  for (int s = 0; s < Tile<BN>::A_LOADS; ++s) {
+    const int f = tid + Tile<BN>::NT * s;
     if (!TA) stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), ra[s]);
     else stage_k4<BM>(As, f % BM, 4 * (f / BM), ra[s]);
   }
 #pragma unroll
-  for (int s = 0; s < B_LOADS; ++s) {
-    const int f = tid + 256 * s;
+  for (int s = 0; s < Tile<BN>::B_LOADS; ++s) {
+    const int f = tid + Tile<BN>::NT * s;
     if (TB) stage_k4<BN>(Bs, f / (BK / 4), 4 * (f % (BK / 4)), rb[s]);
     else stage_k4<BN>(Bs, f % BN, 4 * (f / BN), rb[s]);
   }
 }
 
-template <bool TA, bool TB, bool MASK, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+template <int BN, bool TA, bool TB, bool MASK, bool SPLIT>
+__global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) __bf16 As[3 * BM * KS];
   __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * BN * KS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1;        // 32-row half of the block tile
-  const int wn = wid & 1;         // 64-column half
+  const int wm = wid / (BN / 64);   // 32-row half of the block tile
+  const int wn = wid % (BN / 64);   // 64-column slice
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
@@ -162,16 +170,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum[j][r] = 0.0;
 
-  float4 ra[A_LOADS], rb[B_LOADS];
+  float4 ra[Tile<BN>::A_LOADS], rb[Tile<BN>::B_LOADS];
 
   if (kbeg < kend) {
-    load_tiles<TA, TB, MASK>(p, tid, m0, n0, kbeg, kend, ra, rb);
-    store_tiles<TA, TB>(As, Bs, tid, ra, rb);
+    load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, kbeg, kend, ra, rb);
+    store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
     __syncthreads();
   }
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
-    if (more) load_tiles<TA, TB, MASK>(p, tid, m0, n0, k0 + BK, kend, ra, rb);
+    if (more) load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, k0 + BK, kend, ra, rb);
     floatx16 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) sum[ni][r] += static_cast<double>(acc[ni][r]);
     __syncthreads();
     if (more) {
-      store_tiles<TA, TB>(As, Bs, tid, ra, rb);
+      store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
       __syncthreads();
     }
   }
@@ -238,14 +246,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   *dst = v;
 }
 
-template <bool TA, bool TB, bool MASK>
-hipError_t launch_variant(const GemmArgs& p, hipStream_t s) {
+template <int BN, bool TA, bool TB, bool MASK>
+hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p.m + BM - 1) / BM), static_cast<unsigned>((p.n + BN - 1) / BN),
                   static_cast<unsigned>(p.splits));
   if (p.splits > 1)
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, MASK, true>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true>), grid, dim3(Tile<BN>::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, MASK, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;
   const int64_t mn = p.m * p.n;
@@ -253,10 +261,16 @@ hipError_t launch_variant(const GemmArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool TA, bool TB, bool MASK>
+hipError_t launch_variant(const GemmArgs& p, hipStream_t s) {
+  return tile_n(p.n) == 256 ? launch_tiled<256, TA, TB, MASK>(p, s) : launch_tiled<128, TA, TB, MASK>(p, s);
+}
+
 }  // namespace
 
 void gemm_split_rule(int64_t m, int64_t n, int64_t k, int32_t* splits, int64_t* k_per_split) {
-  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int bn = tile_n(n);
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + bn - 1) / bn);
   int64_t s = 1;
   if (tiles < 256 && k > 8 * BK * 16) {
     s = (512 + tiles - 1) / tiles;                 // about two blocks per compute unit
