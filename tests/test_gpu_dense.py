@@ -10,10 +10,12 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("m,d_in,d_out", [(1, 16, 16), (1001, 16, 16), (777, 64, 64), (3001, 128, 128),
                                           (1, 128, 128), (65, 128, 128), (70001, 128, 128),
-                                          (1000, 256, 256), (513, 512, 256), (130, 32, 48)])
+                                          (1000, 256, 256), (513, 512, 256), (130, 32, 48), (300, 64, 512),
+                                          (1001, 128, 516)])
 def test_forward_projection_relu(m, d_in, d_out):
     """d_in = d_out = 128 runs the row-panel kernel (W in LDS; ragged last panel, several panels per
-    block at m = 70001); beta = 1 always takes the general kernel."""
+    block at m = 70001); beta = 1 always takes the general kernel, whose outputs of 512 columns or
+    more use 256-wide block tiles (a ragged last tile at 516)."""
     H.require_gpu()
     import torch
     from quantized_halo_aggregation_amd import binding as B
@@ -33,7 +35,7 @@ def test_forward_projection_relu(m, d_in, d_out):
 
 
 @pytest.mark.parametrize("m,d_in,d_out", [(1001, 16, 16), (3001, 128, 128), (20000, 128, 128),
-                                          (4099, 512, 256), (70000, 256, 256)])
+                                          (4099, 512, 256), (70000, 256, 256), (777, 516, 64)])
 def test_backward_projection(m, d_in, d_out):
     """dA = (dH * [H > 0]) W and dW = (dH * [H > 0])^T A; large m exercises the split-k reduction."""
     H.require_gpu()
