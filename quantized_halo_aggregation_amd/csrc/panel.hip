@@ -15,7 +15,7 @@
 // (W's parts in registers, as in the forward) while four form the block's dW partial, so dH, H
 // and A are each read once and dZ is formed once.
 // Precision: for the forward and dA each MFMA chain adds 32 k-steps in float32 and those partial
-// sums are added in float64.  A block's dW tiles are float32 MFMA sums over its panels' rows
+// sums are added in float64.  A block's dW tiles are float32 matrix-core sums over its panels' rows
 // (about m/256 rows); a second kernel adds the blocks' partials in float64 in a fixed order, so
 // results are deterministic.
 #include "qha_internal.hpp"

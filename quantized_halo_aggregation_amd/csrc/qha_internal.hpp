@@ -105,7 +105,7 @@ struct GemmArgs {
   int64_t k_per_split;
 };
 
-// Row-panel products of width-128 layers (W resident in LDS, 64-row panels streamed).
+// Row-panel products of width-128 layers (W's split parts held on chip, row panels streamed).
 constexpr int kPanelBlocks = 256;    // one block per compute unit of an MI355X
 struct PanelArgs {
   int64_t m;

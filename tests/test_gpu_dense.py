@@ -1,4 +1,5 @@
-"""qha_dense_project (fp32 MFMA) against the oracle's float64 projection and gradients."""
+"""qha_dense_project and qha_dense_backward (float32 products on the matrix cores) against the
+oracle's float64 projection and gradients, and their error against float64."""
 import numpy as np
 import pytest
 
@@ -13,9 +14,9 @@ pytestmark = pytest.mark.gpu
                                           (1000, 256, 256), (513, 512, 256), (130, 32, 48), (300, 64, 512),
                                           (1001, 128, 516)])
 def test_forward_projection_relu(m, d_in, d_out):
-    """d_in = d_out = 128 runs the row-panel kernel (W in LDS; ragged last panel, several panels per
-    block at m = 70001); beta = 1 always takes the general kernel, whose outputs of 512 columns or
-    more use 256-wide block tiles (a ragged last tile at 516)."""
+    """d_in = d_out = 128 runs the row-panel kernel (W's parts on chip; ragged last panel, several
+    panels per block at m = 70001); beta = 1 always takes the general kernel, whose outputs of 512
+    columns or more use 256-wide block tiles (a ragged last tile at 516)."""
     H.require_gpu()
     import torch
     from quantized_halo_aggregation_amd import binding as B
