@@ -128,6 +128,17 @@ def test_agg_plan_covers_every_edge_and_row_once(skip_empty, group_edges):
     assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 8
 
 
+@pytest.mark.parametrize("lens, unit", [([1, 1, 1, 1], 1), ([1], 1), ([1, 2, 1], 0), ([1, 0, 1], 0),
+                                        ([0], 0), ([3], 0)])
+def test_agg_plan_marks_one_edge_rows(lens, unit):
+    """unit_rows is set exactly when every row holds one edge (empty rows and longer rows clear it)."""
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    st, items, _, _ = _plan_host(ptr, 512, False)
+    assert st.unit_rows == unit
+    if unit:                                   # with one edge a row, row r's edge is edge r
+        assert np.array_equal(ptr, np.arange(len(lens) + 1))
+
+
 def test_device_calls_reject_bad_arguments_before_any_hip_call():
     q = B._quantize_pack
     # unsupported width
