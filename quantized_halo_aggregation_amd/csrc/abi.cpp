@@ -68,6 +68,8 @@ int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d
   if (plan->n_split_rows > 0 && (!plan->split_row || !plan->split_ptr))
     return fail(QHA_ERR_INVALID_ARG, "plan split arrays are NULL");
   if (plan->skip_empty && beta != 1) return fail(QHA_ERR_INVALID_ARG, "a plan that skips empty rows needs beta = 1");
+  if (plan->unit_rows != 0 && (plan->unit_rows != 1 || plan->n_split_rows != 0 || (n_rows > 0 && plan->n_items == 0)))
+    return fail(QHA_ERR_INVALID_ARG, "plan: unit_rows is inconsistent with its counts");
   const size_t need = qha_agg_workspace_bytes(plan, d);
   if (need > 0) {
     if (!ws || ws_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);

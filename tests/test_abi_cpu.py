@@ -189,6 +189,16 @@ def test_device_calls_reject_bad_arguments_before_any_hip_call():
     assert call(n_rows=3, plan=C.byref(st2)) == B.QHA_ERR_WORKSPACE
     # plan built for another row count
     assert call(n_rows=4, plan=C.byref(st2)) == B.QHA_ERR_INVALID_ARG
+    # a one-edge-row flag that its counts contradict (split rows, or a value other than 0 / 1)
+    ws = np.zeros(1 << 16, np.float64)
+    st2.unit_rows = 1
+    assert call(n_rows=3, plan=C.byref(st2), ws=ws.ctypes.data, wsb=ws.nbytes) == B.QHA_ERR_INVALID_ARG
+    assert "unit_rows" in B._last_error().decode()
+    st3, *_ = _plan_host(np.arange(4, dtype=np.int32), 512, False)
+    st3.items = st3.split_row = st3.split_ptr = FAKE
+    assert st3.unit_rows == 1
+    st3.unit_rows = 2
+    assert call(n_rows=3, plan=C.byref(st3)) == B.QHA_ERR_INVALID_ARG
 
     g = B._aggregate_bwd
     assert g(10, FAKE, FAKE, None, None, FAKE, 128, 10, 128, 3, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
