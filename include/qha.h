@@ -133,7 +133,7 @@ typedef struct qha_agg_plan {
   int32_t chunk;           /* edge budget of one chunk of a split row */
   int32_t group_edges;     /* edge budget of a group of whole rows */
   int32_t skip_empty;      /* 1 if rows without edges belong to no item */
-  int32_t unit_rows;       /* set by qha_agg_plan_size: 1 if every row has exactly one edge */
+  int32_t reserved;
   int64_t n_items;         /* items */
   int64_t n_split_items;   /* leading items that are chunks of split rows (= partial-sum slots) */
   int64_t n_split_rows;    /* rows split into chunks */
@@ -211,10 +211,8 @@ int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int
  * separately, then in chunk order), added to the old value when beta = 1 and rounded to float32
  * once; results are deterministic.  With `classes` alone (bits and word_offset NULL), x_inner's
  * rows and the packed codes must each span less than 4 GiB; otherwise the call fails with HIP
- * (invalid value) and the per-row arrays are needed.  A call with n_inner == 0, `classes` and a
- * plan whose unit_rows is set (every row one edge, so row i's edge is edge i) runs a row-parallel
- * kernel that ignores the plan's items and gives the same bits.  Errors: INVALID_ARG,
- * UNSUPPORTED (d), WORKSPACE, HIP. */
+ * (invalid value) and the per-row arrays are needed.  Errors: INVALID_ARG, UNSUPPORTED (d),
+ * WORKSPACE, HIP. */
 int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
                               const float* w, const int32_t* row_ids, const qha_agg_plan* plan,
                               const float* x_inner, int64_t ldx, int64_t n_inner,

@@ -52,7 +52,7 @@ _i32, _i64, _u32, _u64, _sz, _vp = C.c_int32, C.c_int64, C.c_uint32, C.c_uint64,
 
 class AggPlanStruct(C.Structure):
     _fields_ = [("n_rows", _i64), ("chunk", _i32), ("group_edges", _i32), ("skip_empty", _i32),
-                ("unit_rows", _i32), ("n_items", _i64), ("n_split_items", _i64), ("n_split_rows", _i64),
+                ("reserved", _i32), ("n_items", _i64), ("n_split_items", _i64), ("n_split_rows", _i64),
                 ("items", _vp), ("split_row", _vp), ("split_ptr", _vp)]
 
 

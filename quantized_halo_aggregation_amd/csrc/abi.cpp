@@ -68,8 +68,6 @@ int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d
   if (plan->n_split_rows > 0 && (!plan->split_row || !plan->split_ptr))
     return fail(QHA_ERR_INVALID_ARG, "plan split arrays are NULL");
   if (plan->skip_empty && beta != 1) return fail(QHA_ERR_INVALID_ARG, "a plan that skips empty rows needs beta = 1");
-  if (plan->unit_rows != 0 && (plan->unit_rows != 1 || plan->n_split_rows != 0 || (n_rows > 0 && plan->n_items == 0)))
-    return fail(QHA_ERR_INVALID_ARG, "plan: unit_rows is inconsistent with its counts");
   const size_t need = qha_agg_workspace_bytes(plan, d);
   if (need > 0) {
     if (!ws || ws_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
@@ -86,7 +84,6 @@ void fill_plan_args(qha::GatherArgs& g, const qha_agg_plan* plan, int64_t n_rows
     g.n_split_rows = plan->n_split_rows;
     g.split_row = plan->split_row;
     g.split_ptr = plan->split_ptr;
-    g.unit_rows = plan->unit_rows;
   } else {
     g.n_items = n_rows;
     g.n_split_items = 0;
@@ -94,7 +91,6 @@ void fill_plan_args(qha::GatherArgs& g, const qha_agg_plan* plan, int64_t n_rows
     g.n_split_rows = 0;
     g.split_row = nullptr;
     g.split_ptr = nullptr;
-    g.unit_rows = 0;
   }
   g.partial = static_cast<double*>(ws);
 }
@@ -130,7 +126,6 @@ int take_classes(const qha_width_classes* cls, int64_t n_rows, int32_t d, qha::C
 // Walks the rows once and either counts (out == nullptr) or writes the plan's arrays.
 struct PlanWalk {
   int64_t items = 0, split_items = 0, split_rows = 0;
-  bool unit_rows = true;      // every row has exactly one edge
 };
 
 int walk_plan(const int32_t* rowptr, int64_t n_rows, int32_t chunk, int32_t group_edges, int32_t skip_empty,
@@ -169,7 +164,6 @@ int walk_plan(const int32_t* rowptr, int64_t n_rows, int32_t chunk, int32_t grou
   };
   for (int64_t r = 0; r < n_rows; ++r) {
     const int64_t len = static_cast<int64_t>(rowptr[r + 1]) - rowptr[r];
-    if (len != 1) w.unit_rows = false;
     if (len > chunk) {
       close();
       continue;
@@ -309,7 +303,6 @@ int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int3
   plan->n_items = w.items;
   plan->n_split_items = w.split_items;
   plan->n_split_rows = w.split_rows;
-  plan->unit_rows = w.unit_rows ? 1 : 0;
   return ok();
 }
 

@@ -32,9 +32,6 @@
 // lane-parallel, and when x, the codes and the (min, scale) pairs lie within 4 GiB of one base
 // every load is that base plus a 32-bit offset, so an edge costs no scalar selects.  gather_kernel
 // is the general form: per-row offset tables, 64-bit addresses, and the fused quantising epilogue.
-// A fourth kernel, received_add_kernel, serves halo gathers whose every row holds exactly one edge
-// (the received-gradient add when each inner node has one halo copy): it skips the plan and runs
-// one row per group of d / 16 lanes.
 #include "../../include/qha.h"
 #include "qha_internal.hpp"
 #include "quant_common.hpp"
@@ -67,9 +64,6 @@ constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
 #endif
 #ifndef QHA_GROUPED_KERNEL
 #define QHA_GROUPED_KERNEL 1
-#endif
-#ifndef QHA_RECEIVED_KERNEL
-#define QHA_RECEIVED_KERNEL 1
 #endif
 #ifndef QHA_ROWS_KERNEL
 #define QHA_ROWS_KERNEL 1
@@ -849,91 +843,6 @@ __global__ __launch_bounds__(256) void edge_weights_kernel(int64_t n_rows, const
     w[e] = __fmul_rn(rf, c ? c[colidx[e]] : 1.0f);
 }
 
-// scale * q + min for the 16 features of a lane whose codes of width B (< 32) start at bit s0 of
-// w[0] (s0 = 16 for the odd lanes of 1-bit rows, else 0).
-template <uint32_t B>
-__device__ __forceinline__ void dequant16(const uint32_t (&w)[16], uint32_t s0, float mn, float sc, float (&xv)[16]) {
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const uint32_t bp = static_cast<uint32_t>(v) * B;
-    xv[v] = dequant(sc, __builtin_amdgcn_ubfe(w[bp >> 5], (s0 + bp) & 31u, B), mn);
-  }
-}
-
-// The received add of the backward pass when every row of the CSR holds exactly one edge (each
-// inner node has one halo copy elsewhere): out[row_ids[r]] (+)= w_e * message(colidx[e]) over a
-// width-grouped message, every column a halo row.  With one edge a row, row r's edge is edge r.
-// Rows are independent, so instead of walking plan items edge by edge each lane takes 16 features
-// of one row (d / 16 lanes a row, 64 * 16 / d rows a wavefront) and issues its loads in two
-// rounds: the edge's column, weight and output row; then the old output row, the (min, scale)
-// pair and the code words.  The code words come by 16 one-word loads that every lane issues
-// whatever its row's width (a quantised row repeats its last word), so no load sits in a branch
-// that waits for it before the next width's loads can start.  The sum is formed exactly as the
-// general gather forms a one-edge row (w * value + 0 in float64, then old + that, rounded once),
-// so both give the same bits.
-template <int D, bool BETA>
-__global__ __launch_bounds__(256) void received_add_kernel(GatherArgs a) {
-  constexpr int G = D / 16;                   // lanes per row
-  constexpr int RPW = 64 / G;                 // rows per wavefront
-  const int lane = threadIdx.x & 63;
-  const int li = lane % G;
-  const int64_t r = (static_cast<int64_t>(blockIdx.x) * 4 + static_cast<int64_t>(threadIdx.x >> 6)) * RPW + lane / G;
-  if (r >= a.n_rows) return;
-  // round 1 (absent weights and row ids read a valid word instead, so the loads are unconditional)
-  const int32_t k = a.colidx[r];             // a halo row: the call has no inner columns
-  const float wv = (a.w != nullptr ? a.w : reinterpret_cast<const float*>(a.colidx))[r];
-  const int32_t rv = (a.row_ids != nullptr ? a.row_ids : a.colidx)[r];
-  const float wt = a.w != nullptr ? wv : 1.0f;
-  const int64_t orow = a.row_ids != nullptr ? static_cast<int64_t>(rv) : r;
-
-  // the row's width class: the last class that starts at or before k
-  int32_t b = a.cls.bits[0], st = a.cls.start[0];
-  uint32_t cb = a.cls.base[0];
-#pragma unroll
-  for (int c = 1; c < kMaxClasses; ++c) {
-    const bool ge = c < a.cls.n && k >= a.cls.start[c];
-    b = ge ? a.cls.bits[c] : b;
-    st = ge ? a.cls.start[c] : st;
-    cb = ge ? a.cls.base[c] : cb;
-  }
-  const uint32_t ub = static_cast<uint32_t>(b);
-  const uint64_t row_words = ub == 32u ? static_cast<uint64_t>(D) : static_cast<uint64_t>((D * ub + 31u) / 32u);
-  const uint32_t bit0 = static_cast<uint32_t>(li) * 16u * ub;
-  const uint32_t* lp = a.codes + cb + static_cast<uint64_t>(k - st) * row_words + (bit0 >> 5);
-  const uint32_t last = ub == 32u ? 15u : (ub >= 2u ? ub / 2u - 1u : 0u);   // the lane's last word
-
-  // round 2
-  float* dst = a.out + orow * a.ldo + 16 * li;
-  float old[16];
-  if constexpr (BETA) load_row<16>(dst, old);
-  const float2 ms = reinterpret_cast<const float2*>(a.meta)[k];
-  uint32_t cw[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) cw[v] = lp[min(static_cast<uint32_t>(v), last)];
-
-  float xv[16];
-  if (ub == 32u) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) xv[v] = __uint_as_float(cw[v]);
-  } else if (ub == 4u) {
-    dequant16<4>(cw, 0u, ms.x, ms.y, xv);
-  } else if (ub == 8u) {
-    dequant16<8>(cw, 0u, ms.x, ms.y, xv);
-  } else if (ub == 2u) {
-    dequant16<2>(cw, 0u, ms.x, ms.y, xv);
-  } else {
-    dequant16<1>(cw, bit0 & 31u, ms.x, ms.y, xv);
-  }
-  const double wd = static_cast<double>(wt);
-  float res[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const double t = fma(wd, static_cast<double>(xv[v]), 0.0);
-    res[v] = BETA ? static_cast<float>(static_cast<double>(old[v]) + t) : static_cast<float>(t);
-  }
-  store_row<16>(dst, res);
-}
-
 template <int D>
 hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_out, hipStream_t s) {
   // the plain-row kernel addresses x with 32-bit byte offsets
@@ -964,14 +873,6 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_ou
     single_base = QHA_SINGLE_BASE && hi - lo <= 0xFFFFFFFFull;
   }
 
-  if (with_halo && !quantize_out && a.unit_rows && a.n_inner == 0 && a.cls.n > 0 && QHA_RECEIVED_KERNEL) {
-    constexpr int64_t rows_per_block = 4 * (64 / (D / 16));
-    if (a.n_rows == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((a.n_rows + rows_per_block - 1) / rows_per_block));
-    if (a.beta) hipLaunchKernelGGL((received_add_kernel<D, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((received_add_kernel<D, false>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
   if (a.n_items > 0) {
     const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
     if (quantize_out) {

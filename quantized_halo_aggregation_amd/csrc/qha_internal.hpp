@@ -61,7 +61,6 @@ struct GatherArgs {
   int64_t n_split_rows;
   const int32_t* split_row;
   const int32_t* split_ptr;
-  int32_t unit_rows;          // every row has exactly one edge (from the plan)
   const float* w;             // per-edge weights (nullptr: 1)
   // values
   const float* x;

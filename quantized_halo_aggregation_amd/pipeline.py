@@ -79,20 +79,12 @@ class GpuPartition:
         self.colptr, self.rowidx = dev(colptr), dev(rowidx)
 
         # mirror map as a compact CSR: one row per inner node that has halo copies, listing them,
-        # with row_ids naming the inner node.  When no inner node has two copies, the rows follow
-        # the messages instead (row k adds message k to inner node mirror[k]): the codes and
-        # (min, scale) pairs are then read in order and only the output rows are scattered
+        # with row_ids naming the inner node
         m_ptr, m_idx = B.csr_transpose(np.arange(n_h + 1, dtype=np.int32), part.mirror, n_in)
-        if n_h > 0 and int(np.diff(m_ptr).max()) <= 1:
-            mc_ptr = np.arange(n_h + 1, dtype=np.int32)
-            mc_idx = np.arange(n_h, dtype=np.int32)
-            targets = np.ascontiguousarray(part.mirror, dtype=np.int32)
-        else:
-            targets = np.flatnonzero(np.diff(m_ptr) > 0).astype(np.int32)
-            mc_ptr = np.concatenate([[0], np.cumsum(np.diff(m_ptr)[targets])]).astype(np.int32)
-            mc_idx = m_idx
+        targets = np.flatnonzero(np.diff(m_ptr) > 0).astype(np.int32)
+        mc_ptr = np.concatenate([[0], np.cumsum(np.diff(m_ptr)[targets])]).astype(np.int32)
         self.mirror = dev(part.mirror)
-        self.m_ptr, self.m_idx, self.m_rows = dev(mc_ptr), dev(mc_idx), dev(targets)
+        self.m_ptr, self.m_idx, self.m_rows = dev(mc_ptr), dev(m_idx), dev(targets)
         self.h_m_ptr = mc_ptr
 
         self.set_bits(part.bits if bits is None else bits)

@@ -128,17 +128,6 @@ def test_agg_plan_covers_every_edge_and_row_once(skip_empty, group_edges):
     assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 8
 
 
-@pytest.mark.parametrize("lens, unit", [([1, 1, 1, 1], 1), ([1], 1), ([1, 2, 1], 0), ([1, 0, 1], 0),
-                                        ([0], 0), ([3], 0)])
-def test_agg_plan_marks_one_edge_rows(lens, unit):
-    """unit_rows is set exactly when every row holds one edge (empty rows and longer rows clear it)."""
-    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    st, items, _, _ = _plan_host(ptr, 512, False)
-    assert st.unit_rows == unit
-    if unit:                                   # with one edge a row, row r's edge is edge r
-        assert np.array_equal(ptr, np.arange(len(lens) + 1))
-
-
 def test_device_calls_reject_bad_arguments_before_any_hip_call():
     q = B._quantize_pack
     # unsupported width
@@ -189,16 +178,6 @@ def test_device_calls_reject_bad_arguments_before_any_hip_call():
     assert call(n_rows=3, plan=C.byref(st2)) == B.QHA_ERR_WORKSPACE
     # plan built for another row count
     assert call(n_rows=4, plan=C.byref(st2)) == B.QHA_ERR_INVALID_ARG
-    # a one-edge-row flag that its counts contradict (split rows, or a value other than 0 / 1)
-    ws = np.zeros(1 << 16, np.float64)
-    st2.unit_rows = 1
-    assert call(n_rows=3, plan=C.byref(st2), ws=ws.ctypes.data, wsb=ws.nbytes) == B.QHA_ERR_INVALID_ARG
-    assert "unit_rows" in B._last_error().decode()
-    st3, *_ = _plan_host(np.arange(4, dtype=np.int32), 512, False)
-    st3.items = st3.split_row = st3.split_ptr = FAKE
-    assert st3.unit_rows == 1
-    st3.unit_rows = 2
-    assert call(n_rows=3, plan=C.byref(st3)) == B.QHA_ERR_INVALID_ARG
 
     g = B._aggregate_bwd
     assert g(10, FAKE, FAKE, None, None, FAKE, 128, 10, 128, 3, FAKE, 128, None, 0, None) == B.QHA_ERR_INVALID_ARG
