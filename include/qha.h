@@ -269,8 +269,11 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
  * beta = 0) runs as a row-panel kernel with W's parts held on chip; other shapes as tiled
  * products.  When m*n is small and k large the reduction is split over k
  * into float64 partials in the workspace (device, 16-byte aligned, qha_dense_project_workspace
- * bytes) and summed in a fixed order; results are deterministic.  beta is 0 or 1.
- * Errors: INVALID_ARG, WORKSPACE, HIP. */
+ * bytes) and summed in a fixed order; results are deterministic.  A tiled product with
+ * trans_a = 0, no split and at least 16384 rows splits B into its bf16 parts once per call when
+ * the workspace holds them (qha_dense_project_workspace counts them; with less, or none, B is
+ * split per tile): the same bits either way.  beta is 0 or 1.
+ * Errors: INVALID_ARG, WORKSPACE (a split reduction without room for its partials), HIP. */
 int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k,
                       const float* a, int64_t lda, const float* b, int64_t ldb,
                       int32_t beta, float* c, int64_t ldc,
@@ -290,9 +293,11 @@ size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, 
  * products, both products run on the bf16 matrix cores with the three-way split of
  * qha_dense_project's width-128 forward (W's parts held on chip), and per-block dW partials
  * (workspace) are added in a fixed order.  Other widths run as the two qha_dense_project
- * products.  dA sums are chains of 32 products accumulated in float32 and added in float64; dW
+ * products (dA's W split once into the workspace when it has room, before dW's partials use
+ * it).  dA sums are chains of 32 products accumulated in float32 and added in float64; dW
  * adds float32 sums over each block's rows in float64.  workspace: device, 16-byte aligned,
- * qha_dense_backward_workspace bytes.  Results are deterministic.
+ * qha_dense_backward_workspace bytes (less only where the partials still fit).  Results are
+ * deterministic.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */
 int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t ldg, const float* h, int64_t ldh,
                        const float* a, int64_t lda, const float* w, int64_t ldw, float* da, int64_t ldda,

@@ -507,14 +507,20 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
                     "aggregate_bwd_quantize");
 }
 
-size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k) {
-  (void)trans_a;
-  (void)trans_b;
+// Workspace a tiled product cannot run without: its split-k partials.
+static size_t gemm_required_bytes(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
   int32_t s;
   int64_t kps;
   qha::gemm_split_rule(m, n, k, &s, &kps);
   return s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(m) * static_cast<size_t>(n) * sizeof(double) : 0;
+}
+
+size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k) {
+  (void)trans_b;
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  const size_t req = gemm_required_bytes(m, n, k), pre = qha::gemm_bsplit_bytes(trans_a, m, n, k);
+  return req > pre ? req : pre;
 }
 
 int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, const float* a, int64_t lda,
@@ -572,18 +578,32 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
   qha::gemm_split_rule(m, n, k, &g.splits, &g.k_per_split);
   g.ws = static_cast<double*>(workspace);
   if (g.splits > 1) {
-    const size_t need = qha_dense_project_workspace(trans_a, trans_b, m, n, k);
+    const size_t need = gemm_required_bytes(m, n, k);
     if (!workspace || workspace_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
     if (!aligned16(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
   }
+  // B split once per call when the workspace has room for its parts (the same bits either way)
+  const size_t pre = qha::gemm_bsplit_bytes(trans_a, m, n, k);
+  g.bsplit = (pre > 0 && workspace && aligned16(workspace) && workspace_bytes >= pre) ? static_cast<uint32_t*>(workspace)
+                                                                                       : nullptr;
   return hip_status(qha::launch_gemm(g, static_cast<hipStream_t>(stream)), "dense_project");
 }
 
-size_t qha_dense_backward_workspace(int64_t m, int64_t n, int64_t k) {
+// Workspace the backward cannot run without: the panel path's dW partials, or the split-k
+// partials of dW = dZ^T A.
+static size_t dense_bwd_required_bytes(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
   if (qha::panel_fits(n, k)) return qha::panel_bwd_workspace(m);
-  // dA = dZ W needs none; dW = dZ^T A may split its m-long reduction
-  return qha_dense_project_workspace(1, 0, n, k, m);
+  return gemm_required_bytes(n, k, m);
+}
+
+size_t qha_dense_backward_workspace(int64_t m, int64_t n, int64_t k) {
+  const size_t req = dense_bwd_required_bytes(m, n, k);
+  if (m <= 0 || n <= 0 || k <= 0 || qha::panel_fits(n, k)) return req;
+  // dA = dZ W may split W once into the same workspace (dW's partials are written after dA has
+  // read W's parts, on the same stream)
+  const size_t pre = qha::gemm_bsplit_bytes(0, m, k, n);
+  return req > pre ? req : pre;
 }
 
 int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t ldg, const float* h, int64_t ldh,
@@ -600,7 +620,7 @@ int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t
     if (!a || lda < k || (lda & 3) || !aligned16(a)) return fail(QHA_ERR_INVALID_ARG, "A / lda out of contract");
     if (!da || ldda < k || !aligned4(da)) return fail(QHA_ERR_INVALID_ARG, "dA / ldda out of contract");
   }
-  const size_t need = qha_dense_backward_workspace(m, n, k);
+  const size_t need = dense_bwd_required_bytes(m, n, k);
   if (need) {
     if (!workspace || workspace_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
     if (!aligned16(workspace)) return fail(QHA_ERR_INVALID_ARG, "workspace misaligned");
@@ -634,9 +654,13 @@ int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t
     g.pro = QHA_PRO_RELU_MASK; g.aux = h; g.ld_aux = ldh; g.epi = QHA_EPI_NONE;
     qha::gemm_split_rule(g.m, g.n, g.k, &g.splits, &g.k_per_split);
     if (g.splits > 1) return fail(QHA_ERR_INVALID_ARG, "unexpected split of dA");
+    const size_t pre = qha::gemm_bsplit_bytes(0, g.m, g.n, g.k);
+    g.bsplit = (pre > 0 && workspace && aligned16(workspace) && workspace_bytes >= pre)
+                   ? static_cast<uint32_t*>(workspace) : nullptr;
     const int st = hip_status(qha::launch_gemm(g, s), "dense_backward");
     if (st) return st;
   }
+  g.bsplit = nullptr;
   g.ta = 1; g.tb = 0; g.m = n; g.n = k; g.k = m;
   g.a = dh; g.lda = m > 0 ? ldg : n; g.b = a; g.ldb = m > 0 ? lda : k; g.beta = 0; g.c = dw; g.ldc = lddw;
   g.pro = m > 0 ? QHA_PRO_RELU_MASK : QHA_PRO_NONE; g.aux = h; g.ld_aux = m > 0 ? ldh : n; g.epi = QHA_EPI_NONE;

@@ -14,6 +14,9 @@
 // staged k-contiguous ([row][k] for A, [column][k] for B, 40 bf16 per row so that the 16-byte
 // operand reads and the 8-byte staging writes hit distinct banks); operands stored k-major are
 // read four k at a time with coalesced 4-byte loads, which transposes them on the way in.
+// When A has many rows and the caller's workspace has room, B (the weights) is split once per call
+// by split_b_kernel into three k-contiguous bf16 planes, and its tiles are then copied into LDS
+// with 16-byte loads instead of being split again by every block (the same parts, so the same bits).
 // The next tile's global loads are issued before the current tile is consumed.  Each 32-wide k
 // step accumulates into fresh fp32 MFMA accumulators that are then added into float64 running
 // sums, so a long dot product is rounded in float32 only over 32 terms at a time (for K = 512 this
@@ -27,6 +30,7 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 64;
 constexpr int BK = 32;
@@ -41,6 +45,9 @@ struct Tile {
   static constexpr int B_LOADS = BN * BK / 4 / NT;
 };
 int tile_n(int64_t n) { return n >= 512 ? 256 : 128; }
+// B is split once per call (into the workspace) when A has at least this many rows: below it the
+// per-tile split of B costs little and the extra launch would not pay
+constexpr int64_t kBSplitMinRows = 16384;
 
 // x = hi + mid + lo exactly for a pair of values, as packed bf16 words (first value in the low
 // half): each part is rounded to nearest even, and the remainders x - hi and (x - hi) - mid are
@@ -147,7 +154,85 @@ __device__ __forceinline__ void store_tiles(__bf16* As, __bf16* Bs, int tid, con
   }
 }
 
-template <int BN, bool TA, bool TB, bool MASK, bool SPLIT>
+// B's parts split once per call: plane q holds part q (hi, mid, lo) of B's column j at
+// [q][j][kk] as bf16, rows padded to the column tile and k to BK with zeros, so the tiles need no
+// range checks.  The split is split_pair's, so the staged parts equal those of the per-tile split.
+__global__ __launch_bounds__(256) void split_b_kernel(const float* b, int64_t ldb, int32_t tb, int64_t n, int64_t k,
+                                                      uint32_t* planes, int64_t n_pad, int64_t k_pad) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // a pair (j, 2 kq .. + 1)
+  const int64_t pairs = n_pad * (k_pad / 2);
+  if (i >= pairs) return;
+  const int64_t j = i / (k_pad / 2), kk = 2 * (i % (k_pad / 2));
+  float v[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bool ok = j < n && kk + t < k;
+    v[t] = ok ? b[tb ? j * ldb + kk + t : (kk + t) * ldb + j] : 0.0f;
+  }
+  uint32_t h, m, l;
+  split_pair(v[0], v[1], h, m, l);
+  planes[i] = h;
+  planes[pairs + i] = m;
+  planes[2 * pairs + i] = l;
+}
+
+// 16-byte chunks of B's split parts per thread and k step: 3 planes x BN columns x BK bf16
+template <int BN>
+constexpr int kBChunks = 3 * BN * BK / 8 / Tile<BN>::NT;
+
+template <int BN>
+__device__ __forceinline__ void load_bsplit(const GemmArgs& p, int tid, int64_t n0, int64_t k0, u32x4 (&rq)[kBChunks<BN>]) {
+  const int64_t kc = (p.k + BK - 1) / BK * (BK / 8);              // 16-byte chunks per padded column
+  const int64_t plane = (p.n + BN - 1) / BN * BN * kc;
+  const u32x4* src = reinterpret_cast<const u32x4*>(p.bsplit);
+#pragma unroll
+  for (int s = 0; s < kBChunks<BN>; ++s) {
+    const int c = tid + Tile<BN>::NT * s;
+    const int q = c / (BN * BK / 8), r = c % (BN * BK / 8);
+    rq[s] = src[q * plane + (n0 + r / (BK / 8)) * kc + k0 / 8 + r % (BK / 8)];
+  }
+}
+
+template <int BN>
+__device__ __forceinline__ void store_bsplit(__bf16* Bs, int tid, const u32x4 (&rq)[kBChunks<BN>]) {
+#pragma unroll
+  for (int s = 0; s < kBChunks<BN>; ++s) {
+    const int c = tid + Tile<BN>::NT * s;
+    const int q = c / (BN * BK / 8), r = c % (BN * BK / 8);
+    *reinterpret_cast<u32x4*>(Bs + q * BN * KS + (r / (BK / 8)) * KS + 8 * (r % (BK / 8))) = rq[s];
+  }
+}
+
+// One k step's global loads and its staging: with PB, B's tiles are copied from its parts split
+// once per call (p.bsplit) instead of being split here.
+template <int BN, bool TA, bool TB, bool MASK, bool PB, int NB, int NQ>
+__device__ __forceinline__ void load_step(const GemmArgs& p, int tid, int64_t m0, int64_t n0, int64_t k0, int64_t kend,
+                                          float4 (&ra)[Tile<BN>::A_LOADS], float4 (&rb)[NB], u32x4 (&rq)[NQ]) {
+  if constexpr (PB) {
+    load_k4<TA, BM, Tile<BN>::A_LOADS, Tile<BN>::NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra);
+    load_bsplit<BN>(p, tid, n0, k0, rq);
+  } else {
+    load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, k0, kend, ra, rb);
+  }
+}
+
+template <int BN, bool TA, bool TB, bool PB, int NB, int NQ>
+__device__ __forceinline__ void stage_step(__bf16* As, __bf16* Bs, int tid, const float4 (&ra)[Tile<BN>::A_LOADS],
+                                           const float4 (&rb)[NB], const u32x4 (&rq)[NQ]) {
+  if constexpr (PB) {
+#pragma unroll
+    for (int s = 0; s < Tile<BN>::A_LOADS; ++s) {
+      const int f = tid + Tile<BN>::NT * s;
+      if (!TA) stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), ra[s]);
+      else stage_k4<BM>(As, f % BM, 4 * (f / BM), ra[s]);
+    }
+    store_bsplit<BN>(Bs, tid, rq);
+  } else {
+    store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
+  }
+}
+
+template <int BN, bool TA, bool TB, bool MASK, bool SPLIT, bool PB>
 __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) __bf16 As[3 * BM * KS];
   __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * BN * KS];
@@ -170,16 +255,17 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum[j][r] = 0.0;
 
-  float4 ra[Tile<BN>::A_LOADS], rb[Tile<BN>::B_LOADS];
+  float4 ra[Tile<BN>::A_LOADS], rb[PB ? 1 : Tile<BN>::B_LOADS];
+  u32x4 rq[PB ? kBChunks<BN> : 1];
 
   if (kbeg < kend) {
-    load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, kbeg, kend, ra, rb);
-    store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
+    load_step<BN, TA, TB, MASK, PB>(p, tid, m0, n0, kbeg, kend, ra, rb, rq);
+    stage_step<BN, TA, TB, PB>(As, Bs, tid, ra, rb, rq);
     __syncthreads();
   }
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
-    if (more) load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, k0 + BK, kend, ra, rb);
+    if (more) load_step<BN, TA, TB, MASK, PB>(p, tid, m0, n0, k0 + BK, kend, ra, rb, rq);
     floatx16 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -207,7 +293,7 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) sum[ni][r] += static_cast<double>(acc[ni][r]);
     __syncthreads();
     if (more) {
-      store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
+      stage_step<BN, TA, TB, PB>(As, Bs, tid, ra, rb, rq);
       __syncthreads();
     }
   }
@@ -250,10 +336,22 @@ template <int BN, bool TA, bool TB, bool MASK>
 hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p.m + BM - 1) / BM), static_cast<unsigned>((p.n + BN - 1) / BN),
                   static_cast<unsigned>(p.splits));
+  if constexpr (!TA) {
+    if (p.bsplit != nullptr && p.splits == 1) {
+      const int64_t n_pad = (p.n + BN - 1) / BN * BN, k_pad = (p.k + BK - 1) / BK * BK;
+      const int64_t pairs = n_pad * (k_pad / 2);
+      hipLaunchKernelGGL(split_b_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, s, p.b,
+                         p.ldb, p.tb, p.n, p.k, p.bsplit, n_pad, k_pad);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, true>), grid, dim3(Tile<BN>::NT), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (p.splits > 1)
-    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true>), grid, dim3(Tile<BN>::NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;
   const int64_t mn = p.m * p.n;
@@ -285,6 +383,15 @@ void gemm_split_rule(int64_t m, int64_t n, int64_t k, int32_t* splits, int64_t* 
   if (s < 1) s = 1;
   *splits = static_cast<int32_t>(s);
   *k_per_split = s == 1 ? (k < 1 ? 1 : k) : kps;
+}
+
+size_t gemm_bsplit_bytes(int32_t ta, int64_t m, int64_t n, int64_t k) {
+  int32_t splits;
+  int64_t kps;
+  gemm_split_rule(m, n, k, &splits, &kps);
+  if (ta || splits != 1 || m < kBSplitMinRows || n <= 0 || k <= 0) return 0;
+  const int64_t bn = tile_n(n);
+  return static_cast<size_t>(3 * ((n + bn - 1) / bn * bn) * ((k + BK - 1) / BK * BK) * 2);
 }
 
 hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {

@@ -103,6 +103,8 @@ struct GemmArgs {
   double* ws;          // float64 split-k partials [splits, m, n]
   int32_t splits;
   int64_t k_per_split;
+  uint32_t* bsplit;    // workspace for B's three bf16 parts, split once per call (nullptr: B is
+                       // split as its tiles are staged); used when A is not transposed and k is not split
 };
 
 // Row-panel products of width-128 layers (W's split parts held on chip, row panels streamed).
@@ -133,6 +135,9 @@ hipError_t launch_panel_bwd(const PanelArgs& p, hipStream_t s);
 
 // Split-k rule shared by the workspace query and the launcher.
 void gemm_split_rule(int64_t m, int64_t n, int64_t k, int32_t* splits, int64_t* k_per_split);
+// Bytes of B's split parts when splitting B once per call pays (A not transposed, k not split and
+// enough rows of A), else 0.
+size_t gemm_bsplit_bytes(int32_t ta, int64_t m, int64_t n, int64_t k);
 
 hipError_t launch_degree_norm(const int32_t* deg, int64_t n, int32_t kind, float* out, hipStream_t s);
 hipError_t launch_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r,

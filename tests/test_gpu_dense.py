@@ -245,3 +245,62 @@ def test_general_width_error_is_float32_class(m, d_in, d_out):
     assert e_f.max() <= 8 * 2.0 ** -24, f"forward: {e_f.max() * 2**24:.2f} units of 2^-24"
     assert e_da.max() <= 8 * 2.0 ** -24, f"dA: {e_da.max() * 2**24:.2f} units of 2^-24"
     assert e_dw.max() <= 16 * 2.0 ** -24, f"dW: {e_dw.max() * 2**24:.2f} units of 2^-24"
+
+
+@pytest.mark.parametrize("m,n,k,tb,mask", [(20000, 256, 512, 1, False), (20000, 512, 256, 0, True),
+                                           (16384, 516, 64, 1, False), (17001, 52, 132, 0, True),
+                                           (16383, 256, 512, 1, False)])
+def test_b_split_once_gives_the_same_bits(m, n, k, tb, mask):
+    """With a workspace of qha_dense_project_workspace bytes, a product over at least 16384 rows of
+    A splits B into its bf16 parts once per call instead of per tile; the bits must not change
+    (same parts, same products, same order): ragged n and k, both storage orders of B, the ReLU
+    mask, and a row count just below the threshold (no split, same bits trivially)."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(m + n + k)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    b = (rng.standard_normal((n, k) if tb else (k, n)) / np.sqrt(k)).astype(np.float32)
+    b[0, :7] = -0.0
+    aux = np.where(rng.random((m, k)) < 0.5, -1.0, 1.0).astype(np.float32) if mask else None
+    pro = B.PRO_RELU_MASK if mask else B.PRO_NONE
+    ws_bytes = B.dense_project_workspace(0, tb, m, n, k)
+    assert (ws_bytes > 0) == (m >= 16384)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    a_d, b_d = H.dev(a), H.dev(b)
+    aux_d = H.dev(aux) if mask else None
+    outs = []
+    for w in (ws, None):
+        H.note(f"b split once m={m} n={n} k={k} tb={tb} mask={mask} ws={w is not None}")
+        c = torch.full((m, n), np.nan, dtype=torch.float32, device="cuda")
+        B.dense_project(0, tb, a_d, b_d, 0, c, prologue=pro, aux=aux_d, workspace=w)
+        outs.append(H.host(c))
+    H.assert_bits_equal(outs[0], outs[1], "B split once against B split per tile")
+    a64 = np.where(aux > 0, a, 0.0) if mask else a.astype(np.float64)
+    b64 = b.astype(np.float64)
+    H.assert_close(outs[0], a64 @ (b64.T if tb else b64), what="op(A) op(B)")
+
+
+def test_backward_b_split_once_matches_dense_project():
+    """qha_dense_backward at general widths: its dA (W split once into the workspace that dW's
+    partials reuse afterwards) equals the per-tile split of qha_dense_project bit for bit."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    m, n, k = 20000, 256, 512
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    w = (rng.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
+    h = np.where(rng.random((m, n)) < 0.5, 0.0, 1.0).astype(np.float32)
+    dh = rng.standard_normal((m, n)).astype(np.float32)
+    dh_d, h_d, a_d, w_d = H.dev(dh), H.dev(h), H.dev(a), H.dev(w)
+    wsb = torch.empty(B.dense_backward_workspace(m, n, k) // 4 + 1, dtype=torch.float32, device="cuda")
+    H.note("dense_backward dA against dense_project dA")
+    da = torch.full((m, k), np.nan, dtype=torch.float32, device="cuda")
+    dw = torch.full((n, k), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_backward(dh_d, h_d, a_d, w_d, da, dw, workspace=wsb)
+    da2 = torch.full((m, k), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(0, 0, dh_d, w_d, 0, da2, prologue=B.PRO_RELU_MASK, aux=h_d)
+    H.assert_bits_equal(H.host(da), H.host(da2), "dA")
+    _, dw_ref = OD.project_backward(a, w, h, dh)
+    H.assert_close_normwise(H.host(dw), dw_ref, what="dW after dA's use of the workspace")
