@@ -263,6 +263,8 @@ def main():
         print(f"[bench] asynchronous epochs: {a_ms:.3f} ms/step", file=sys.stderr, flush=True)
         del ast
 
+    copy_gbs = stream_copy_gbs()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(part, bytes_by_stage)
@@ -278,6 +280,8 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "instrumented_pass": {"ms_per_step": round(inst_ms_step, 4), "stage_events_ms_per_step": round(gpu_ms_step, 4)},
         "kernel_quant_aggregate_gbs": round(kernel_qa_gbs, 1),
+        "stream_copy": {"gbs": round(copy_gbs, 1), "value_pct": round(100 * value / copy_gbs, 2),
+                        "kernel_quant_aggregate_pct": round(100 * kernel_qa_gbs / copy_gbs, 2)},
         "g_edge_feat_per_s": {"aggregate_fwd": round(gef_agg, 2), "full_layer": round(gef_layer, 2)},
         "quant_aggregate_bytes_per_step": qa_bytes_step,
         "message_bytes": {"main": int(4 * hw.sum()), "scales": 8 * n_h},
@@ -383,6 +387,25 @@ def measured_traffic(workload, stage):
                 if kv.get("src") == want and "bytes_per_call" in kv:
                     return int(kv["bytes_per_call"])
     return None
+
+
+def stream_copy_gbs(mib=1024, reps=5):
+    """A STREAM-style device copy on this GPU (read + write bytes per second), after the timed
+    region: the practical streaming rate that the headline rates are also quoted against."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def calibrate_copy(mib):
