@@ -31,6 +31,7 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data, range-checked against num_records
 
 constexpr int BM = 64;
 constexpr int BK = 32;
@@ -94,7 +95,39 @@ __device__ __forceinline__ floatx16 mfma6(const bf16x8& ah, const bf16x8& am, co
 // operand's first element instead (no branch around the loads).
 template <bool TRANS, int ROWS, int NL, int NT>
 __device__ __forceinline__ void load_k4(const float* x, int64_t ld, const float* aux, int64_t ld_aux, bool mask,
-                                        int64_t r0, int64_t rows, int64_t k0, int64_t kend, int tid, float4 (&v)[NL]) {
+                                        int64_t r0, int64_t rows, int64_t k0, int64_t kend, int tid, float4 (&v)[NL],
+                                        bool buf32 = false) {
+  if (TRANS && buf32) {
+    // k-major operand within 2 GiB: range-checked buffer loads at 32-bit offsets.  The buffer ends
+    // at row kend, so reads past the k range return 0 by themselves; lanes past the last column get
+    // an offset beyond every buffer.  The four k of a float4 differ by a scalar offset.
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x), 0, static_cast<int32_t>(kend * ld * 4), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(mask ? aux : x), 0, static_cast<int32_t>(kend * (mask ? ld_aux : ld) * 4), kBufferWord3);
+#pragma unroll
+    for (int s = 0; s < NL; ++s) {
+      const int f = tid + NT * s;
+      const int row = f % ROWS;
+      const int kq = f / ROWS;
+      const int64_t gr = r0 + row, gk = k0 + 4 * kq;
+      const bool ok = gr < rows;
+      const uint32_t ox = ok ? static_cast<uint32_t>((gk * ld + gr) * 4) : 0x80000000u;
+      const uint32_t oa = ok ? static_cast<uint32_t>((gk * ld_aux + gr) * 4) : 0x80000000u;
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, ox, static_cast<int32_t>(j * ld * 4), 0));
+        if (mask) {
+          const float a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, oa, static_cast<int32_t>(j * ld_aux * 4), 0));
+          t = a > 0.0f ? t : 0.0f;
+        }
+        e[j] = t;
+      }
+      v[s] = make_float4(e[0], e[1], e[2], e[3]);
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < NL; ++s) {
     const int f = tid + NT * s;
@@ -132,8 +165,8 @@ __device__ __forceinline__ void load_k4(const float* x, int64_t ld, const float*
 template <int BN, bool TA, bool TB, bool MASK>
 __device__ __forceinline__ void load_tiles(const GemmArgs& p, int tid, int64_t m0, int64_t n0, int64_t k0, int64_t kend,
                                            float4 (&ra)[Tile<BN>::A_LOADS], float4 (&rb)[Tile<BN>::B_LOADS]) {
-  load_k4<TA, BM, Tile<BN>::A_LOADS, Tile<BN>::NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra);
-  load_k4<!TB, BN, Tile<BN>::B_LOADS, Tile<BN>::NT>(p.b, p.ldb, nullptr, 0, false, n0, p.n, k0, kend, tid, rb);
+  load_k4<TA, BM, Tile<BN>::A_LOADS, Tile<BN>::NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra, p.buf32 != 0);
+  load_k4<!TB, BN, Tile<BN>::B_LOADS, Tile<BN>::NT>(p.b, p.ldb, nullptr, 0, false, n0, p.n, k0, kend, tid, rb, p.buf32 != 0);
 }
 
 // registers -> the k-contiguous bf16 planes of the tiles
@@ -394,8 +427,16 @@ size_t gemm_bsplit_bytes(int32_t ta, int64_t m, int64_t n, int64_t k) {
   return static_cast<size_t>(3 * ((n + bn - 1) / bn * bn) * ((k + BK - 1) / BK * BK) * 2);
 }
 
-hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
-  if (p.m == 0 || p.n == 0) return hipSuccess;
+hipError_t launch_gemm(const GemmArgs& p0, hipStream_t s) {
+  if (p0.m == 0 || p0.n == 0) return hipSuccess;
+  // k-major operands (and the mask beside A) are read with 32-bit buffer offsets when every one
+  // of them spans less than 2 GiB
+  GemmArgs p = p0;
+  const int64_t lim = int64_t(1) << 31;
+  bool fits = true;
+  if (p.ta) fits = fits && p.k * p.lda * 4 < lim && (p.pro != 1 || p.k * p.ld_aux * 4 < lim);
+  if (!p.tb) fits = fits && p.k * p.ldb * 4 < lim;
+  p.buf32 = fits ? 1 : 0;
   const bool mask = p.pro == 1;
   if (!p.ta && p.tb && !mask) return launch_variant<false, true, false>(p, s);
   if (!p.ta && p.tb && mask) return launch_variant<false, true, true>(p, s);

@@ -105,6 +105,7 @@ struct GemmArgs {
   int64_t k_per_split;
   uint32_t* bsplit;    // workspace for B's three bf16 parts, split once per call (nullptr: B is
                        // split as its tiles are staged); used when A is not transposed and k is not split
+  int32_t buf32;       // set by the launcher: k-major operands are read with 32-bit buffer offsets
 };
 
 // Row-panel products of width-128 layers (W's split parts held on chip, row panels streamed).
