@@ -13,7 +13,8 @@
 // below 2^-23 of the product, about one float32 rounding).  K advances 32 at a time; the tiles are
 // staged k-contiguous ([row][k] for A, [column][k] for B, 40 bf16 per row so that the 16-byte
 // operand reads and the 8-byte staging writes hit distinct banks); operands stored k-major are
-// read four k at a time with coalesced 4-byte loads, which transposes them on the way in.
+// read four k at a time with coalesced 4-byte loads, which transposes them on the way in (range-
+// checked buffer loads at 32-bit offsets when they span under 2 GiB, else 64-bit addresses).
 // When A has many rows and the caller's workspace has room, B (the weights) is split once per call
 // by split_b_kernel into three k-contiguous bf16 planes, and its tiles are then copied into LDS
 // with 16-byte loads instead of being split again by every block (the same parts, so the same bits).

@@ -304,3 +304,30 @@ def test_backward_b_split_once_matches_dense_project():
     H.assert_bits_equal(H.host(da), H.host(da2), "dA")
     _, dw_ref = OD.project_backward(a, w, h, dh)
     H.assert_close_normwise(H.host(dw), dw_ref, what="dW after dA's use of the workspace")
+
+
+def test_k_major_operand_beyond_2gib():
+    """A k-major operand spanning more than 2 GiB (a 64-column slice of rows 16 KiB apart) is read
+    with 64-bit addresses instead of 32-bit buffer offsets: the same bits as the contiguous copy,
+    which takes the buffer loads, and the oracle's weight-gradient sum."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    m, n, k, ld = 140000, 16, 64, 4096
+    assert m * ld * 4 >= 2 ** 31
+    rng = np.random.default_rng(11)
+    dz = rng.standard_normal((m, n)).astype(np.float32)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    H.note(f"k-major operand beyond 2 GiB: m={m} ld={ld}")
+    big = torch.zeros((m, ld), dtype=torch.float32, device="cuda")
+    big[:, :k] = H.dev(a)
+    dz_d = H.dev(dz)
+    outs = []
+    for b_op in (big[:, :k], big[:, :k].contiguous()):
+        ws = torch.empty(max(B.dense_project_workspace(1, 0, n, k, m), 16) // 4 + 4, dtype=torch.float32, device="cuda")
+        c = torch.full((n, k), np.nan, dtype=torch.float32, device="cuda")
+        B.dense_project(1, 0, dz_d, b_op, 0, c, workspace=ws)
+        outs.append(H.host(c))
+    del big
+    H.assert_bits_equal(outs[0], outs[1], "strided beyond 2 GiB against contiguous")
+    H.assert_close_normwise(outs[0], dz.astype(np.float64).T @ a.astype(np.float64), what="dZ^T A")
