@@ -50,6 +50,10 @@ int tile_n(int64_t n) { return n >= 512 ? 256 : 128; }
 // B is split once per call (into the workspace) when A has at least this many rows: below it the
 // per-tile split of B costs little and the extra launch would not pay
 constexpr int64_t kBSplitMinRows = 16384;
+constexpr int64_t kXcds = 8;        // accelerator complex dies of an MI355X, each with its own L2
+#ifndef QHA_GEMM_ORDER
+#define QHA_GEMM_ORDER 2
+#endif
 
 // x = hi + mid + lo exactly for a pair of values, as packed bf16 words (first value in the low
 // half): each part is rounded to nearest even, and the remainders x - hi and (x - hi) - mid are
@@ -278,8 +282,24 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
   const int wn = wid % (BN / 64);   // 64-column slice
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  int64_t mbk = blockIdx.x, nbk = blockIdx.y;
+  if constexpr (!SPLIT && QHA_GEMM_ORDER > 0) {
+    // one-dimensional grid: the column tiles of a row tile are consecutive blocks (order 1), or
+    // consecutive blocks of one XCD (order 2: blocks are dealt to the eight XCDs in turn), so that
+    // A's rows, read once per column tile, come from cache the second time
+    const int64_t nb = (p.n + BN - 1) / BN, b = blockIdx.x;
+    if constexpr (QHA_GEMM_ORDER == 1) {
+      nbk = b % nb;
+      mbk = b / nb;
+    } else {
+      const int64_t sl = b / kXcds;
+      nbk = sl % nb;
+      mbk = sl / nb * kXcds + b % kXcds;
+      if (mbk * BM >= p.m) return;     // the padding of the last group of XCD rows
+    }
+  }
+  const int64_t m0 = mbk * BM;
+  const int64_t n0 = nbk * BN;
   const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * p.k_per_split;
   const int64_t kend = min(p.k, kbeg + p.k_per_split);
 
@@ -368,8 +388,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 
 template <int BN, bool TA, bool TB, bool MASK>
 hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((p.m + BM - 1) / BM), static_cast<unsigned>((p.n + BN - 1) / BN),
-                  static_cast<unsigned>(p.splits));
+  const int64_t mb = (p.m + BM - 1) / BM, nb = (p.n + BN - 1) / BN;
+  const dim3 grid(static_cast<unsigned>(mb), static_cast<unsigned>(nb), static_cast<unsigned>(p.splits));
+  // the unsplit kernels run on a one-dimensional grid in the order described in gemm_kernel
+  const dim3 grid1(static_cast<unsigned>(QHA_GEMM_ORDER == 2 ? (mb + kXcds - 1) / kXcds * kXcds * nb : mb * nb));
+  const dim3 gridu = QHA_GEMM_ORDER > 0 ? grid1 : grid;
   if constexpr (!TA) {
     if (p.bsplit != nullptr && p.splits == 1) {
       const int64_t n_pad = (p.n + BN - 1) / BN * BN, k_pad = (p.k + BK - 1) / BK * BK;
@@ -378,14 +401,14 @@ hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
                          p.ldb, p.tb, p.n, p.k, p.bsplit, n_pad, k_pad);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, true>), grid, dim3(Tile<BN>::NT), 0, s, p);
+      hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, true>), gridu, dim3(Tile<BN>::NT), 0, s, p);
       return hipGetLastError();
     }
   }
   if (p.splits > 1)
     hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, false>), gridu, dim3(Tile<BN>::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;
   const int64_t mn = p.m * p.n;
