@@ -282,7 +282,17 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
   const int wn = wid % (BN / 64);   // 64-column slice
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  int64_t mbk = blockIdx.x, nbk = blockIdx.y;
+  int64_t mbk = blockIdx.x, nbk = blockIdx.y, zk = blockIdx.z;
+  if constexpr (SPLIT && QHA_GEMM_ORDER == 2) {
+    // split reductions on a one-dimensional grid: the output tiles of one k range are consecutive
+    // blocks of one XCD, so the rows of that range, which every tile reads, are shared in its L2
+    const int64_t mb = (p.m + BM - 1) / BM, tiles = mb * ((p.n + BN - 1) / BN), b = blockIdx.x;
+    const int64_t sl = b / kXcds, t = sl % tiles;
+    zk = sl / tiles * kXcds + b % kXcds;
+    if (zk >= p.splits) return;        // the padding of the last group of XCD splits
+    mbk = t % mb;
+    nbk = t / mb;
+  }
   if constexpr (!SPLIT && QHA_GEMM_ORDER > 0) {
     // one-dimensional grid: the column tiles of a row tile are consecutive blocks (order 1), or
     // consecutive blocks of one XCD (order 2: blocks are dealt to the eight XCDs in turn), so that
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
   }
   const int64_t m0 = mbk * BM;
   const int64_t n0 = nbk * BN;
-  const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * p.k_per_split;
+  const int64_t kbeg = zk * p.k_per_split;
   const int64_t kend = min(p.k, kbeg + p.k_per_split);
 
   double sum[2][16];
@@ -362,7 +372,7 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
       if (grow < p.m && gcol < p.n) {
         const double s = sum[ni][r];
         if (SPLIT) {
-          p.ws[static_cast<int64_t>(blockIdx.z) * p.m * p.n + grow * p.n + gcol] = s;
+          p.ws[zk * p.m * p.n + grow * p.n + gcol] = s;
         } else {
           float* dst = p.c + grow * p.ldc + gcol;
           float v = static_cast<float>(p.beta ? static_cast<double>(*dst) + s : s);
@@ -393,6 +403,8 @@ hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
   // the unsplit kernels run on a one-dimensional grid in the order described in gemm_kernel
   const dim3 grid1(static_cast<unsigned>(QHA_GEMM_ORDER == 2 ? (mb + kXcds - 1) / kXcds * kXcds * nb : mb * nb));
   const dim3 gridu = QHA_GEMM_ORDER > 0 ? grid1 : grid;
+  const dim3 grids = QHA_GEMM_ORDER == 2 ? dim3(static_cast<unsigned>((p.splits + kXcds - 1) / kXcds * kXcds * mb * nb))
+                                         : grid;
   if constexpr (!TA) {
     if (p.bsplit != nullptr && p.splits == 1) {
       const int64_t n_pad = (p.n + BN - 1) / BN * BN, k_pad = (p.k + BK - 1) / BK * BK;
@@ -406,7 +418,7 @@ hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
     }
   }
   if (p.splits > 1)
-    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true, false>), grid, dim3(Tile<BN>::NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true, false>), grids, dim3(Tile<BN>::NT), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, false>), gridu, dim3(Tile<BN>::NT), 0, s, p);
   hipError_t e = hipGetLastError();
