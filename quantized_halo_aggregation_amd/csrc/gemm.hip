@@ -399,6 +399,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 template <int BN, bool TA, bool TB, bool MASK>
 hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
   const int64_t mb = (p.m + BM - 1) / BM, nb = (p.n + BN - 1) / BN;
+  if ((mb + kXcds) * nb * (p.splits + kXcds) > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;   // grid size
   const dim3 grid(static_cast<unsigned>(mb), static_cast<unsigned>(nb), static_cast<unsigned>(p.splits));
   // the unsplit kernels run on a one-dimensional grid in the order described in gemm_kernel
   const dim3 grid1(static_cast<unsigned>(QHA_GEMM_ORDER == 2 ? (mb + kXcds - 1) / kXcds * kXcds * nb : mb * nb));
