@@ -97,34 +97,45 @@ __device__ __forceinline__ floatx16 mfma6(const bf16x8& ah, const bf16x8& am, co
 // stored k-contiguous is read with one 16-byte load per float4 (eight lanes per row); one stored
 // k-major with four 4-byte loads whose lanes run along the rows (coalesced), which transposes it on
 // the way in.  Values outside the operands (rows, columns, k) are zero; out-of-range loads read the
-// operand's first element instead (no branch around the loads).
+// operand's first element instead (no branch around the loads).  A k-contiguous operand has k a
+// multiple of 4 (the entry points require it), so none of its float4s runs past the last k; a
+// k-major operand's k (a row count) is arbitrary, and each of its four k is checked.
 template <bool TRANS, int ROWS, int NL, int NT>
 __device__ __forceinline__ void load_k4(const float* x, int64_t ld, const float* aux, int64_t ld_aux, bool mask,
                                         int64_t r0, int64_t rows, int64_t k0, int64_t kend, int tid, float4 (&v)[NL],
                                         bool buf32 = false) {
   if (TRANS && buf32) {
-    // k-major operand within 2 GiB: range-checked buffer loads at 32-bit offsets.  The buffer ends
-    // at row kend, so reads past the k range return 0 by themselves; lanes past the last column get
-    // an offset beyond every buffer.  The four k of a float4 differ by a scalar offset.
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(x), 0, static_cast<int32_t>(kend * ld * 4), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(mask ? aux : x), 0, static_cast<int32_t>(kend * (mask ? ld_aux : ld) * 4), kBufferWord3);
+    // k-major operand within 2 GiB: range-checked buffer loads at 32-bit offsets.  The hardware
+    // checks only the per-lane offset against a buffer's size (not the scalar offset), so each of
+    // the four k of a float4 gets a buffer of its own: buffer j starts j rows further on and ends
+    // at row kend, so a read of row gk + j >= kend returns 0 while every lane uses the same offset.
+    // Lanes past the last column or past kend get an offset beyond every buffer.
+    __amdgpu_buffer_rsrc_t rx[4], ra[4];
+    const float* xa = mask ? aux : x;
+    const int64_t lda_ = mask ? ld_aux : ld;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t left = kend - j > 0 ? kend - j : 0;
+      rx[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x + j * ld), 0, static_cast<int32_t>(left * ld * 4),
+                                               kBufferWord3);
+      ra[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(xa + j * lda_), 0,
+                                               static_cast<int32_t>(left * lda_ * 4), kBufferWord3);
+    }
 #pragma unroll
     for (int s = 0; s < NL; ++s) {
       const int f = tid + NT * s;
       const int row = f % ROWS;
       const int kq = f / ROWS;
       const int64_t gr = r0 + row, gk = k0 + 4 * kq;
-      const bool ok = gr < rows;
+      const bool ok = gr < rows && gk < kend;
       const uint32_t ox = ok ? static_cast<uint32_t>((gk * ld + gr) * 4) : 0x80000000u;
       const uint32_t oa = ok ? static_cast<uint32_t>((gk * ld_aux + gr) * 4) : 0x80000000u;
       float e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, ox, static_cast<int32_t>(j * ld * 4), 0));
+        float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx[j], ox, 0, 0));
         if (mask) {
-          const float a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, oa, static_cast<int32_t>(j * ld_aux * 4), 0));
+          const float a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra[j], oa, 0, 0));
           t = a > 0.0f ? t : 0.0f;
         }
         e[j] = t;

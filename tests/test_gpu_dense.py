@@ -331,3 +331,49 @@ def test_k_major_operand_beyond_2gib():
     del big
     H.assert_bits_equal(outs[0], outs[1], "strided beyond 2 GiB against contiguous")
     H.assert_close_normwise(outs[0], dz.astype(np.float64).T @ a.astype(np.float64), what="dZ^T A")
+
+
+def _poisoned(rows, cols, data, device="cuda"):
+    """data in the first `rows` rows of a buffer whose next rows hold NaN, returned as a view of
+    those rows: a read past the operand's last row turns the result into NaN."""
+    import torch
+    buf = torch.full((rows + 8, cols), np.nan, dtype=torch.float32, device=device)
+    buf[:rows] = H.dev(data)
+    return buf[:rows]
+
+
+@pytest.mark.parametrize("m,d_in,d_out", [(1001, 16, 16), (777, 256, 256), (4099, 512, 256), (3, 16, 16),
+                                          (70001, 256, 256), (4098, 64, 512)])
+def test_k_major_reduction_reads_nothing_past_its_rows(m, d_in, d_out):
+    """dW = dZ^T A reduces over the m rows (k-major operands, m not a multiple of 4): the rows after
+    dH, H and A hold NaN, and neither dW nor dA may see them (dense_project with trans_a = 1, and
+    qha_dense_backward at general widths)."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    rng = np.random.default_rng(m + 5 * d_in + d_out)
+    a = rng.standard_normal((m, d_in)).astype(np.float32)
+    w = (rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).astype(np.float32)
+    h = OD.project(a, w).astype(np.float32)
+    dh = rng.standard_normal((m, d_out)).astype(np.float32)
+    da_ref, dw_ref = OD.project_backward(a, w, h, dh)
+    dh_d, h_d, a_d = _poisoned(m, d_out, dh), _poisoned(m, d_out, h), _poisoned(m, d_in, a)
+    w_d = H.dev(w)
+    H.note(f"k-major ragged reduction m={m} {d_in}->{d_out}")
+    ws_bytes = max(B.dense_project_workspace(1, 0, d_out, d_in, m), B.dense_backward_workspace(m, d_out, d_in))
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    dw = torch.full((d_out, d_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_project(1, 0, dh_d, a_d, 0, dw, prologue=B.PRO_RELU_MASK, aux=h_d, workspace=ws)
+    H.assert_close_normwise(H.host(dw), dw_ref, what="dW (dense_project, trans_a = 1)")
+    # B stored k-major too (trans_b = 0): C = A^T A over the m rows
+    c = torch.full((d_in, d_in), np.nan, dtype=torch.float32, device="cuda")
+    ws2_bytes = B.dense_project_workspace(1, 0, d_in, d_in, m)
+    ws2 = torch.empty(max(ws2_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    B.dense_project(1, 0, a_d, a_d, 0, c, workspace=ws2)
+    a64 = a.astype(np.float64)
+    H.assert_close_normwise(H.host(c), a64.T @ a64, what="A^T A")
+    da = torch.full((m, d_in), np.nan, dtype=torch.float32, device="cuda")
+    dw2 = torch.full((d_out, d_in), np.nan, dtype=torch.float32, device="cuda")
+    B.dense_backward(dh_d, h_d, a_d, w_d, da, dw2, workspace=ws)
+    H.assert_close(H.host(da), da_ref, what="dA (dense_backward)")
+    H.assert_close_normwise(H.host(dw2), dw_ref, what="dW (dense_backward)")
