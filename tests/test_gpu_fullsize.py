@@ -3,11 +3,16 @@
 GpuPartition plans, workspaces and layouts), against the oracle.
 
 Each call is fed seeded inputs of its real shape, or the oracle's own messages, so that no oracle
-input comes from the GPU.  Quantised messages are compared bit for bit in full; aggregations and
-projections on sampled rows and columns (random ones plus the heaviest rows and columns, which
-the plan splits into chunks, and the first and last), which the oracle computes one by one from
-its sparse matrix; dW is compared in full.
+input comes from the GPU.  Quantised messages are compared bit for bit in full.  Aggregations and
+projections are compared on every row for the partitions of up to 600k inner nodes; on the
+1.8M-node partition, whose host sparse products would take minutes per call, on sampled rows and
+columns (random ones plus the heaviest rows and columns, which the plan splits into chunks, and the
+first and last), which the oracle computes one by one from its sparse matrix.  dW is compared in
+full.  The 1.8M-node partition is also run at each uniform width of the guide's fixed-width
+ablation (1, 2, 4, 8 bits and FP32 messages).
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -21,9 +26,28 @@ pytestmark = pytest.mark.gpu
 
 SEED = synth.QUANT_SEED
 N_SAMPLE = 1500
+EVERY_ROW_MAX = 600_000       # partitions with at most this many inner nodes are compared on every row
 
 
-def _sample(rng, n, weight, k=N_SAMPLE, heavy=16):
+@functools.lru_cache(maxsize=1)
+def _partition(wl_index):
+    return synth.make_partition(synth.WORKLOADS[wl_index])
+
+
+@functools.lru_cache(maxsize=1)
+def _matrices(wl_index):
+    """The oracle's normalised matrix (rows: inner nodes, columns: inner then halo nodes) and its CSC."""
+    part = _partition(wl_index)
+    if part.wl.model == "sage":
+        mat = OA.mean_matrix(part.nbr_ptr, part.nbr_idx, part.n_in + part.n_h)
+    else:
+        mat = OA.gcn_matrix(part.nbr_ptr, part.nbr_idx, part.deg)
+    return mat, mat.tocsc()
+
+
+def _sample(rng, n, weight, every, k=N_SAMPLE, heavy=16):
+    if every:
+        return np.arange(n, dtype=np.int64)
     pick = set(rng.choice(n, size=min(k, n), replace=False).tolist())
     pick.update(np.argsort(weight)[-heavy:].tolist())
     pick.update([0, n - 1])
@@ -32,6 +56,8 @@ def _sample(rng, n, weight, k=N_SAMPLE, heavy=16):
 
 def _rows_product(mat, rows, x):
     """mat[rows] @ x in float64, touching only the columns those rows use."""
+    if rows.size == mat.shape[0]:
+        return np.asarray(mat @ np.asarray(x, dtype=np.float64))
     sub = mat[rows]
     used = np.unique(sub.indices)
     remap = np.zeros(mat.shape[1], dtype=np.int64)
@@ -51,7 +77,7 @@ def test_full_size_layer_calls(wl_index):
 
     wl = synth.WORKLOADS[wl_index]
     H.note(f"full size {wl.name}: generating")
-    part = synth.make_partition(wl)
+    part = _partition(wl_index)
     n_in, n_h, d = part.n_in, part.n_h, part.d
     sage = wl.model == "sage"
     k_in = 2 * d if sage else d
@@ -59,13 +85,12 @@ def test_full_size_layer_calls(wl_index):
     gp = GpuPartition(part)
     rng = np.random.default_rng(700 + wl_index)
 
-    # the oracle's normalised matrix (rows: inner nodes, columns: inner then halo nodes)
-    mat = OA.mean_matrix(part.nbr_ptr, part.nbr_idx, n_in + n_h) if sage else \
-        OA.gcn_matrix(part.nbr_ptr, part.nbr_idx, part.deg)
-    mat_c = mat.tocsc()
-    rows = _sample(rng, n_in, np.diff(mat.indptr))
-    cols = _sample(rng, n_in + n_h, np.diff(mat_c.indptr))
+    mat, mat_c = _matrices(wl_index)
+    every = n_in <= EVERY_ROW_MAX
+    rows = _sample(rng, n_in, np.diff(mat.indptr), every)
+    cols = _sample(rng, n_in + n_h, np.diff(mat_c.indptr), every)
     cols_in, cols_h = cols[cols < n_in], cols[cols >= n_in] - n_in
+    kind = "every" if every else "sampled"
 
     # ---- a1: quantise the send set x[mirror] (full message, bit for bit) ----------------------
     H.note(f"full size {wl.name}: quantize fwd")
@@ -89,7 +114,7 @@ def test_full_size_layer_calls(wl_index):
         out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
     gp.aggregate_fwd(x_d, omsg, out)
     x_cols = np.concatenate([x, ref_f["received"]])
-    H.assert_close(H.host(out)[rows], _rows_product(mat, rows, x_cols), what="aggregate fwd (sampled rows)")
+    H.assert_close(H.host(out)[rows], _rows_product(mat, rows, x_cols), what=f"aggregate fwd ({kind} rows)")
     del out, omsg, x_cols
     if sage:
         del acat
@@ -101,7 +126,7 @@ def test_full_size_layer_calls(wl_index):
     a_d, w_d = H.dev(a_in), H.dev(w)
     h_out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
     B.dense_project(0, 1, a_d, w_d, 0, h_out, epilogue=B.EPI_RELU)
-    H.assert_close(H.host(h_out)[rows], OD.project(a_in[rows], w), what="dense fwd (sampled rows)")
+    H.assert_close(H.host(h_out)[rows], OD.project(a_in[rows], w), what=f"dense fwd ({kind} rows)")
     del h_out
 
     # ---- a5: dense backward on seeded dH and H -------------------------------------------------
@@ -113,7 +138,7 @@ def test_full_size_layer_calls(wl_index):
     dw = torch.full((d, k_in), np.nan, dtype=torch.float32, device="cuda")
     B.dense_backward(H.dev(dh), H.dev(hh), a_d, w_d, da, dw, workspace=ws)
     dz = np.where(hh > 0, dh, 0).astype(np.float64)
-    H.assert_close(H.host(da)[rows], dz[rows] @ w.astype(np.float64), what="dA (sampled rows)")
+    H.assert_close(H.host(da)[rows], dz[rows] @ w.astype(np.float64), what=f"dA ({kind} rows)")
     H.assert_close_normwise(H.host(dw), dz.T @ a_in.astype(np.float64), what="dW")
     del da, dw, a_d, dz, dh, hh, a_in
 
@@ -124,13 +149,25 @@ def test_full_size_layer_calls(wl_index):
     dxh = torch.full((n_h, d), np.nan, dtype=torch.float32, device="cuda")
     gp.aggregate_bwd_halo(g_d, dxh)
     ref_h = np.asarray(mat_c[:, n_in + cols_h].T @ g.astype(np.float64))
-    H.assert_close(H.host(dxh)[cols_h], ref_h, what="dX halo (sampled columns)")
+    H.assert_close(H.host(dxh)[cols_h], ref_h, what=f"dX halo ({kind} columns)")
     beta = 1 if sage else 0
     dxi0 = rng.standard_normal((n_in, d)).astype(np.float32)
     dxi = H.dev(dxi0)
     gp.aggregate_bwd_inner(g_d, dxi, beta)
     ref_i = np.asarray(mat_c[:, cols_in].T @ g.astype(np.float64)) + (dxi0[cols_in] if beta else 0)
-    H.assert_close(H.host(dxi)[cols_in], ref_i, what="dX inner (sampled columns)")
+    H.assert_close(H.host(dxi)[cols_in], ref_i, what=f"dX inner ({kind} columns)")
+    if not sage:
+        # the one-launch form over all n_in + n_h columns that the GCN step runs
+        H.note(f"full size {wl.name}: aggregate bwd, all columns in one launch")
+        dxa = torch.full((n_in + n_h, d), np.nan, dtype=torch.float32, device="cuda")
+        gp.aggregate_bwd_all(g_d, dxa)
+        dxa_h = H.host(dxa)
+        H.assert_close(dxa_h[cols], np.asarray(mat_c[:, cols].T @ g.astype(np.float64)),
+                       what=f"dX all columns, one launch ({kind} columns)")
+        # each column's sum is the one the range calls form, bit for bit
+        H.assert_bits_equal(dxa_h[n_in:], H.host(dxh), "one launch vs halo range call")
+        H.assert_bits_equal(dxa_h[:n_in], H.host(dxi), "one launch vs inner range call")
+        del dxa, dxa_h
     del g_d, dxh, dxi
 
     # ---- a7: quantise halo gradients (same widths, backward stream) ----------------------------
@@ -150,7 +187,7 @@ def test_full_size_layer_calls(wl_index):
     dxr = H.dev(dxi0)
     gp.add_received(omsg_b, dxr)
     ref_r = OA.add_received(dxi0, part.mirror, ref_b["received"])
-    H.assert_close(H.host(dxr)[rows], ref_r[rows], what="received add (sampled rows)")
+    H.assert_close(H.host(dxr)[rows], ref_r[rows], what=f"received add ({kind} rows)")
     del dxr
 
     # ---- a6 (inner range) + a8 folded into one gather, as the bench runs them ----------------
@@ -159,4 +196,71 @@ def test_full_size_layer_calls(wl_index):
     gp.aggregate_bwd_inner_received(H.dev(g), omsg_b, dxf, beta)
     recv = OA.add_received(np.zeros((n_in, d), np.float32), part.mirror, ref_b["received"])
     ref_f = np.asarray(mat_c[:, cols_in].T @ g.astype(np.float64)) + recv[cols_in] + (dxi0[cols_in] if beta else 0)
-    H.assert_close(H.host(dxf)[cols_in], ref_f, what="inner gradients + received (sampled columns)")
+    H.assert_close(H.host(dxf)[cols_in], ref_f, what=f"inner gradients + received ({kind} columns)")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bits", [1, 2, 8, 32])
+def test_full_size_width_sweep(bits):
+    """The 1.8M-inner + 600k-halo partition at each uniform width of the guide's fixed-width ablation
+    (4 bits is its own width, covered above): both quantisations bit for bit in full, and the calls
+    that read the messages -- the dequantising forward aggregation, the received-gradient add and the
+    inner columns' transposed gather with the received messages folded in -- against the oracle on
+    sampled rows.  The transposed gathers that read no message do not depend on the width."""
+    H.require_gpu()
+    import torch
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition
+
+    wl = synth.WORKLOADS[5]
+    H.note(f"width sweep {wl.name}: generating")
+    part = _partition(5)
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    layer = wl.layers - 1
+    widths = np.full(n_h, bits, dtype=np.uint8)
+    gp = GpuPartition(part, bits=widths)
+    rng = np.random.default_rng(800 + bits)
+    mat, mat_c = _matrices(5)
+    rows = _sample(rng, n_in, np.diff(mat.indptr), False)
+    cols = _sample(rng, n_in, np.diff(mat_c.indptr)[:n_in], False)
+
+    H.note(f"width sweep {wl.name} b={bits}: quantize fwd")
+    x_d = H.dev(part.x)
+    msg = gp.new_messages()
+    gp.quantize_send(x_d, gp.mirror, msg, 1, 2 * layer)
+    ref_f = OL.send_halo(part.x[part.mirror], widths, SEED, 1, 2 * layer, n_in)
+    H.assert_bits_equal(H.host(msg.codes).view(np.uint32)[:ref_f["words"].size], ref_f["words"], f"codes fwd b={bits}")
+    H.assert_bits_equal(H.host(msg.scale), ref_f["scale"], f"scale fwd b={bits}")
+    H.assert_bits_equal(H.host(msg.zero_point), ref_f["zero_point"], f"zero-point fwd b={bits}")
+    del msg
+
+    H.note(f"width sweep {wl.name} b={bits}: aggregate fwd")
+    out = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_fwd(x_d, H.upload_messages(gp, ref_f), out)
+    x_cols = np.concatenate([part.x, ref_f["received"]])
+    H.assert_close(H.host(out)[rows], _rows_product(mat, rows, x_cols), what=f"aggregate fwd b={bits} (sampled rows)")
+    del out, x_cols, x_d
+
+    H.note(f"width sweep {wl.name} b={bits}: quantize bwd")
+    gh = (0.05 * rng.standard_normal((n_h, d))).astype(np.float32)
+    msg_b = gp.new_messages()
+    gp.quantize_send(H.dev(gh), None, msg_b, 1, 2 * layer + 1)
+    ref_b = OL.send_halo(gh, widths, SEED, 1, 2 * layer + 1, n_in)
+    H.assert_bits_equal(H.host(msg_b.codes).view(np.uint32)[:ref_b["words"].size], ref_b["words"], f"codes bwd b={bits}")
+    H.assert_bits_equal(H.host(msg_b.scale), ref_b["scale"], f"scale bwd b={bits}")
+    H.assert_bits_equal(H.host(msg_b.zero_point), ref_b["zero_point"], f"zero-point bwd b={bits}")
+    del msg_b
+
+    H.note(f"width sweep {wl.name} b={bits}: received add and folded inner gather")
+    omsg_b = H.upload_messages(gp, ref_b)
+    dx0 = rng.standard_normal((n_in, d)).astype(np.float32)
+    dxr = H.dev(dx0)
+    gp.add_received(omsg_b, dxr)
+    ref_r = OA.add_received(dx0, part.mirror, ref_b["received"])
+    H.assert_close(H.host(dxr)[rows], ref_r[rows], what=f"received add b={bits} (sampled rows)")
+    del dxr
+    g = rng.standard_normal((n_in, d)).astype(np.float32)
+    dxf = torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_inner_received(H.dev(g), omsg_b, dxf, 0)
+    recv = OA.add_received(np.zeros((n_in, d), np.float32), part.mirror, ref_b["received"])
+    ref_f2 = np.asarray(mat_c[:, cols].T @ g.astype(np.float64)) + recv[cols]
+    H.assert_close(H.host(dxf)[cols], ref_f2, what=f"inner gradients + received b={bits} (sampled columns)")

@@ -1,0 +1,115 @@
+"""The bench's step, every call checked in full: LayerStack.step exactly as bench.py runs it (the
+same buffers, plans, one-base gather addressing and, for GCN, the one-launch transposed gather over
+all n_in + n_h columns), with every call fed the oracle's inputs and every output row compared.
+
+Teacher forcing: the stack's stage hook runs after each call is enqueued.  It waits for the call,
+compares its output with the oracle's result for that call, and then overwrites the output with the
+oracle's value, so that the next call consumes exactly the oracle's input (the oracle never
+consumes a GPU output).  Quantised messages are compared bit for bit; float outputs element by
+element at rtol 1e-5 / atol 1e-6 against the oracle's float64 result (or its float32 rounding,
+which is within 2^-24 relative of it); dW norm-wise (a reduction over every row).
+
+Workloads: the tiny partition (widths from {1,2,4,8}), a small three-layer GCN and a small
+two-layer GraphSAGE-mean stack with 4/8-bit halos, and the full 300k-inner + 150k-halo d = 128
+partition that bench.py times (4 bits, top 10% by degree at 8 bits).
+"""
+import numpy as np
+import pytest
+
+import gpu_helpers as H
+from oracle import dense as OD
+from oracle import layer as OL
+from quantized_halo_aggregation_amd import synth
+
+pytestmark = pytest.mark.gpu
+SEED = synth.QUANT_SEED
+EPOCH = 3
+
+
+class TeacherForcing:
+    """The stage hook: checks each call against the oracle, then puts the oracle's value in place."""
+
+    def __init__(self, st, part, fwds, bwds):
+        self.st, self.part, self.fwds, self.bwds = st, part, fwds, bwds
+        self.seen = []
+
+    def _messages(self, msg, ref, what):
+        H.assert_bits_equal(H.host(msg.codes).view(np.uint32)[:ref["words"].size], ref["words"], what + " codes")
+        H.assert_bits_equal(H.host(msg.zero_point), ref["zero_point"], what + " zero-point")
+        H.assert_bits_equal(H.host(msg.scale), ref["scale"], what + " scale")
+
+    def __call__(self, name, l):
+        import torch
+        st, part, f, b = self.st, self.part, self.fwds[l], self.bwds[l]
+        n_in, d = part.n_in, part.d
+        put = lambda t, a: t.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(t.device))
+        self.seen.append((name, l))
+        H.note(f"full step {part.wl.name}: layer {l} {name}")
+        if name == "quantize_fwd":
+            self._messages(st.msg_f[l][0], f["msg"], f"layer {l} forward message")
+        elif name == "aggregate_fwd":
+            out = st.A[l][:, d:] if st.sage else st.A[l]
+            ref = f["a"][:, d:] if st.sage else f["a"]
+            H.assert_close(H.host(out), ref, what=f"layer {l} aggregate fwd (every row)")
+            put(out, ref)
+        elif name == "dense_fwd":
+            H.assert_close(H.host(st.H[l]), OD.project(f["a"], part.weights[l]), what=f"layer {l} dense fwd (every row)")
+            put(st.H[l], f["h"])
+        elif name == "dense_bwd":
+            dh = part.grad_top if l == st.L - 1 else self.bwds[l + 1]["dx"]
+            da64, _ = OD.project_backward(f["a"], part.weights[l], f["h"], dh)
+            H.assert_close(H.host(st.dA[l]), da64, what=f"layer {l} dA (every row)")
+            H.assert_close_normwise(H.host(st.dW[l]), b["dw"], what=f"layer {l} dW")
+            put(st.dA[l], b["da"])
+        elif name == "aggregate_bwd":                 # GCN: one launch over all columns
+            H.assert_close(H.host(st.dX_cols[l]), b["dx_cols"], what=f"layer {l} transposed aggregate (every column)")
+            put(st.dX_cols[l], b["dx_cols"])
+        elif name == "aggregate_bwd_halo":
+            buf = st.dX_halo[l if len(st.dX_halo) > 1 else 0]
+            H.assert_close(H.host(buf), b["dx_cols"][n_in:], what=f"layer {l} transposed aggregate (halo columns)")
+            put(buf, b["dx_cols"][n_in:])
+        elif name == "quantize_bwd":
+            self._messages(st.msg_b[l][0], b["msg"], f"layer {l} backward message")
+        elif name == "aggregate_bwd_inner":           # GraphSAGE: added into dA's self half
+            H.assert_close(H.host(st.dX[l]), b["dx_cols"][:n_in], what=f"layer {l} transposed aggregate (inner columns)")
+            put(st.dX[l], b["dx_cols"][:n_in])
+        elif name == "add_received":
+            H.assert_close(H.host(st.dX[l]), b["dx"], what=f"layer {l} received add (every row)")
+            put(st.dX[l], b["dx"])
+        else:
+            raise AssertionError(f"unexpected stage {name}")
+
+
+def _run(part):
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
+    H.note(f"full step {part.wl.name}: oracle chain")
+    fwds, bwds = OL.stack(part, SEED, EPOCH)
+    gp = GpuPartition(part)                        # bench.py's chunk and group sizes
+    st = LayerStack(gp, part.weights, part.x, part.grad_top)
+    hook = TeacherForcing(st, part, fwds, bwds)
+    st.step(epoch=EPOCH, hook=hook)
+    H.host(st.dX[0])
+    return st, hook
+
+
+@pytest.mark.parametrize("wl", [
+    synth.WORKLOADS[1],
+    synth.Workload(93, "step-gcn-small", 3001, 1499, 40_000, 64, 3, "gcn", ("top", 4, 8, 0.1)),
+    synth.Workload(94, "step-sage-small", 2003, 997, 30_000, 64, 2, "sage", ("top", 4, 8, 0.1)),
+], ids=lambda w: w.name)
+def test_step_call_by_call_small(wl):
+    H.require_gpu()
+    st, hook = _run(synth.make_partition(wl))
+    per_layer = 7 if not st.sage else 8
+    assert len(hook.seen) == per_layer * wl.layers, hook.seen
+
+
+@pytest.mark.timeout(600)
+def test_bench_step_full_size_every_row():
+    """The partition bench.py times, at its real size; every call of the step, every row."""
+    H.require_gpu()
+    wl = synth.WORKLOADS[2]
+    st, hook = _run(synth.make_partition(wl))
+    assert st.one_bwd_gather
+    assert [n for n, _ in hook.seen] == ["quantize_fwd", "aggregate_fwd", "dense_fwd", "dense_bwd", "aggregate_bwd",
+                                         "quantize_bwd", "add_received"]

@@ -6,6 +6,8 @@
   so each GPU call is fed the oracle's own intermediate inputs and compared with the oracle's next
   result (the oracle never consumes a GPU output).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -23,20 +25,39 @@ def _stack(part):
     return LayerStack(gp, part.weights, part.x, part.grad_top)
 
 
-@pytest.mark.parametrize("model,layers,d", [("gcn", 3, 64), ("gcn", 2, 128), ("sage", 2, 64)])
-def test_unquantised_stack_matches_oracle(model, layers, d):
+@pytest.mark.parametrize("model,layers,d,n_in", [("gcn", 3, 64, 700), ("gcn", 2, 128, 700), ("gcn", 2, 16, 701),
+                                                  ("sage", 2, 64, 700)])
+def test_unquantised_stack_matches_oracle(model, layers, d, n_in):
+    """Every halo at b = 32: the stacks make no random decisions, so the GPU's outputs, embedding
+    gradients and weight gradients are compared with the oracle's end to end, at the per-call rule
+    (rtol 1e-5, atol 1e-6; dW norm-wise).  n_in = 701 makes the weight-gradient reductions run over a
+    row count that is not a multiple of 4.
+
+    GraphSAGE's embedding gradient dX = dA_self + mean^T(dA_mean) adds two products that cancel on
+    some elements, and dA's own float32-class error (at most 8 units of 2^-24 of sum |dz w| per
+    element, bounded by the dense error tests) then exceeds 1e-6 there.  Its check adds the error the
+    chain can carry, 16 * 2^-24 * M, where M is the element's sum of absolute terms through the
+    whole chain (the oracle run on |x|, |W|, |dH|)."""
     H.require_gpu()
-    wl = synth.Workload(95, f"stack-{model}", 700, 300, 9000, d, layers, model, ("const", 32))
+    wl = synth.Workload(95, f"stack-{model}", n_in, 300, 9000, d, layers, model, ("const", 32))
     part = synth.make_partition(wl)
     fwds, bwds = OL.stack(part, SEED, 0)
     st = _stack(part)
-    H.note(f"stack b=32 {model} L={layers} d={d}")
+    H.note(f"stack b=32 {model} L={layers} d={d} n_in={n_in}")
     st.step(epoch=0)
+    slack = None
+    if model == "sage":
+        mag = dataclasses.replace(part, x=np.abs(part.x), weights=[np.abs(w) for w in part.weights],
+                                  grad_top=np.abs(part.grad_top))
+        _, mb = OL.stack(mag, SEED, 0)
+        slack = [16 * 2.0 ** -24 * mb[l]["dx"].astype(np.float64) for l in range(layers)]
     for l in range(layers):
-        # float32 rounding differences compound through the layers; ReLU keeps them from growing
-        H.assert_close(H.host(st.H[l]), fwds[l]["h"], rtol=2e-5, atol=2e-6, what=f"H[{l}]")
-        H.assert_close(H.host(st.dX[l]), bwds[l]["dx"], rtol=2e-5, atol=2e-6, what=f"dX[{l}]")
-        H.assert_close_normwise(H.host(st.dW[l]), bwds[l]["dw"], rtol=2e-5, what=f"dW[{l}]")
+        H.assert_close(H.host(st.H[l]), fwds[l]["h"], what=f"H[{l}]")
+        if slack is None:
+            H.assert_close(H.host(st.dX[l]), bwds[l]["dx"], what=f"dX[{l}]")
+        else:
+            H.assert_close(H.host(st.dX[l]), bwds[l]["dx"], atol=1e-6 + slack[l], what=f"dX[{l}] (chained bound)")
+        H.assert_close_normwise(H.host(st.dW[l]), bwds[l]["dw"], what=f"dW[{l}]")
 
 
 def test_tiny_partition_layer_call_by_call():
