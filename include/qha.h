@@ -10,6 +10,7 @@
  *
  *   qha_quantize_pack         per-vector stochastic integer quantisation + bit packing
  *   qha_dequant_aggregate_fwd dequantisation fused into the normalised neighbour gather (SpMM)
+ *                             (and an allocation-free form of it, ..._noalloc)
  *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
  *   qha_aggregate_bwd_quantize the same over the halo columns, quantising each gradient row
  *   qha_dense_project         the dense projection (float32 products on matrix cores) with ReLU
@@ -18,7 +19,8 @@
  * plus small set-up helpers.  Conventions shared by every entry point:
  *   - Array arguments are caller-owned.  Pointers documented as "device" must be HIP device
  *     memory (or host memory the device can access); "host" pointers are read on the CPU.
- *   - The library allocates no memory and keeps no state between calls.  Device calls enqueue
+ *   - The library allocates no memory and keeps no state between calls (the one exception is the
+ *     device scratch of qha_dequant_aggregate_fwd_noalloc, declared below).  Device calls enqueue
  *     asynchronously on `stream` (a hipStream_t; NULL is the default stream) and return once
  *     the work is queued.
  *   - Every scalar and pointer argument is checked on the host before anything is enqueued; a
@@ -221,6 +223,28 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
                               const float* meta, int64_t n_halo,
                               int32_t d, int32_t beta, float* out, int64_t ldo,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free form of qha_dequant_aggregate_fwd, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same call without the workspace arguments: the float64 partial sums of split rows go to a scratch
+ * array of QHA_NOALLOC_SCRATCH_BYTES bytes that the library holds in device memory (one copy on each
+ * GPU it is loaded on, kept until the process ends).  Its address is looked up once per device, on
+ * the first call with that device current, after the arguments have been checked; the call then
+ * allocates nothing (no hipMalloc, no library routine that allocates).  Every call on a GPU shares
+ * that GPU's scratch, which keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from several host threads) race on it and must be ordered by the caller.
+ * Nothing in it needs clearing, since a call reads only partials it has written itself.
+ * Errors: those of qha_dequant_aggregate_fwd; WORKSPACE when the plan's partials
+ * (qha_agg_workspace_bytes) exceed QHA_NOALLOC_SCRATCH_BYTES, reported before any HIP call; HIP
+ * when the scratch's device address cannot be found. */
+#define QHA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qha_dequant_aggregate_fwd_noalloc(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
+                                      const float* w, const int32_t* row_ids, const qha_agg_plan* plan,
+                                      const float* x_inner, int64_t ldx, int64_t n_inner,
+                                      const uint32_t* codes, const uint32_t* word_offset,
+                                      const uint8_t* bits, const qha_width_classes* classes,
+                                      const float* meta, int64_t n_halo,
+                                      int32_t d, int32_t beta, float* out, int64_t ldo, void* stream);
 
 /* Transposed aggregation for embedding gradients (guide sections 3 and 11: gradients flow back
  * along the same cross-partition dependencies).  Given the transpose of the forward CSR

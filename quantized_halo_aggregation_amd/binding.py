@@ -104,6 +104,9 @@ _quantize_pack = _sig("qha_quantize_pack", _i32, _vp, _i64, _vp, _i64, _i32, _vp
 _dequant_aggregate_fwd = _sig("qha_dequant_aggregate_fwd", _i32, _i64, _vp, _vp, _vp, _vp, _P(AggPlanStruct), _vp,
                               _i64, _i64, _vp, _vp, _vp, _P(WidthClassesStruct), _vp, _i64, _i32, _i32, _vp, _i64, _vp,
                               _sz, _vp)
+_dequant_aggregate_fwd_noalloc = _sig("qha_dequant_aggregate_fwd_noalloc", _i32, _i64, _vp, _vp, _vp, _vp,
+                                      _P(AggPlanStruct), _vp, _i64, _i64, _vp, _vp, _vp, _P(WidthClassesStruct), _vp,
+                                      _i64, _i32, _i32, _vp, _i64, _vp)
 _aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64, _i64, _i32, _i32,
                       _vp, _i64, _vp, _sz, _vp)
 _aggregate_bwd_quantize = _sig("qha_aggregate_bwd_quantize", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64,
@@ -119,7 +122,8 @@ _dense_bwd_ws = _sig("qha_dense_backward_workspace", _sz, _i64, _i64, _i64)
 EXPORTED = ["qha_abi_version", "qha_status_string", "qha_last_error", "qha_pack_layout", "qha_pack_classes",
             "qha_edge_weights", "qha_validate_csr",
             "qha_csr_transpose", "qha_agg_plan_size", "qha_agg_plan_fill", "qha_agg_workspace_bytes",
-            "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_aggregate_bwd",
+            "qha_degree_norm", "qha_quantize_pack", "qha_dequant_aggregate_fwd", "qha_dequant_aggregate_fwd_noalloc",
+            "qha_aggregate_bwd",
             "qha_aggregate_bwd_quantize", "qha_dense_project", "qha_dense_project_workspace", "qha_dense_backward",
             "qha_dense_backward_workspace", "qha_mask_levels", "qha_node_bits", "qha_level_order",
             "qha_coordinator_init", "qha_coordinator_step"]
@@ -359,26 +363,44 @@ def quantize_pack(x, row_index, n_rows: int, bits, word_offset, classes, seed: i
            "qha_quantize_pack")
 
 
-def dequant_aggregate_fwd(rowptr, colidx, w, plan, x_inner, n_inner: int, codes, word_offset, bits, classes, meta,
-                          n_halo: int, beta: int, out, workspace=None, row_ids=None, n_rows=None, stream=None):
+def _dequant_aggregate_args(rowptr, colidx, w, plan, x_inner, n_inner, codes, word_offset, bits, classes, meta,
+                            n_halo, beta, out, row_ids, n_rows):
     import torch
     n_rows = rowptr.numel() - 1 if n_rows is None else int(n_rows)
     px, ldx = _rows(x_inner, "x_inner")
     po, ldo = _rows(out, "out")
     d = out.shape[1]
     halo = n_halo > 0
+    return (n_rows, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"),
+            _dev(w, torch.float32, "w", allow_none=True), _dev(row_ids, torch.int32, "row_ids", allow_none=True),
+            _plan_ref(plan), px, ldx, int(n_inner),
+            _dev32(codes, "codes") if halo else None,
+            _dev32(word_offset, "word_offset") if (halo and word_offset is not None) else None,
+            _dev(bits, torch.uint8, "bits") if (halo and bits is not None) else None,
+            _cls_ref(classes) if halo else None,
+            _dev(meta, torch.float32, "meta") if halo else None,
+            int(n_halo), int(d), int(beta), po, ldo)
+
+
+def dequant_aggregate_fwd(rowptr, colidx, w, plan, x_inner, n_inner: int, codes, word_offset, bits, classes, meta,
+                          n_halo: int, beta: int, out, workspace=None, row_ids=None, n_rows=None, stream=None):
+    args = _dequant_aggregate_args(rowptr, colidx, w, plan, x_inner, n_inner, codes, word_offset, bits, classes, meta,
+                                   n_halo, beta, out, row_ids, n_rows)
     ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_dequant_aggregate_fwd(
-        n_rows, _dev(rowptr, torch.int32, "rowptr"), _dev(colidx, torch.int32, "colidx"),
-        _dev(w, torch.float32, "w", allow_none=True), _dev(row_ids, torch.int32, "row_ids", allow_none=True),
-        _plan_ref(plan), px, ldx, int(n_inner),
-        _dev32(codes, "codes") if halo else None,
-        _dev32(word_offset, "word_offset") if (halo and word_offset is not None) else None,
-        _dev(bits, torch.uint8, "bits") if (halo and bits is not None) else None,
-        _cls_ref(classes) if halo else None,
-        _dev(meta, torch.float32, "meta") if halo else None,
-        int(n_halo), int(d), int(beta), po, ldo, ws_ptr, ws_bytes, _stream(stream)), "qha_dequant_aggregate_fwd")
+    _check(_dequant_aggregate_fwd(*args, ws_ptr, ws_bytes, _stream(stream)), "qha_dequant_aggregate_fwd")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dequant_aggregate_fwd_noalloc(rowptr, colidx, w, plan, x_inner, n_inner: int, codes, word_offset, bits, classes,
+                                  meta, n_halo: int, beta: int, out, row_ids=None, n_rows=None, stream=None):
+    """dequant_aggregate_fwd without a workspace: split-row partials go to the library's device scratch
+    (no allocation in the call; calls that overlap on one GPU race on the scratch)."""
+    args = _dequant_aggregate_args(rowptr, colidx, w, plan, x_inner, n_inner, codes, word_offset, bits, classes, meta,
+                                   n_halo, beta, out, row_ids, n_rows)
+    _check(_dequant_aggregate_fwd_noalloc(*args, _stream(stream)), "qha_dequant_aggregate_fwd_noalloc")
 
 
 def aggregate_bwd(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, beta: int, grad_in, workspace=None,

@@ -58,7 +58,9 @@ int check_rows(const char* name, const float* p, int64_t ld, int32_t d) {
   return QHA_OK;
 }
 
-int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d, const void* ws, size_t ws_bytes) {
+// ws_given: the caller passes the workspace (checked here); otherwise the library's scratch is used.
+int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d, const void* ws, size_t ws_bytes,
+               bool ws_given = true) {
   if (!plan) return QHA_OK;
   if (plan->n_rows != n_rows) return fail(QHA_ERR_INVALID_ARG, "plan was built for %lld rows, call has %lld", (long long)plan->n_rows, (long long)n_rows);
   if (plan->chunk <= 0 || plan->group_edges <= 0) return fail(QHA_ERR_INVALID_ARG, "plan budgets must be positive");
@@ -69,7 +71,10 @@ int check_plan(const qha_agg_plan* plan, int64_t n_rows, int32_t beta, int32_t d
     return fail(QHA_ERR_INVALID_ARG, "plan split arrays are NULL");
   if (plan->skip_empty && beta != 1) return fail(QHA_ERR_INVALID_ARG, "a plan that skips empty rows needs beta = 1");
   const size_t need = qha_agg_workspace_bytes(plan, d);
-  if (need > 0) {
+  if (!ws_given) {
+    if (need > QHA_NOALLOC_SCRATCH_BYTES)
+      return fail(QHA_ERR_WORKSPACE, "the plan's split-row partials need %zu bytes, the static scratch holds %zu", need, (size_t)QHA_NOALLOC_SCRATCH_BYTES);
+  } else if (need > 0) {
     if (!ws || ws_bytes < need) return fail(QHA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (!aligned16(ws)) return fail(QHA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   }
@@ -374,12 +379,13 @@ int qha_quantize_pack(const float* x, int64_t ldx, const int32_t* row_index, int
   return hip_status(qha::launch_quantize(a, d, static_cast<hipStream_t>(stream)), "quantize_pack");
 }
 
-int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* w,
-                              const int32_t* row_ids, const qha_agg_plan* plan, const float* x_inner, int64_t ldx,
-                              int64_t n_inner, const uint32_t* codes, const uint32_t* word_offset,
-                              const uint8_t* bits, const qha_width_classes* classes, const float* meta,
-                              int64_t n_halo, int32_t d, int32_t beta, float* out, int64_t ldo, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+// qha_dequant_aggregate_fwd, with the caller's workspace (ws_given) or the library's scratch.
+static int dequant_aggregate(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* w,
+                             const int32_t* row_ids, const qha_agg_plan* plan, const float* x_inner, int64_t ldx,
+                             int64_t n_inner, const uint32_t* codes, const uint32_t* word_offset,
+                             const uint8_t* bits, const qha_width_classes* classes, const float* meta,
+                             int64_t n_halo, int32_t d, int32_t beta, float* out, int64_t ldo, void* workspace,
+                             size_t workspace_bytes, bool ws_given, void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex || n_inner < 0 || n_halo < 0 || n_inner + n_halo > kMaxIndex)
     return fail(QHA_ERR_INVALID_ARG, "bad sizes");
   if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
@@ -402,8 +408,13 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
     st = take_classes(classes, n_halo, d, &g.cls);
     if (st) return st;
   }
-  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
+  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes, ws_given);
   if (st) return st;
+  if (!ws_given) {
+    hipError_t e = hipSuccess;
+    workspace = qha::noalloc_scratch(&e);
+    if (!workspace) return hip_status(e, "dequant_aggregate_fwd_noalloc: scratch address");
+  }
   g.n_rows = n_rows;
   g.rowptr = rowptr;
   g.colidx = colidx;
@@ -422,6 +433,26 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
   g.out = out;
   g.ldo = ldo;
   return hip_status(qha::launch_gather(g, d, n_halo > 0, static_cast<hipStream_t>(stream)), "dequant_aggregate_fwd");
+}
+
+int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* w,
+                              const int32_t* row_ids, const qha_agg_plan* plan, const float* x_inner, int64_t ldx,
+                              int64_t n_inner, const uint32_t* codes, const uint32_t* word_offset,
+                              const uint8_t* bits, const qha_width_classes* classes, const float* meta,
+                              int64_t n_halo, int32_t d, int32_t beta, float* out, int64_t ldo, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return dequant_aggregate(n_rows, rowptr, colidx, w, row_ids, plan, x_inner, ldx, n_inner, codes, word_offset, bits,
+                           classes, meta, n_halo, d, beta, out, ldo, workspace, workspace_bytes, true, stream);
+}
+
+int qha_dequant_aggregate_fwd_noalloc(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* w,
+                                      const int32_t* row_ids, const qha_agg_plan* plan, const float* x_inner,
+                                      int64_t ldx, int64_t n_inner, const uint32_t* codes,
+                                      const uint32_t* word_offset, const uint8_t* bits,
+                                      const qha_width_classes* classes, const float* meta, int64_t n_halo, int32_t d,
+                                      int32_t beta, float* out, int64_t ldo, void* stream) {
+  return dequant_aggregate(n_rows, rowptr, colidx, w, row_ids, plan, x_inner, ldx, n_inner, codes, word_offset, bits,
+                           classes, meta, n_halo, d, beta, out, ldo, nullptr, 0, false, stream);
 }
 
 int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,

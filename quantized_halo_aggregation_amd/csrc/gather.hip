@@ -36,6 +36,7 @@
 #include "qha_internal.hpp"
 #include "quant_common.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 // the dequantisation scale * q + min is two roundings, as the message format defines it
@@ -930,6 +931,36 @@ hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStre
     case 512: return launch_gather_d<512>(a, with_halo, quantize_out, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Scratch of the allocation-free aggregation: the float64 partial rows of split heavy rows.  Each GPU
+// the library is loaded on holds its own copy until the process ends.  In host code this name is a
+// stand-in, not a device address: the kernels get the address hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) unsigned char scratch[QHA_NOALLOC_SCRATCH_BYTES];
+
+void* noalloc_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 hipError_t launch_edge_weights(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx, const float* r,

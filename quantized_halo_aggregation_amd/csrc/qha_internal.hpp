@@ -147,4 +147,8 @@ hipError_t launch_quantize(const QuantArgs& a, int32_t d, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int32_t d, bool with_halo, hipStream_t s, bool quantize_out = false);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// Device address of the allocation-free aggregation's scratch (QHA_NOALLOC_SCRATCH_BYTES bytes) on
+// the current device, looked up once per device; nullptr, with *err set, if the lookup fails.
+void* noalloc_scratch(hipError_t* err);
+
 }  // namespace qha

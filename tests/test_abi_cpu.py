@@ -216,3 +216,28 @@ def test_device_calls_reject_bad_arguments_before_any_hip_call():
     assert B.dense_backward_workspace(300000, 256, 512) == B.dense_project_workspace(1, 0, 256, 512, 300000)
     assert bcall(n=256, k=512, ldg=256, ldh=256, lda=512, ldw=512, ldda=512, lddw=512, m=300000) == B.QHA_ERR_WORKSPACE
     assert bcall(n=0) == B.QHA_OK
+
+
+def test_noalloc_aggregation_rejects_before_any_hip_call():
+    """The allocation-free aggregation refuses a plan whose split-row partials exceed its scratch, and
+    bad arguments, before it looks anything up on the device."""
+    f = B._dequant_aggregate_fwd_noalloc
+    lens = np.full(100, 4000, np.int32)                    # 100 rows split into 250 chunks of 16 each
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    st, *_ = _plan_host(ptr, 16, False)
+    st.items = st.split_row = st.split_ptr = FAKE
+    assert B._plan_ws(C.byref(st), 512) > B.NOALLOC_SCRATCH_BYTES
+    args = dict(n_rows=100, rowptr=FAKE, colidx=FAKE, w=None, row_ids=None, plan=C.byref(st), x=FAKE, ldx=512,
+                n_inner=5, codes=None, wo=None, bits=None, classes=None, meta=None, n_halo=0, d=512, beta=0, out=FAKE,
+                ldo=512, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+    assert call() == B.QHA_ERR_WORKSPACE
+    assert "static scratch" in B._last_error().decode()
+    assert B._plan_ws(C.byref(st), 128) <= B.NOALLOC_SCRATCH_BYTES
+    assert call(d=128, ldx=128, ldo=128, beta=2) == B.QHA_ERR_INVALID_ARG
+    assert call(d=128, ldx=128, ldo=96) == B.QHA_ERR_INVALID_ARG
+    assert call(d=100) == B.QHA_ERR_UNSUPPORTED
+    assert call(n_rows=0) == B.QHA_OK
