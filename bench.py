@@ -8,9 +8,11 @@ one pass), transposed aggregate over the halo columns, quantise the halo gradien
 call with --fused-halo-bwd), transposed aggregate over the inner columns, dequantise + add the
 received gradients.
 
-Prints one JSON line.  value = algorithmic bytes of the quantise and aggregate calls of a step
-divided by the whole step's wall time (the dense projections are inside the timed step too).
-Per-kernel times come from HIP events recorded on the launch stream inside the timed steps.
+Prints one JSON line.  value = per-edge gather bytes of the quantise and aggregate calls of a step
+(every edge reads its whole source row, no reuse assumed) divided by the whole step's wall time (the
+dense projections are inside the timed step too).  Per-kernel times come from HIP events recorded on
+the launch stream inside the timed steps; each kernel's roofline fraction is taken against its
+compulsory bytes (each array once), a lower bound on its HBM traffic.
 """
 from __future__ import annotations
 
@@ -72,6 +74,20 @@ def gather_bytes(rowptr, colidx, n_inner, d, halo_words, beta, weighted=True, ro
     return int(edge + rows)
 
 
+def compulsory_bytes(rowptr, colidx, n_inner, d, halo_words, beta, n_norm, row_ids=False):
+    """Each array a gather needs, once: the row bounds and column indices, one normalisation factor
+    per node (the per-edge weights are derived from them), every distinct source row (a feature row,
+    or a halo row's packed codes and (min, scale) pair) and the output rows (read too when beta = 1).
+    A lower bound on the HBM traffic of the call."""
+    n_rows = rowptr.size - 1
+    cols = np.unique(colidx).astype(np.int64)
+    inner = cols[cols < n_inner]
+    halo = cols[cols >= n_inner] - n_inner
+    src = inner.size * 4 * d + (int(4 * halo_words[halo].sum()) + 8 * halo.size if halo.size else 0)
+    return int(4 * (n_rows + 1) + 4 * colidx.size + 4 * n_norm + (4 * n_rows if row_ids else 0) + src +
+               4 * d * n_rows * (2 if beta else 1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,17 +118,23 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
 
-    import torch
-    from quantized_halo_aggregation_amd import binding as B
     from quantized_halo_aggregation_amd import synth
-    from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = synth.WORKLOADS[args.workload]
     t0 = time.time()
     part = synth.make_partition(wl)
     gen_s = time.time() - t0
     print(f"[bench] generated {wl.describe()} in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    # the oracle's timings come first: its all-core run forks worker processes, which must happen
+    # before this process touches the GPU
+    cpu_times = None
+    if not args.no_cpu_baseline and not args.sweep_bits:
+        cpu_times = cpu_baseline_times(part)
+
+    import torch
+    from quantized_halo_aggregation_amd import binding as B
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     gp = GpuPartition(part, chunk=args.chunk or B.DEFAULT_CHUNK)
     st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd,
                     split_interior=args.split_interior)
@@ -134,23 +156,39 @@ def main():
         return
     hw = row_words(d, part.bits)
     nw = gp.h_colptr
-    # algorithmic bytes per call of one layer
-    b_q_fwd = quantize_bytes(n_h, d, part.bits, gathered=True)
     sage = wl.model == "sage"
-    b_agg_fwd = gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0)
-    b_bwd_inner = gather_bytes(nw[:n_in + 1], gp.h_rowidx[:nw[n_in]], 1 << 62, d, hw, beta=1 if sage else 0)
-    b_add = gather_bytes(gp.h_m_ptr, np.arange(n_h), 0, d, hw, beta=1, weighted=False, row_ids=True)
-    b_bwd_halo = gather_bytes(nw[n_in:], gp.h_rowidx[nw[n_in]:], 1 << 62, d, hw, beta=0)
+    n_cols = n_in + n_h
+    n_norm = n_cols if not sage else n_in        # GCN: one factor per node; SAGE: 1/|N(v)| per row
+    # per-edge (gather) bytes and compulsory bytes per call of one layer
+    b_q_fwd = quantize_bytes(n_h, d, part.bits, gathered=True)
     b_q_bwd = quantize_bytes(n_h, d, part.bits, gathered=False)
+    inner_t, halo_t = (nw[:n_in + 1], gp.h_rowidx[:nw[n_in]]), (nw[n_in:] - nw[n_in], gp.h_rowidx[nw[n_in]:])
+    bwd_beta = 1 if sage else 0
+    edge = {"quantize_fwd": b_q_fwd, "quantize_bwd": b_q_bwd,
+            "aggregate_fwd": gather_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, beta=0),
+            "aggregate_bwd_inner": gather_bytes(*inner_t, 1 << 62, d, hw, beta=bwd_beta),
+            "aggregate_bwd_halo": gather_bytes(*halo_t, 1 << 62, d, hw, beta=0),
+            "add_received": gather_bytes(gp.h_m_ptr, np.arange(n_h), 0, d, hw, beta=1, weighted=False, row_ids=True),
+            "aggregate_bwd_halo_quantize": gather_quant_bytes(nw[n_in:], int(nw[-1] - nw[n_in]), d, hw)}
+    comp = {"quantize_fwd": b_q_fwd, "quantize_bwd": b_q_bwd,
+            "aggregate_fwd": compulsory_bytes(gp.h_ptr, gp.h_idx, n_in, d, hw, 0, n_norm),
+            "aggregate_bwd_inner": compulsory_bytes(*inner_t, 1 << 62, d, hw, bwd_beta, n_norm),
+            "aggregate_bwd_halo": compulsory_bytes(*halo_t, 1 << 62, d, hw, 0, n_norm),
+            "add_received": compulsory_bytes(gp.h_m_ptr, np.arange(n_h), 0, d, hw, 1, 0, row_ids=True)}
+    # the fused halo path writes codes and (min, scale) pairs instead of the gradient rows
+    comp["aggregate_bwd_halo_quantize"] = comp["aggregate_bwd_halo"] - 4 * d * n_h + int(4 * hw.sum()) + 8 * n_h
+    # one launch over all columns: the two ranges together
+    edge["aggregate_bwd"] = edge["aggregate_bwd_halo"] + edge["aggregate_bwd_inner"]
+    comp["aggregate_bwd"] = compulsory_bytes(nw, gp.h_rowidx, 1 << 62, d, hw, 0, n_norm)
     if args.fused_halo_bwd:
-        bwd = {"aggregate_bwd_halo_quantize": gather_quant_bytes(nw[n_in:], int(nw[-1] - nw[n_in]), d, hw),
-               "aggregate_bwd_inner": b_bwd_inner}
+        bwd = ["aggregate_bwd_halo_quantize", "aggregate_bwd_inner"]
     elif st.one_bwd_gather:
-        # one launch over all columns: the two ranges' bytes
-        bwd = {"aggregate_bwd": b_bwd_halo + b_bwd_inner, "quantize_bwd": b_q_bwd}
+        bwd = ["aggregate_bwd", "quantize_bwd"]
     else:
-        bwd = {"aggregate_bwd_halo": b_bwd_halo, "quantize_bwd": b_q_bwd, "aggregate_bwd_inner": b_bwd_inner}
-    bytes_by_stage = {"quantize_fwd": b_q_fwd, "aggregate_fwd": b_agg_fwd, **bwd, "add_received": b_add}
+        bwd = ["aggregate_bwd_halo", "quantize_bwd", "aggregate_bwd_inner"]
+    byte_stages = ["quantize_fwd", "aggregate_fwd", *bwd, "add_received"]
+    bytes_by_stage = {k: edge[k] for k in byte_stages}
+    comp_by_stage = {k: comp[k] for k in byte_stages}
     k_in = 2 * d if sage else d
     flops_by_stage = {"dense_fwd": 2 * n_in * k_in * d, "dense_bwd": 4 * n_in * k_in * d}
     qa_bytes_step = wl.layers * sum(bytes_by_stage.values())
@@ -210,8 +248,10 @@ def main():
     for s, ms in avg_ms.items():
         rec = {"avg_ms": round(ms, 5)}
         if s in bytes_by_stage:
-            gbs = bytes_by_stage[s] / (ms * 1e-3) / 1e9
-            rec.update(bytes=bytes_by_stage[s], gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+            gbs = comp_by_stage[s] / (ms * 1e-3) / 1e9
+            rec.update(bytes_compulsory=comp_by_stage[s], gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                       bytes_per_edge_model=bytes_by_stage[s],
+                       gather_gbs=round(bytes_by_stage[s] / (ms * 1e-3) / 1e9, 1))
         if s in flops_by_stage:
             # float32 products per second, and the bf16 part products the matrix cores ran
             tf = flops_by_stage[s] / (ms * 1e-3) / 1e12
@@ -224,13 +264,18 @@ def main():
     gef_agg = edges_fwd * d / (avg_ms["aggregate_fwd"] * 1e-3) / 1e9
     gef_layer = edges_fwd * d * wl.layers / (ms_per_step * 1e-3) / 1e9
 
-    # roofline of a stage (each is one kernel launch, plus a short combine or reduce launch)
+    # roofline of a stage (one call: the kernel, plus a short combine launch for split rows)
     def roofline_of(st_name):
         t = avg_ms[st_name]
         if st_name in bytes_by_stage:
-            ach = bytes_by_stage[st_name] / (t * 1e-3) / 1e9
-            return {"kernel": st_name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, st_name),
+            ach = comp_by_stage[st_name] / (t * 1e-3) / 1e9
+            return {"kernel": st_name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, st_name),
+                    "bytes": "compulsory (each array once, a lower bound on HBM traffic)",
+                    "bytes_per_call": comp_by_stage[st_name],
+                    "gather_gbs_per_edge_model": round(bytes_by_stage[st_name] / (t * 1e-3) / 1e9, 1),
+                    "traffic_note": "rocprofv3 FETCH_SIZE + WRITE_SIZE per call, scaled by a plain copy; it counts "
+                                    "the L2's requests to memory, including those the Infinity Cache serves",
                     "avg_us": round(t * 1e3, 1)}
         ach = PARTS * flops_by_stage[st_name] / (t * 1e-3) / 1e12     # bf16 part products
         return {"kernel": st_name, "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
@@ -266,8 +311,8 @@ def main():
     copy_gbs = stream_copy_gbs()
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(part, bytes_by_stage)
+    if cpu_times is not None:
+        cpu = cpu_baseline_record(cpu_times, qa_bytes_step)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -277,7 +322,11 @@ def main():
                    "d": d, "layers": wl.layers, "model": wl.model,
                    "halo_bits": {str(k): v for k, v in part.stats()["bits_hist"].items()},
                    "parallelism": "single-gpu"},
+        "value_bytes": "per-edge gather model of the quantise and aggregate calls (every edge reads its whole "
+                       "source row, no reuse assumed; it counts reads the caches serve, so it can exceed the HBM "
+                       "peak), divided by the whole step's wall time",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "compulsory_gbs": round(wl.layers * sum(comp_by_stage.values()) / (ms_per_step * 1e-3) / 1e9, 1),
         "instrumented_pass": {"ms_per_step": round(inst_ms_step, 4), "stage_events_ms_per_step": round(gpu_ms_step, 4)},
         "kernel_quant_aggregate_gbs": round(kernel_qa_gbs, 1),
         "stream_copy": {"gbs": round(copy_gbs, 1), "value_pct": round(100 * value / copy_gbs, 2),
@@ -421,37 +470,124 @@ def calibrate_copy(mib):
     print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 5}))
 
 
-def cpu_baseline(part, bytes_by_stage):
-    """The oracle, as it is, on the host: the quantise and aggregate calls of one full step (send-set
-    quantisation, forward aggregation, both transposed aggregations, gradient quantisation and the
-    received-gradient add) on the same partition, reported with the same bytes model."""
-    import os as _os
+# ------------------------------------------------------------------------------------------------
+# the oracle on the host cores (timed before the GPU is touched)
+# ------------------------------------------------------------------------------------------------
 
-    from threadpoolctl import threadpool_limits
+_CPU = {}          # the partition, and per-stage buffers in memory shared with forked workers
 
+
+def _blocks(n, k):
+    edges = np.linspace(0, n, k + 1).astype(np.int64)
+    return [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+def _shared(shape, dtype):
+    """An array in anonymous shared memory: worker processes forked after it write into it directly."""
+    import mmap
+    count = int(np.prod(shape))
+    buf = mmap.mmap(-1, max(count * np.dtype(dtype).itemsize, 1))
+    return np.frombuffer(buf, dtype=dtype, count=count).reshape(shape)
+
+
+def _cpu_task(task):
+    """One piece of a stage of the oracle's step: rows [a, b) of the stage's output, written in place."""
     from oracle import aggregate as OA
     from oracle import layer as OL
     from quantized_halo_aggregation_amd import synth
+    kind, a, b = task
+    c = _CPU
+    part = c["part"]
+    n_in = part.n_in
+    rows = np.arange(a, b)
+    gcn = part.wl.model == "gcn"
+    if kind == "send_fwd":
+        c["x_cols"][n_in + a:n_in + b] = OL.send_halo(part.x[part.mirror[a:b]], part.bits[a:b], synth.QUANT_SEED, 0,
+                                                      0, n_in + a)["received"]
+    elif kind == "aggregate_fwd":
+        c["a"][a:b] = (OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, c["x_cols"], rows=rows) if gcn else
+                       OA.mean_aggregate(part.nbr_ptr, part.nbr_idx, c["x_cols"], rows=rows))
+    elif kind == "aggregate_bwd":
+        c["dx"][a:b] = (OA.gcn_aggregate_t(part.nbr_ptr, part.nbr_idx, part.deg, c["g"], cols=rows) if gcn else
+                        OA.mean_aggregate_t(part.nbr_ptr, part.nbr_idx, c["g"], n_in + part.n_h, cols=rows))
+    elif kind == "send_bwd":
+        c["recv_b"][a:b] = OL.send_halo(c["dx"][n_in + a:n_in + b], part.bits[a:b], synth.QUANT_SEED, 0, 1,
+                                        n_in + a)["received"]
+    elif kind == "add_received":
+        ks = np.flatnonzero((part.mirror >= a) & (part.mirror < b))
+        c["dxi"][a:b] = OA.add_received(c["dx"][a:b], part.mirror[ks] - a, c["recv_b"][ks])
+    else:
+        raise ValueError(kind)
 
-    n_in, d = part.n_in, part.d
-    g = np.random.default_rng(7).standard_normal((n_in, d)).astype(np.float32)
+
+def _cpu_step(run):
+    """The quantise and aggregate calls of one layer step, stage by stage; run(kind, n) computes the
+    stage's n output rows (in row blocks)."""
+    n_in, n_h = _CPU["part"].n_in, _CPU["part"].n_h
+    run("send_fwd", n_h)
+    run("aggregate_fwd", n_in)
+    run("aggregate_bwd", n_in + n_h)
+    run("send_bwd", n_h)
+    run("add_received", n_in)
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def cpu_baseline_times(part, repeats=3):
+    """The oracle as it is, timed on the host on the quantise and aggregate calls of one full layer step
+    of the same partition (send-set quantisation, forward aggregation, the transposed aggregation over
+    every column, gradient quantisation and the received-gradient add): on one thread, then with the
+    same calls split over row blocks across one worker process per core.  Median of `repeats` runs each."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    _CPU.clear()
+    _CPU.update(part=part, g=np.random.default_rng(7).standard_normal((n_in, d)).astype(np.float32),
+                x_cols=_shared((n_in + n_h, d), np.float32), a=_shared((n_in, d), np.float64),
+                dx=_shared((n_in + n_h, d), np.float32), recv_b=_shared((n_h, d), np.float32),
+                dxi=_shared((n_in, d), np.float64))
+    _CPU["x_cols"][:n_in] = part.x
+    single = []
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        msg = OL.send_halo(part.x[part.mirror], part.bits, synth.QUANT_SEED, 0, 0, n_in)
-        x_cols = np.concatenate([part.x, msg["received"]])
-        if part.wl.model == "gcn":
-            OA.gcn_aggregate(part.nbr_ptr, part.nbr_idx, part.deg, x_cols)
-            dx = OA.gcn_aggregate_t(part.nbr_ptr, part.nbr_idx, part.deg, g).astype(np.float32)
-        else:
-            OA.mean_aggregate(part.nbr_ptr, part.nbr_idx, x_cols)
-            dx = OA.mean_aggregate_t(part.nbr_ptr, part.nbr_idx, g, n_in + part.n_h).astype(np.float32)
-        back = OL.send_halo(dx[n_in:], part.bits, synth.QUANT_SEED, 0, 1, n_in)
-        OA.add_received(dx[:n_in], part.mirror, back["received"])
-        secs = time.perf_counter() - t0
-    byts = sum(bytes_by_stage.values())
-    return {"value": round(byts / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the quantise and aggregate calls of one full layer step ({secs:.1f} s on one thread of "
-                      f"{_os.cpu_count()} host CPUs; same bytes model as value)"}
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            _cpu_step(lambda kind, n: _cpu_task((kind, 0, n)))
+            single.append(time.perf_counter() - t0)
+    print(f"[bench] oracle, one thread: {np.median(single):.2f} s per step", file=sys.stderr, flush=True)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    multi = []
+    with mp.get_context("fork").Pool(cores, initializer=_worker_init) as pool:
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            _cpu_step(lambda kind, n: pool.map(_cpu_task, [(kind, a, b) for a, b in _blocks(n, cores)], chunksize=1))
+            multi.append(time.perf_counter() - t0)
+    print(f"[bench] oracle, {cores} processes: {np.median(multi):.2f} s per step", file=sys.stderr, flush=True)
+    _CPU.clear()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"single": sorted(single), "multi": sorted(multi), "cores": cores, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def cpu_baseline_record(t, step_bytes):
+    """The CPU figures in the unit of value: the same bytes of one step over the oracle's step time."""
+    med_1, med_n = float(np.median(t["single"])), float(np.median(t["multi"]))
+    return {"value": round(step_bytes / med_n / 1e9, 3), "unit": "GB/s", "cores": t["cores"], "kind": "oracle",
+            "sample": f"the quantise and aggregate calls of one full layer step of the same partition "
+                      f"({med_n:.2f} s with the calls split over row blocks across {t['cores']} worker processes, "
+                      f"one thread each; median of {len(t['multi'])}); same bytes model as value",
+            "seconds": [round(x, 3) for x in t["multi"]],
+            "single_thread": {"value": round(step_bytes / med_1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "seconds": [round(x, 3) for x in t["single"]]},
+            "nproc": t["nproc"], "affinity_cpus": t["affinity"], "cpu_model": t["cpu_model"]}
 
 
 if __name__ == "__main__":
