@@ -4,8 +4,8 @@
 A step is one pass of the whole hot path over the 300k-inner + 150k-halo, d = 128 partition
 (power-law in-degree, mean 25; halo widths 4 bits, 8 bits for the top 10% by degree):
 quantise the send set, fused dequantise + aggregate, project + ReLU, project backward (dA and dW in
-one pass), transposed aggregate over the halo columns, quantise the halo gradients (or both in one
-call with --fused-halo-bwd), transposed aggregate over the inner columns, dequantise + add the
+one pass), the transposed aggregate over every column with the halo columns' gradients quantised in
+place (or, with --unfused-halo-bwd, stored and quantised by a second call), dequantise + add the
 received gradients.
 
 Prints one JSON line.  value = per-edge gather bytes of the quantise and aggregate calls of a step
@@ -103,9 +103,9 @@ def main():
                     help="instead of the step line: one line with the step, quantise and aggregate times and "
                          "message bytes for every halo width in {1, 2, 4, 8, 32} on the chosen partition")
     ap.add_argument("--chunk", type=int, default=None)
-    ap.add_argument("--fused-halo-bwd", action="store_true",
-                    help="quantise the halo gradients inside the transposed gather (one call) instead of "
-                         "gathering them into a buffer and quantising that")
+    ap.add_argument("--unfused-halo-bwd", action="store_true",
+                    help="gather the halo columns' gradients into a buffer and quantise that, instead of coding "
+                         "them inside the one-launch transposed gather (the default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -119,6 +119,7 @@ def main():
         return
 
     from quantized_halo_aggregation_amd import synth
+    fused = not args.unfused_halo_bwd
     wl = synth.WORKLOADS[args.workload]
     t0 = time.time()
     part = synth.make_partition(wl)
@@ -136,7 +137,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     gp = GpuPartition(part, chunk=args.chunk or B.DEFAULT_CHUNK)
-    st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd,
+    st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=fused,
                     split_interior=args.split_interior)
     torch.cuda.synchronize()
     print("[bench] device set-up done", file=sys.stderr, flush=True)
@@ -180,8 +181,13 @@ def main():
     # one launch over all columns: the two ranges together
     edge["aggregate_bwd"] = edge["aggregate_bwd_halo"] + edge["aggregate_bwd_inner"]
     comp["aggregate_bwd"] = compulsory_bytes(nw, gp.h_rowidx, 1 << 62, d, hw, 0, n_norm)
-    if args.fused_halo_bwd:
-        bwd = ["aggregate_bwd_halo_quantize", "aggregate_bwd_inner"]
+    # ... with the halo rows coded in place (codes and (min, scale) pairs written instead of the
+    # rows) and, for SAGE, the inner rows added to dA's self half
+    coded = int(4 * hw.sum()) + 8 * n_h - 4 * d * n_h + (4 * d * n_in if sage else 0)
+    edge["aggregate_bwd_quantize"] = edge["aggregate_bwd"] + coded
+    comp["aggregate_bwd_quantize"] = comp["aggregate_bwd"] + coded
+    if fused:
+        bwd = ["aggregate_bwd_quantize"]
     elif st.one_bwd_gather:
         bwd = ["aggregate_bwd", "quantize_bwd"]
     else:
@@ -292,7 +298,7 @@ def main():
     # partition and weights, epoch 0 synchronous, then asynchronous epochs
     async_rec = None
     if not args.no_async:
-        ast = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=args.fused_halo_bwd,
+        ast = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=fused,
                          pipelined=True)
         ast.step(epoch=0)
         for w in range(args.warmup):
@@ -403,6 +409,9 @@ KERNEL_SOURCES = {
     "aggregate_fwd": ["csrc/gather.hip"],
     "aggregate_bwd_inner": ["csrc/gather.hip"],
     "aggregate_bwd": ["csrc/gather.hip"],
+    "aggregate_bwd_quantize": ["csrc/gather.hip", "csrc/quant_common.hpp"],
+    "quantize_fwd": ["csrc/quantize.hip", "csrc/quant_common.hpp"],
+    "add_received": ["csrc/gather.hip"],
     "dense_fwd": ["csrc/gemm.hip", "csrc/panel.hip"],
     "dense_bwd": ["csrc/gemm.hip", "csrc/panel.hip"],
 }

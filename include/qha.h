@@ -12,7 +12,7 @@
  *   qha_dequant_aggregate_fwd dequantisation fused into the normalised neighbour gather (SpMM)
  *                             (and an allocation-free form of it, ..._noalloc)
  *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
- *   qha_aggregate_bwd_quantize the same over the halo columns, quantising each gradient row
+ *   qha_aggregate_bwd_quantize the same with the halo columns' gradient rows quantised in place
  *   qha_dense_project         the dense projection (float32 products on matrix cores) with ReLU
  *   qha_dense_backward        its gradients dA and dW in one pass (float32 products on matrix cores)
  *
@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QHA_ABI_VERSION 1
+#define QHA_ABI_VERSION 2
 
 /* status codes */
 #define QHA_OK 0
@@ -260,18 +260,26 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
                       int32_t d, int32_t beta, float* grad_in, int64_t ldi,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* The transposed gather over the halo columns with the sender's quantisation fused in (guide
- * section 11: the gradients of the boundary nodes are quantised with the same per-node widths and
- * sent; section 6 for the code).  For every row r < n_rows of the transposed CSR it forms
- * g_r = sum over the row's entries of w * grad_out (as qha_aggregate_bwd with beta = 0, rounded to
- * float32) and codes g_r exactly as qha_quantize_pack codes a row holding g_r (node id
- * node_base + r, the same seed / epoch / stream_id, widths from classes or bits / word_offset,
- * codes and (min, scale) written in place), without storing g_r.  The plan must not skip empty
- * rows: an empty row is a zero gradient and is coded as one.  Arguments as in qha_aggregate_bwd
- * and qha_quantize_pack; errors likewise. */
+/* The transposed gather with the sender's quantisation fused in (guide section 11: the gradients of
+ * the boundary nodes are quantised with the same per-node widths and sent; section 6 for the code).
+ * For every row r < n_rows of the transposed CSR it forms g_r = sum over the row's entries of
+ * w * grad_out (as qha_aggregate_bwd).  Rows r < n_stored are stored, grad_in[r] = (beta ? grad_in[r]
+ * : 0) + g_r, as qha_aggregate_bwd stores them; every row r >= n_stored is message row
+ * m = r - n_stored, coded exactly as qha_quantize_pack codes a row holding g_r rounded to float32
+ * (node id node_base + m, the same seed / epoch / stream_id, widths from classes or bits /
+ * word_offset, which describe the n_rows - n_stored message rows), codes and (min, scale) written
+ * in place, without storing g_r.  With n_stored = n_inner over a CSR whose rows are the inner
+ * columns followed by the halo columns, one launch produces the inner nodes' embedding gradients
+ * and the halo nodes' gradient messages.  Consecutive message rows of a work item share the
+ * rounding generator's calls (one per lane for 512 / d rows); the draws are those of
+ * qha_quantize_pack.  The plan must not skip empty rows: an empty message row is a zero gradient
+ * and is coded as one.  grad_in may be NULL when n_stored = 0; codes, meta and the widths may be
+ * NULL when n_stored = n_rows.  Arguments otherwise as in qha_aggregate_bwd and
+ * qha_quantize_pack; errors likewise. */
 int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,
                                const qha_agg_plan* plan, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
-                               int32_t d, const uint8_t* bits, const uint32_t* word_offset,
+                               int32_t d, int64_t n_stored, int32_t beta, float* grad_in, int64_t ldi,
+                               const uint8_t* bits, const uint32_t* word_offset,
                                const qha_width_classes* classes, uint64_t seed, uint32_t epoch, uint32_t stream_id,
                                uint32_t node_base, uint32_t* codes, float* meta, void* workspace,
                                size_t workspace_bytes, void* stream);

@@ -110,8 +110,8 @@ _dequant_aggregate_fwd_noalloc = _sig("qha_dequant_aggregate_fwd_noalloc", _i32,
 _aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64, _i64, _i32, _i32,
                       _vp, _i64, _vp, _sz, _vp)
 _aggregate_bwd_quantize = _sig("qha_aggregate_bwd_quantize", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64,
-                               _i64, _i32, _vp, _vp, _P(WidthClassesStruct), _u64, _u32, _u32, _u32, _vp, _vp, _vp,
-                               _sz, _vp)
+                               _i64, _i32, _i64, _i32, _vp, _i64, _vp, _vp, _P(WidthClassesStruct), _u64, _u32, _u32,
+                               _u32, _vp, _vp, _vp, _sz, _vp)
 _dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
                       _i64, _i32, _vp, _i64, _i32, _vp, _sz, _vp)
 _dense_ws = _sig("qha_dense_project_workspace", _sz, _i32, _i32, _i64, _i64, _i64)
@@ -419,20 +419,25 @@ def aggregate_bwd(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, beta: int
 
 def aggregate_bwd_quantize(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, d: int, bits, word_offset, classes,
                            seed: int, epoch: int, stream_id: int, node_base: int, codes, meta, workspace=None,
-                           n_rows=None, stream=None):
-    """The transposed gather over colptr's rows, each gradient row quantised into codes / meta."""
+                           n_rows=None, stream=None, grad_in=None, n_stored: int = 0, beta: int = 0):
+    """The transposed gather over colptr's rows: rows below n_stored are stored into grad_in (added
+    to it when beta = 1), every later row is quantised into codes / meta as message row r - n_stored."""
     import torch
     n_rows = colptr.numel() - 1 if n_rows is None else int(n_rows)
     pg, ldg = _rows(grad_out, "grad_out")
+    pi, ldi = _rows(grad_in, "grad_in") if grad_in is not None else (None, d)
+    msgs = n_rows > n_stored
     ws_ptr = None if workspace is None else _dev(workspace, workspace.dtype, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_aggregate_bwd_quantize(n_rows, _dev(colptr, torch.int32, "colptr"), _dev(rowidx, torch.int32, "rowidx"),
                                    _dev(w, torch.float32, "w", allow_none=True), _plan_ref(plan), pg, ldg,
-                                   int(n_grad_rows), int(d), _dev(bits, torch.uint8, "bits", allow_none=True),
-                                   None if word_offset is None else _dev32(word_offset, "word_offset"),
-                                   _cls_ref(classes), int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch), int(stream_id),
-                                   int(node_base), _dev32(codes, "codes"), _dev(meta, torch.float32, "meta"), ws_ptr,
-                                   ws_bytes, _stream(stream)), "qha_aggregate_bwd_quantize")
+                                   int(n_grad_rows), int(d), int(n_stored), int(beta), pi, ldi,
+                                   _dev(bits, torch.uint8, "bits", allow_none=True) if msgs else None,
+                                   None if (word_offset is None or not msgs) else _dev32(word_offset, "word_offset"),
+                                   _cls_ref(classes) if msgs else None, int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch),
+                                   int(stream_id), int(node_base), _dev32(codes, "codes") if msgs else None,
+                                   _dev(meta, torch.float32, "meta") if msgs else None, ws_ptr, ws_bytes,
+                                   _stream(stream)), "qha_aggregate_bwd_quantize")
 
 
 def dense_project(trans_a: int, trans_b: int, a, b, beta: int, c, prologue: int = PRO_NONE, aux=None,

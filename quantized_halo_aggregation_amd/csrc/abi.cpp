@@ -491,13 +491,15 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
 
 int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,
                                const qha_agg_plan* plan, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
-                               int32_t d, const uint8_t* bits, const uint32_t* word_offset,
-                               const qha_width_classes* classes, uint64_t seed, uint32_t epoch, uint32_t stream_id,
-                               uint32_t node_base, uint32_t* codes, float* meta, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  if (n_rows < 0 || n_rows > kMaxIndex || n_grad_rows < 0 || n_grad_rows > kMaxIndex)
+                               int32_t d, int64_t n_stored, int32_t beta, float* grad_in, int64_t ldi,
+                               const uint8_t* bits, const uint32_t* word_offset, const qha_width_classes* classes,
+                               uint64_t seed, uint32_t epoch, uint32_t stream_id, uint32_t node_base, uint32_t* codes,
+                               float* meta, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > kMaxIndex || n_grad_rows < 0 || n_grad_rows > kMaxIndex || n_stored < 0 ||
+      n_stored > n_rows)
     return fail(QHA_ERR_INVALID_ARG, "bad sizes");
   if (!width_supported(d)) return fail(QHA_ERR_UNSUPPORTED, "d=%d not supported", d);
+  if (beta != 0 && beta != 1) return fail(QHA_ERR_INVALID_ARG, "beta must be 0 or 1");
   if (n_rows == 0) return ok();
   if (!colptr || !rowidx) return fail(QHA_ERR_INVALID_ARG, "colptr/rowidx is NULL");
   int st = 0;
@@ -505,18 +507,27 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
     st = check_rows("grad_out", grad_out, ldg, d);
     if (st) return st;
   }
-  if (!codes || !meta || (!classes && (!bits || !word_offset))) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned4(codes) || !aligned8(meta) || (word_offset && !aligned4(word_offset)))
-    return fail(QHA_ERR_INVALID_ARG, "misaligned array");
-  if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_rows) - 1 > 0xFFFFFFFFull)
-    return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
-  st = check_plan(plan, n_rows, 0, d, workspace, workspace_bytes);
+  if (n_stored > 0) {
+    st = check_rows("grad_in", grad_in, ldi, d);
+    if (st) return st;
+  }
+  const int64_t n_msg = n_rows - n_stored;
+  if (n_msg > 0) {
+    if (!codes || !meta || (!classes && (!bits || !word_offset))) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned4(codes) || !aligned8(meta) || (word_offset && !aligned4(word_offset)))
+      return fail(QHA_ERR_INVALID_ARG, "misaligned array");
+    if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_msg) - 1 > 0xFFFFFFFFull)
+      return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
+  }
+  st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
   if (st) return st;
-  if (plan->skip_empty) return fail(QHA_ERR_INVALID_ARG, "every row is coded: the plan may not skip empty rows");
+  if (plan && plan->skip_empty) return fail(QHA_ERR_INVALID_ARG, "every row is written or coded: the plan may not skip empty rows");
   qha::GatherArgs g;
   std::memset(&g, 0, sizeof(g));
-  st = take_classes(classes, n_rows, d, &g.q.cls);
-  if (st) return st;
+  if (n_msg > 0) {
+    st = take_classes(classes, n_msg, d, &g.q.cls);
+    if (st) return st;
+  }
   g.n_rows = n_rows;
   g.rowptr = colptr;
   g.colidx = rowidx;
@@ -525,6 +536,10 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
   g.x = grad_out;
   g.ldx = ldg;
   g.n_inner = n_grad_rows;
+  g.beta = beta;
+  g.out = grad_in;
+  g.ldo = ldi;
+  g.q.first = n_stored;
   g.q.codes = codes;
   g.q.meta = meta;
   g.q.bits = bits;

@@ -138,16 +138,54 @@ __device__ __forceinline__ void load_row(const float* p, float (&xv)[VEC]) {
   }
 }
 
-// Quantises output row k of a gather, held VEC features per lane (lane l owns features l*VEC ..,
-// idle lanes of narrow rows shadow lane 0), with the arithmetic of quantize_pack_kernel: exact
-// row min / max, one Philox call per group of 8 features, codes packed least-significant first
-// and the pieces of lanes that share a word merged with lane shuffles.  Every lane must call it.
+// Quantises message row k of a gather, held VEC features per lane (lane l owns features l*VEC ..,
+// idle lanes of narrow rows shadow lane 0), with the arithmetic of quantize_pack_kernel: exact row
+// min / max, the lane's rounding draws taken from the four words w of its group's Philox call,
+// codes packed least-significant first and the pieces of lanes that share a word merged with lane
+// shuffles.  Every lane must call it.
+// Cross-lane steps of a message row's coding by DPP within each row of 16 lanes: quad permutes
+// for lanes 1 and 2 apart, then the mirrored lane of the half row and of the row (after the quad
+// steps every lane of a quad holds its quad's value, so a mirror pairs the two quads, then the two
+// halves).  They replace LDS-routed lane shuffles, which the coding of every row would wait for.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Exact min and max over the wavefront's 64 lanes (idle lanes shadow lane 0, so they do not change
+// them): DPP within each row of 16 lanes, then the four rows' results read out.
+__device__ __forceinline__ void wave_min_max(float& mn, float& mx) {
+#define QHA_MM_STEP(C)                                              \
+  mn = fminf(mn, __uint_as_float(dpp_u<C>(__float_as_uint(mn)))); \
+  mx = fmaxf(mx, __uint_as_float(dpp_u<C>(__float_as_uint(mx))));
+  QHA_MM_STEP(kDppXor1)
+  QHA_MM_STEP(kDppXor2)
+  QHA_MM_STEP(kDppHalfMirror)
+  QHA_MM_STEP(kDppMirror)
+#undef QHA_MM_STEP
+  mn = fminf(fminf(rdlanef(mn, 0), rdlanef(mn, 16)), fminf(rdlanef(mn, 32), rdlanef(mn, 48)));
+  mx = fmaxf(fmaxf(rdlanef(mx, 0), rdlanef(mx, 16)), fmaxf(rdlanef(mx, 32), rdlanef(mx, 48)));
+}
+
+// OR of the disjoint code pieces of each aligned group of `share` lanes (1 .. 32), left in every
+// lane of the group.
+__device__ __forceinline__ uint32_t group_or(uint32_t w, uint32_t share) {
+  if (share >= 2u) w |= dpp_u<kDppXor1>(w);
+  if (share >= 4u) w |= dpp_u<kDppXor2>(w);
+  if (share >= 8u) w |= dpp_u<kDppHalfMirror>(w);
+  if (share >= 16u) w |= dpp_u<kDppMirror>(w);
+  if (share >= 32u) w |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), 16));
+  return w;
+}
+
+// Width and first code word of message row k, from the width classes (scalar compares) or the
+// per-row arrays.
 template <int D>
-__device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, const float (&v)[vec_of(D)], int lane,
-                                                 int j0, bool owner) {
-  constexpr int VEC = vec_of(D);
-  constexpr int G = D / VEC;
-  uint32_t b, off;
+__device__ __forceinline__ void message_row_layout(const QuantOut& q, int64_t k, uint32_t& b, uint32_t& off) {
   if (q.cls.n > 0) {
     int32_t st = q.cls.start[0];
     uint32_t base = q.cls.base[0];
@@ -166,17 +204,71 @@ __device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, c
     b = q.bits[k];
     off = q.word_offset[k];
   }
+}
+
+// The width classes held one per lane (class c in lane c), for kernels that look rows up inside a
+// loop: a lookup then costs a few lane reads instead of scalar registers kept live through it.
+struct LaneClasses {
+  int32_t start = 0x7FFFFFFF, bits = 0;
+  uint32_t base = 0;
+  int n = 0;
+};
+
+__device__ __forceinline__ LaneClasses lane_classes(const Classes& cls, int lane) {
+  LaneClasses c;
+  c.n = cls.n;
+#pragma unroll
+  for (int i = 0; i < kMaxClasses; ++i) {
+    if (lane == i && i < cls.n) {
+      c.start = cls.start[i];
+      c.bits = cls.bits[i];
+      c.base = cls.base[i];
+    }
+  }
+  return c;
+}
+
+template <int D>
+__device__ __forceinline__ void message_row_layout(const QuantOut& q, const LaneClasses& lc, int64_t k, uint32_t& b,
+                                                   uint32_t& off) {
+  if (lc.n > 0) {
+    int32_t st = rdlane(lc.start, 0);
+    int32_t bb = rdlane(lc.bits, 0);
+    uint32_t base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), 0));
+    for (int c = 1; c < lc.n; ++c) {
+      const int32_t sc = rdlane(lc.start, c);
+      if (k >= sc) {                                   // k and the class starts are uniform
+        st = sc;
+        bb = rdlane(lc.bits, c);
+        base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), c));
+      }
+    }
+    b = static_cast<uint32_t>(bb);
+    const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (b * static_cast<uint32_t>(D) + 31u) >> 5;
+    off = base + static_cast<uint32_t>(k - st) * words;
+  } else {
+    b = q.bits[k];
+    off = q.word_offset[k];
+  }
+}
+
+// Quantises message row k of a gather (width b, codes from word off), held VEC features per lane
+// (lane l owns features l*VEC .., idle lanes of narrow rows shadow lane 0), with the arithmetic of
+// quantize_pack_kernel: exact row min / max, the lane's rounding draws taken from the four words w
+// of its group's Philox call, codes packed least-significant first and the pieces of lanes that
+// share a word merged with lane shuffles.  Every lane must call it.
+template <int D>
+__device__ __forceinline__ void quantize_row_with_draws(const QuantOut& q, int64_t k, uint32_t b, uint32_t off,
+                                                        const float (&v)[vec_of(D)], int lane, int j0, bool owner,
+                                                        const uint32_t (&w)[4]) {
+  constexpr int VEC = vec_of(D);
   float mn = v[0], mx = v[0];
 #pragma unroll
   for (int i = 1; i < VEC; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
-#pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
+  wave_min_max(mn, mx);
   if (!width_valid(b)) return;              // a row of an unknown width is left untouched
   uint32_t* row = q.codes + off;
   if (b == 32u) {
@@ -188,22 +280,16 @@ __device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, c
     return;
   }
   const RowScale rs = row_scale(mn, mx, b);
-  uint32_t c0 = q.node_base + static_cast<uint32_t>(k);
-  uint32_t c1 = static_cast<uint32_t>(j0 >> 3);
-  uint32_t c2 = q.epoch;
-  uint32_t c3 = q.stream_id;
-  philox4x32_10(c0, c1, c2, c3, q.seed_lo, q.seed_hi);
-  const uint32_t w[4] = {c0, c1, c2, c3};
   uint64_t piece = 0;
 #pragma unroll
   for (int i = 0; i < VEC; ++i)
-    piece |= static_cast<uint64_t>(code_of(v[i], mn, rs, draw16(w, j0 + i))) << (static_cast<uint32_t>(i) * b);
+    piece |= static_cast<uint64_t>(code_of(v[i], mn, rs, draw16_c(w, j0 + i))) << (static_cast<uint32_t>(i) * b);
   const uint32_t lane_bits = static_cast<uint32_t>(VEC) * b;
   const uint32_t first = (static_cast<uint32_t>(j0) * b) >> 5;
   if (lane_bits <= 32u) {
     uint32_t word = static_cast<uint32_t>(piece) << ((static_cast<uint32_t>(j0) * b) & 31u);
     const uint32_t share = 32u / lane_bits;          // lanes whose pieces fill one word
-    for (uint32_t o = 1; o < share; o <<= 1) word |= __shfl_xor(word, static_cast<int>(o));
+    word = group_or(word, share);
     if (owner && (static_cast<uint32_t>(lane) & (share - 1u)) == 0u) row[first] = word;
   } else {
     if (owner) {
@@ -212,6 +298,51 @@ __device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, c
     }
   }
   if (lane == 0) *reinterpret_cast<float2*>(q.meta + 2 * k) = make_float2(rs.zp, rs.sc);
+}
+
+// The same, drawing the lane's Philox call for row k itself (counter: node id, the lane's group).
+template <int D>
+__device__ __forceinline__ void quantize_out_row(const QuantOut& q, int64_t k, const float (&v)[vec_of(D)], int lane,
+                                                 int j0, bool owner) {
+  uint32_t c0 = q.node_base + static_cast<uint32_t>(k);
+  uint32_t c1 = static_cast<uint32_t>(j0 >> 3);
+  uint32_t c2 = q.epoch;
+  uint32_t c3 = q.stream_id;
+  philox4x32_10(c0, c1, c2, c3, q.seed_lo, q.seed_hi);
+  const uint32_t w[4] = {c0, c1, c2, c3};
+  uint32_t b, off;
+  message_row_layout<D>(q, k, b, off);
+  quantize_row_with_draws<D>(q, k, b, off, v, lane, j0, owner, w);
+}
+
+// Rounding draws of 512 / D consecutive message rows from one Philox call per lane: lane l holds the
+// call of row k0 + l / (D / 8), group l % (D / 8).  A gather that codes the consecutive rows of a
+// work item one after another pays one call per lane for several rows instead of one per row.
+struct DrawCache {
+  uint32_t w[4];
+  int64_t k0 = -(int64_t(1) << 62);     // no batch yet: every row is outside it
+};
+
+template <int D>
+__device__ __forceinline__ void draws_of_row(const QuantOut& q, DrawCache& dc, int64_t k, int lane, int j0,
+                                             uint32_t (&w)[4]) {
+  constexpr int GPR = D / 8;                // Philox groups per row
+  constexpr int RB = 64 / GPR;              // rows per batch
+  if (k < dc.k0 || k >= dc.k0 + RB) {       // k is wavefront-uniform
+    dc.k0 = k;
+    uint32_t c0 = q.node_base + static_cast<uint32_t>(k + lane / GPR);
+    uint32_t c1 = static_cast<uint32_t>(lane % GPR);
+    uint32_t c2 = q.epoch;
+    uint32_t c3 = q.stream_id;
+    philox4x32_10(c0, c1, c2, c3, q.seed_lo, q.seed_hi);
+    dc.w[0] = c0;
+    dc.w[1] = c1;
+    dc.w[2] = c2;
+    dc.w[3] = c3;
+  }
+  const int src = static_cast<int>(k - dc.k0) * GPR + (j0 >> 3);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = static_cast<uint32_t>(__shfl(static_cast<int>(dc.w[i]), src));
 }
 
 template <int D, bool HALO, bool BETA, bool QUANT>
@@ -256,11 +387,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
   auto flush = [&]() {                          // write row `cur` and start the next one
     const int64_t orow = rdlane(v_out, cur);
-    if constexpr (QUANT) {
+    if (QUANT && orow >= a.q.first) {
       float res[VEC];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
-      quantize_out_row<D>(a.q, orow, res, lane, j0, owner);
+      quantize_out_row<D>(a.q, orow - a.q.first, res, lane, j0, owner);
     } else if (owner) {
       float* dst = a.out + orow * a.ldo + j0;
       float res[VEC];
@@ -414,11 +545,14 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit buffer, range-che
 // loads straight into scalar registers, so no lane-to-scalar moves are needed and the wait for them
 // does not include the wavefront's earlier row stores; each row load is a buffer load whose offset
 // (column * row pitch + the lane's features) is 32-bit and range-checked by the hardware.
-template <int D, bool BETA>
+#ifndef QHA_QUANT_ROWS_BATCH
+#define QHA_QUANT_ROWS_BATCH 8    // edges per batch when the gather also codes message rows (its epilogue is inlined per edge)
+#endif
+template <int D, bool BETA, bool QUANT>
 __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;
-  constexpr int B = rows_batch_of(D);
+  constexpr int B = QUANT ? (rows_batch_of(D) * QHA_QUANT_ROWS_BATCH / QHA_ROWS_BATCH) : rows_batch_of(D);
   const int lane = threadIdx.x & 63;
   const int j0 = (G == 64 ? lane : (lane < G ? lane : 0)) * VEC;
   const bool owner = (G == 64) || lane < G;
@@ -458,9 +592,21 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
   for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
   int cur = 0;
   int32_t cur_end = rdlane(v_end, 0);
+  DrawCache dc;
+  const LaneClasses lc = QUANT ? lane_classes(a.q.cls, lane) : LaneClasses();
   auto flush = [&]() {
     const int64_t orow = rdlane(v_out, cur);
-    if (owner) {
+    if (QUANT && orow >= a.q.first) {
+      // a message row: coded in place of being stored
+      const int64_t k = orow - a.q.first;
+      float res[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+      uint32_t w[4], b, off;
+      draws_of_row<D>(a.q, dc, k, lane, j0, w);
+      message_row_layout<D>(a.q, lc, k, b, off);
+      quantize_row_with_draws<D>(a.q, k, b, off, res, lane, j0, owner, w);
+    } else if (owner) {
       float* dst = a.out + orow * a.ldo + j0;
       float res[VEC];
       if constexpr (BETA) {
@@ -818,11 +964,11 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
     for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + a.partial[static_cast<int64_t>(i) * D + j0 + v];
   }
   const int64_t orow = a.row_ids ? a.row_ids[row] : row;
-  if constexpr (QUANT) {
+  if (QUANT && orow >= a.q.first) {
     float res[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
-    quantize_out_row<D>(a.q, orow, res, lane, j0, owner);
+    quantize_out_row<D>(a.q, orow - a.q.first, res, lane, j0, owner);
   } else if (owner) {
     float* dst = a.out + orow * a.ldo + j0;
 #pragma unroll
@@ -876,8 +1022,14 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_ou
 
   if (a.n_items > 0) {
     const dim3 grid(static_cast<unsigned>((a.n_items + 3) / 4));
-    if (quantize_out) {
-      hipLaunchKernelGGL((gather_kernel<D, false, false, true>), grid, dim3(256), 0, s, a);
+    if (quantize_out && rows_ok) {
+      GatherArgs r = a;
+      r.x_bytes = static_cast<uint32_t>(x_bytes);
+      if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true, true>), grid, dim3(256), 0, s, r);
+      else hipLaunchKernelGGL((gather_rows_kernel<D, false, true>), grid, dim3(256), 0, s, r);
+    } else if (quantize_out) {
+      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gather_kernel<D, false, false, true>), grid, dim3(256), 0, s, a);
     } else if (with_halo && grouped_ok) {
       GatherArgs r = a;
       if (single_base) {
@@ -899,8 +1051,8 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_ou
     } else if (rows_ok) {
       GatherArgs r = a;
       r.x_bytes = static_cast<uint32_t>(x_bytes);
-      if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true>), grid, dim3(256), 0, s, r);
-      else hipLaunchKernelGGL((gather_rows_kernel<D, false>), grid, dim3(256), 0, s, r);
+      if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true, false>), grid, dim3(256), 0, s, r);
+      else hipLaunchKernelGGL((gather_rows_kernel<D, false, false>), grid, dim3(256), 0, s, r);
     } else {
       if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true, false>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((gather_kernel<D, false, false, false>), grid, dim3(256), 0, s, a);

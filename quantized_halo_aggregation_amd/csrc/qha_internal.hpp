@@ -36,9 +36,10 @@ struct QuantArgs {
   float* meta;          // (min, scale) per row
 };
 
-// Quantised output of a gather: each output row r is coded like qha_quantize_pack row r
-// (node id node_base + r) instead of being stored.
+// Quantised output of a gather: each output row r >= first is coded like qha_quantize_pack row
+// r - first (node id node_base + r - first) instead of being stored; rows below first are stored.
 struct QuantOut {
+  int64_t first;
   uint32_t* codes;
   float* meta;
   const uint8_t* bits;

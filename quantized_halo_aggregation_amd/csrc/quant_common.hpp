@@ -61,22 +61,22 @@ __device__ __forceinline__ RowScale row_scale(float mn, float mx, uint32_t b) {
   return r;
 }
 
-// The code of one value: floor of y = (v - min) * inv, plus one when the 16-bit draw is below the
-// fractional part of y (times 2^16), clamped to L.  y >= +0 (v >= min, inv >= 0), so truncation
-// is its floor and the hardware fraction y - floor(y) is exact.
-__device__ __forceinline__ uint32_t code_of(float v, float mn, const RowScale& r, uint32_t u16) {
-  const float t = v - mn;
-  const float y = t * r.inv;
-  const float fr = __builtin_amdgcn_fractf(y);
-  const uint32_t up = (static_cast<float>(u16) < fr * 65536.0f) ? 1u : 0u;
-  uint32_t q = static_cast<uint32_t>(y) + up;
-  q = q > r.levels ? r.levels : q;
-  return r.flat ? 0u : q;
+// The code of one value: q = floor(y) + [u16 < frac(y) * 2^16], clamped to L, for y = (v - min) * inv
+// and the element's 16-bit draw u16.  Computed as (W + (65535 - u16)) >> 16 with W = ceil(y * 2^16):
+// y >= +0 and y * 2^16 is exact (a power-of-two scale of a value below 2^9), so
+// W = floor(y) * 2^16 + ceil(frac(y) * 2^16), and for an integer u16, u16 < frac(y) * 2^16 exactly
+// when u16 < ceil(frac(y) * 2^16), which is when the low 16 bits of the sum carry.  A flat row has
+// inv = 0, so y = W = 0 and its code is 0.
+__device__ __forceinline__ uint32_t code_of(float v, float mn, const RowScale& r, uint32_t nu16) {
+  const float y = (v - mn) * r.inv;
+  const uint32_t w = static_cast<uint32_t>(__builtin_ceilf(y * 65536.0f));
+  const uint32_t q = (w + nu16) >> 16;
+  return q > r.levels ? r.levels : q;
 }
 
-// The 16-bit draw of feature j from the four words of its group's Philox call.
-__device__ __forceinline__ uint32_t draw16(const uint32_t (&w)[4], int j) {
-  const uint32_t word = w[(j & 7) >> 1];
+// 65535 minus the 16-bit draw of feature j, from the four words of its group's Philox call.
+__device__ __forceinline__ uint32_t draw16_c(const uint32_t (&w)[4], int j) {
+  const uint32_t word = ~w[(j & 7) >> 1];
   return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
 }
 

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = 8 * h + i;
-        const uint32_t q = code_of(v[j], mn, rs, draw16(w, i));
+        const uint32_t q = code_of(v[j], mn, rs, draw16_c(w, i));
         acc[j >> 2] |= q << sh[j & 3];
       }
     }

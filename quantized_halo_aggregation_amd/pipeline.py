@@ -264,6 +264,16 @@ class GpuPartition:
                                  self.n_in, msg.codes, msg.meta,
                                  workspace=self.agg_ws if workspace is None else workspace)
 
+    def aggregate_bwd_all_quantize(self, grad_out, dx_inner, msg: Messages, epoch, stream_id, beta,
+                                   seed=QUANT_SEED):
+        """a6 over every column + a7 in one launch: the inner columns' gradients into dx_inner (added
+        to it when beta = 1), the halo columns' gradients quantised into msg as quantize_send would
+        code them, without storing them."""
+        lay = self._stamp(msg)
+        B.aggregate_bwd_quantize(self.colptr, self.rowidx, self.w_bwd, self.plan_bwd_all, grad_out, self.n_in, self.d,
+                                 lay.bits, lay.word_offset, lay.classes, seed, epoch, stream_id, self.n_in, msg.codes,
+                                 msg.meta, workspace=self.agg_ws, grad_in=dx_inner, n_stored=self.n_in, beta=beta)
+
     def aggregate_bwd_inner(self, grad_out, dx_inner, beta):
         """a6 (inner range): gradients of the inner columns (beta = 1 adds to dx_inner)."""
         B.aggregate_bwd(self.colptr[:self.n_in + 1], self.rowidx, self.w_bwd, self.plan_bwd_inner, grad_out,
@@ -349,8 +359,10 @@ class LayerStack:
         # GCN without the fused or folded halo paths runs its transposed aggregation as one launch
         # over all columns into [n_in + n_h, d]: the inner rows are dX, the halo rows the gradients
         # to quantise (one buffer per layer, since layer l's may still be quantised on the second
-        # stream while layer l - 1 gathers)
+        # stream while layer l - 1 gathers).  The fused path (without the folded received add) runs
+        # one launch over all columns too, coding the halo rows instead of storing them.
         self.one_bwd_gather = not sage and not fused_halo_bwd and not fold_received
+        self.one_fused = fused_halo_bwd and not fold_received
         self.dX_cols = []
         if sage:
             # dL/dh of layer l's input rows = the self half of dA, plus the transposed mean (added
@@ -372,7 +384,7 @@ class LayerStack:
         self.comm = torch.cuda.Stream(device=dev) if (pipelined or split_interior) else None
         # split-row partials of the gather that runs on the second stream (the compute stream's
         # gathers keep using the partition's workspace meanwhile)
-        self.comm_ws = torch.empty_like(gp.agg_ws) if (pipelined and fused_halo_bwd) else None
+        self.comm_ws = torch.empty_like(gp.agg_ws) if (pipelined and fused_halo_bwd and not self.one_fused) else None
         self.dense_ws = gp.dense_workspace((0, 1, n_in, d, k_in), backward=(n_in, d, k_in))
 
     def _arena(self, parts):
@@ -423,7 +435,14 @@ class LayerStack:
         g = self.dA[l][:, d:] if self.sage else self.dA[l]
         msg = self.msg_b[l][slot]
         stream_id = 2 * l + 1
-        if self.fused_halo_bwd:
+        beta = 1 if self.sage else 0
+        if self.one_fused:
+            # one launch over every column: the inner columns' gradients into dX (added to the self
+            # half for SAGE), the halo columns' gradients coded into this epoch's message (it stays on
+            # the compute stream in an asynchronous epoch too: its inner rows are needed next)
+            gp.aggregate_bwd_all_quantize(g, self.dX[l], msg, epoch, stream_id, beta, self.seed)
+            if hook: hook("aggregate_bwd_quantize", l)
+        elif self.fused_halo_bwd:
             send = lambda: gp.aggregate_bwd_halo_quantize(g, msg, epoch, stream_id, self.seed,
                                                           workspace=None if sync else self.comm_ws)
             if sync:
@@ -446,8 +465,7 @@ class LayerStack:
             else:
                 self._on_comm(send)
         received = msg if sync else self.msg_b[l][1 - slot]
-        beta = 1 if self.sage else 0
-        if self.one_bwd_gather:
+        if self.one_bwd_gather or self.one_fused:
             gp.add_received(received, self.dX[l])
             if hook: hook("add_received", l)
         elif self.fold_received:

@@ -24,7 +24,7 @@ def test_header_symbols_are_exported():
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} declared in qha.h but not exported"
     assert declared == set(B.EXPORTED)
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
 
 
 def test_status_strings():

@@ -164,6 +164,41 @@ def test_fused_halo_gradient_quantisation(case, grouped):
     assert np.all(np.abs(sc[q] - (rmax[q] - rmin[q]) / levels) <= range_tol / levels + 3e-7 * sc[q]), "scales"
 
 
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("grouped", [True, False], ids=["width-classes", "offset-table"])
+@pytest.mark.parametrize("beta", [0, 1])
+def test_one_launch_gradients_and_halo_messages(case, grouped, beta):
+    """qha_aggregate_bwd_quantize over every column with n_stored = n_in: the inner columns'
+    gradients are stored (added to the old rows when beta = 1) and the halo columns' gradients are
+    coded in place, bit for bit as the transposed gather followed by qha_quantize_pack (every word
+    and (min, scale) pair; heavy columns split into chunks included)."""
+    H.require_gpu()
+    import torch
+    part, gp = _setup(case)
+    gp.set_bits(part.bits, grouped=grouped)
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    rng = np.random.default_rng(11)
+    g_dev = H.dev(rng.standard_normal((n_in, d)).astype(np.float32))
+    old = rng.standard_normal((n_in, d)).astype(np.float32)
+    H.note(f"one-launch aggregate_bwd_quantize {_case_id(case)} grouped={grouped} beta={beta}")
+    dxc = torch.full((n_in + n_h, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_all(g_dev, dxc)
+    two = gp.new_messages()
+    gp.quantize_send(dxc[n_in:], None, two, 4, 7)
+    ref_in = H.dev(old)
+    gp.aggregate_bwd_inner(g_dev, ref_in, 1)
+    fused = gp.new_messages()
+    fused.codes.fill_(-559038737)                       # 0xDEADBEEF: every word must be written
+    fused.meta.fill_(float("nan"))
+    dxi = H.dev(old) if beta else torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    gp.aggregate_bwd_all_quantize(g_dev, dxi, fused, 4, 7, beta)
+    want = H.host(ref_in) if beta else H.host(dxc)[:n_in]
+    H.assert_bits_equal(H.host(dxi), want, "inner gradients")
+    H.assert_bits_equal(H.host(fused.codes).view(np.uint32)[:gp.total_words],
+                        H.host(two.codes).view(np.uint32)[:gp.total_words], "codes")
+    H.assert_bits_equal(H.host(fused.meta), H.host(two.meta), "(min, scale)")
+
+
 def test_deterministic_repeats():
     H.require_gpu()
     import torch

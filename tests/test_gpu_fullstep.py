@@ -11,7 +11,11 @@ which is within 2^-24 relative of it); dW norm-wise (a reduction over every row)
 
 Workloads: the tiny partition (widths from {1,2,4,8}), a small three-layer GCN and a small
 two-layer GraphSAGE-mean stack with 4/8-bit halos, and the full 300k-inner + 150k-halo d = 128
-partition that bench.py times (4 bits, top 10% by degree at 8 bits).
+partition that bench.py times (4 bits, top 10% by degree at 8 bits).  Each runs in three modes: the
+transposed gather then a separate quantisation of the halo gradients; the one-launch transposed
+gather that codes the halo gradients in place (bench.py's default), whose codes come from the GPU's
+own float32 gradients and are checked within one quantisation step of the oracle before the
+oracle's message is put in place; and the interior / boundary split of the forward aggregation.
 """
 import numpy as np
 import pytest
@@ -37,6 +41,18 @@ class TeacherForcing:
         H.assert_bits_equal(H.host(msg.codes).view(np.uint32)[:ref["words"].size], ref["words"], what + " codes")
         H.assert_bits_equal(H.host(msg.zero_point), ref["zero_point"], what + " zero-point")
         H.assert_bits_equal(H.host(msg.scale), ref["scale"], what + " scale")
+
+    def _near(self, msg, ref, what):
+        from oracle import quantize as OQ
+        part = self.part
+        words = H.host(msg.codes).view(np.uint32)
+        meta = H.host(msg.meta)
+        codes = OQ.unpack(words, self.st.gp.h_word_offset, part.bits, part.d)
+        deq = OQ.dequantize(codes, meta[:, 1], meta[:, 0], part.bits).astype(np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        step = meta[:, 1].astype(np.float64)[:, None] * (1 + 2.0 ** -20)
+        bound = step + 1e-6 + 1e-5 * np.abs(ref) + np.spacing(np.abs(ref).astype(np.float32))
+        assert np.all(np.abs(deq - ref) <= bound), f"{what}: a dequantised value is beyond one step of the oracle"
 
     def __call__(self, name, l):
         import torch
@@ -70,6 +86,16 @@ class TeacherForcing:
             put(buf, b["dx_cols"][n_in:])
         elif name == "quantize_bwd":
             self._messages(st.msg_b[l][0], b["msg"], f"layer {l} backward message")
+        elif name == "aggregate_bwd_quantize":     # one launch: inner gradients stored, halo ones coded
+            H.assert_close(H.host(st.dX[l]), b["dx_cols"][:n_in], what=f"layer {l} transposed aggregate (inner columns)")
+            put(st.dX[l], b["dx_cols"][:n_in])
+            # the codes come from the GPU's own float32 gradients, which may differ from the oracle's in
+            # the last bit: each dequantised value lies within one quantisation step of the oracle's
+            # gradient; then the oracle's message is put in place
+            msg = st.msg_b[l][0]
+            self._near(msg, b["dx_cols"][n_in:], f"layer {l} backward message")
+            put(msg.codes[:b["msg"]["words"].size], b["msg"]["words"].view(np.int32))
+            put(msg.meta, np.stack([b["msg"]["zero_point"], b["msg"]["scale"]], axis=1))
         elif name == "aggregate_bwd_inner":           # GraphSAGE: added into dA's self half
             H.assert_close(H.host(st.dX[l]), b["dx_cols"][:n_in], what=f"layer {l} transposed aggregate (inner columns)")
             put(st.dX[l], b["dx_cols"][:n_in])
@@ -80,12 +106,15 @@ class TeacherForcing:
             raise AssertionError(f"unexpected stage {name}")
 
 
-def _run(part):
+MODES = {"gather+quantize": {}, "one-launch": {"fused_halo_bwd": True}, "interior-split": {"split_interior": True}}
+
+
+def _run(part, mode="gather+quantize"):
     from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
-    H.note(f"full step {part.wl.name}: oracle chain")
+    H.note(f"full step {part.wl.name} ({mode}): oracle chain")
     fwds, bwds = OL.stack(part, SEED, EPOCH)
     gp = GpuPartition(part)                        # bench.py's chunk and group sizes
-    st = LayerStack(gp, part.weights, part.x, part.grad_top)
+    st = LayerStack(gp, part.weights, part.x, part.grad_top, **MODES[mode])
     hook = TeacherForcing(st, part, fwds, bwds)
     st.step(epoch=EPOCH, hook=hook)
     H.host(st.dX[0])
@@ -97,19 +126,26 @@ def _run(part):
     synth.Workload(93, "step-gcn-small", 3001, 1499, 40_000, 64, 3, "gcn", ("top", 4, 8, 0.1)),
     synth.Workload(94, "step-sage-small", 2003, 997, 30_000, 64, 2, "sage", ("top", 4, 8, 0.1)),
 ], ids=lambda w: w.name)
-def test_step_call_by_call_small(wl):
+@pytest.mark.parametrize("mode", list(MODES))
+def test_step_call_by_call_small(wl, mode):
+    """Every call of the step on small stacks; "interior-split" aggregates the rows without halo
+    neighbours on a second stream while the send set is quantised, then the boundary rows."""
     H.require_gpu()
-    st, hook = _run(synth.make_partition(wl))
-    per_layer = 7 if not st.sage else 8
+    st, hook = _run(synth.make_partition(wl), mode)
+    per_layer = 6 if mode == "one-launch" else (7 if not st.sage else 8)
     assert len(hook.seen) == per_layer * wl.layers, hook.seen
+    if mode == "interior-split":
+        assert 0 < st.gp.n_interior < st.gp.n_in
 
 
 @pytest.mark.timeout(600)
-def test_bench_step_full_size_every_row():
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bench_step_full_size_every_row(mode):
     """The partition bench.py times, at its real size; every call of the step, every row."""
     H.require_gpu()
     wl = synth.WORKLOADS[2]
-    st, hook = _run(synth.make_partition(wl))
-    assert st.one_bwd_gather
-    assert [n for n, _ in hook.seen] == ["quantize_fwd", "aggregate_fwd", "dense_fwd", "dense_bwd", "aggregate_bwd",
-                                         "quantize_bwd", "add_received"]
+    st, hook = _run(synth.make_partition(wl), mode)
+    fused = mode == "one-launch"
+    bwd = ["aggregate_bwd_quantize"] if fused else ["aggregate_bwd", "quantize_bwd"]
+    assert [n for n, _ in hook.seen] == ["quantize_fwd", "aggregate_fwd", "dense_fwd", "dense_bwd", *bwd,
+                                         "add_received"]
