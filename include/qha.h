@@ -13,6 +13,7 @@
  *                             (and an allocation-free form of it, ..._noalloc)
  *   qha_aggregate_bwd         the transposed gather that produces embedding gradients
  *   qha_aggregate_bwd_quantize the same with the halo columns' gradient rows quantised in place
+ *                             (and messages received earlier added to the stored rows)
  *   qha_dense_project         the dense projection (float32 products on matrix cores) with ReLU
  *   qha_dense_backward        its gradients dA and dW in one pass (float32 products on matrix cores)
  *
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define QHA_ABI_VERSION 2
+#define QHA_ABI_VERSION 3
 
 /* status codes */
 #define QHA_OK 0
@@ -260,6 +261,27 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
                       int32_t d, int32_t beta, float* grad_in, int64_t ldi,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Messages received for the stored rows of qha_aggregate_bwd_quantize (guide section 11: the
+ * receiver dequantises the gradients sent back for its boundary nodes' remote copies and continues
+ * backward with them added).  Stored row r gets the message rows copy_idx[copy_ptr[r] ..
+ * copy_ptr[r + 1]) of this buffer, each dequantised as qha_dequant_aggregate_fwd dequantises a halo
+ * row, summed in float64 in list order, added to the row's float32 value as stored without them, and
+ * rounded to float32 once more: bit for bit what a following qha_dequant_aggregate_fwd with beta = 1,
+ * w = NULL, n_inner = 0 and the copy lists as its CSR would leave.  The buffer must not be one the
+ * call writes: these are messages that arrived before it (in the asynchronous mode of the guide's
+ * section 10, the previous epoch's), which is what lets one launch both produce this epoch's
+ * messages and consume earlier ones. */
+typedef struct qha_received {
+  const int32_t* copy_ptr;           /* device int32[n_stored + 1]: copy_ptr[0] = 0, non-decreasing */
+  const int32_t* copy_idx;           /* device int32[copy_ptr[n_stored]]: message rows, each < n_rows */
+  int64_t n_rows;                    /* rows of the received buffer */
+  const uint32_t* codes;             /* device, qha_quantize_pack's layout */
+  const float* meta;                 /* device float32[2 n_rows]: (min, scale) per row */
+  const uint8_t* bits;               /* device, or NULL with classes */
+  const uint32_t* word_offset;       /* device, or NULL with classes */
+  const qha_width_classes* classes;  /* host, or NULL for the per-row bits / word_offset */
+} qha_received;
+
 /* The transposed gather with the sender's quantisation fused in (guide section 11: the gradients of
  * the boundary nodes are quantised with the same per-node widths and sent; section 6 for the code).
  * For every row r < n_rows of the transposed CSR it forms g_r = sum over the row's entries of
@@ -274,15 +296,16 @@ int qha_aggregate_bwd(int64_t n_rows, const int32_t* colptr, const int32_t* rowi
  * rounding generator's calls (one per lane for 512 / d rows); the draws are those of
  * qha_quantize_pack.  The plan must not skip empty rows: an empty message row is a zero gradient
  * and is coded as one.  grad_in may be NULL when n_stored = 0; codes, meta and the widths may be
- * NULL when n_stored = n_rows.  Arguments otherwise as in qha_aggregate_bwd and
- * qha_quantize_pack; errors likewise. */
+ * NULL when n_stored = n_rows.  received (host struct, nullable; see qha_received) adds earlier
+ * messages to the stored rows as they are written; its codes and meta must differ from this call's.
+ * Arguments otherwise as in qha_aggregate_bwd and qha_quantize_pack; errors likewise. */
 int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int32_t* rowidx, const float* w,
                                const qha_agg_plan* plan, const float* grad_out, int64_t ldg, int64_t n_grad_rows,
                                int32_t d, int64_t n_stored, int32_t beta, float* grad_in, int64_t ldi,
                                const uint8_t* bits, const uint32_t* word_offset,
                                const qha_width_classes* classes, uint64_t seed, uint32_t epoch, uint32_t stream_id,
-                               uint32_t node_base, uint32_t* codes, float* meta, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               uint32_t node_base, uint32_t* codes, float* meta, const qha_received* received,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Dense projection and its gradients (guide section 2: z_v = W a_v, h_v = sigma(z_v); section 7:
  * dL/dW = sum_v (dL/dh_v * sigma'(z_v)) a_v^T), float32 products on the matrix cores (MFMA):

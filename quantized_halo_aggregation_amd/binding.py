@@ -64,6 +64,11 @@ class WidthClassesStruct(C.Structure):
                 ("base", _u32 * MAX_CLASSES)]
 
 
+class ReceivedStruct(C.Structure):
+    _fields_ = [("copy_ptr", _vp), ("copy_idx", _vp), ("n_rows", _i64), ("codes", _vp), ("meta", _vp), ("bits", _vp),
+                ("word_offset", _vp), ("classes", C.POINTER(WidthClassesStruct))]
+
+
 MAX_LEVELS = 8
 LDR_MAX_DELTA = 64
 
@@ -111,7 +116,7 @@ _aggregate_bwd = _sig("qha_aggregate_bwd", _i32, _i64, _vp, _vp, _vp, _P(AggPlan
                       _vp, _i64, _vp, _sz, _vp)
 _aggregate_bwd_quantize = _sig("qha_aggregate_bwd_quantize", _i32, _i64, _vp, _vp, _vp, _P(AggPlanStruct), _vp, _i64,
                                _i64, _i32, _i64, _i32, _vp, _i64, _vp, _vp, _P(WidthClassesStruct), _u64, _u32, _u32,
-                               _u32, _vp, _vp, _vp, _sz, _vp)
+                               _u32, _vp, _vp, _P(ReceivedStruct), _vp, _sz, _vp)
 _dense_project = _sig("qha_dense_project", _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp,
                       _i64, _i32, _vp, _i64, _i32, _vp, _sz, _vp)
 _dense_ws = _sig("qha_dense_project_workspace", _sz, _i32, _i32, _i64, _i64, _i64)
@@ -419,10 +424,21 @@ def aggregate_bwd(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, beta: int
 
 def aggregate_bwd_quantize(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, d: int, bits, word_offset, classes,
                            seed: int, epoch: int, stream_id: int, node_base: int, codes, meta, workspace=None,
-                           n_rows=None, stream=None, grad_in=None, n_stored: int = 0, beta: int = 0):
+                           n_rows=None, stream=None, grad_in=None, n_stored: int = 0, beta: int = 0,
+                           received=None):
     """The transposed gather over colptr's rows: rows below n_stored are stored into grad_in (added
-    to it when beta = 1), every later row is quantised into codes / meta as message row r - n_stored."""
+    to it when beta = 1), every later row is quantised into codes / meta as message row r - n_stored.
+    received = (copy_ptr, copy_idx, n_rows, codes, meta, bits, word_offset, classes) adds those
+    earlier messages to the stored rows (bits / word_offset may be None with classes)."""
     import torch
+    rs = None
+    if received is not None:
+        c_ptr, c_idx, r_rows, r_codes, r_meta, r_bits, r_off, r_cls = received
+        rs = ReceivedStruct(_dev(c_ptr, torch.int32, "copy_ptr"), _dev(c_idx, torch.int32, "copy_idx"), int(r_rows),
+                            _dev32(r_codes, "received codes"), _dev(r_meta, torch.float32, "received meta"),
+                            _dev(r_bits, torch.uint8, "received bits", allow_none=True),
+                            None if r_off is None else _dev32(r_off, "received word_offset"),
+                            None if r_cls is None else C.pointer(r_cls))
     n_rows = colptr.numel() - 1 if n_rows is None else int(n_rows)
     pg, ldg = _rows(grad_out, "grad_out")
     pi, ldi = _rows(grad_in, "grad_in") if grad_in is not None else (None, d)
@@ -436,7 +452,8 @@ def aggregate_bwd_quantize(colptr, rowidx, w, plan, grad_out, n_grad_rows: int, 
                                    None if (word_offset is None or not msgs) else _dev32(word_offset, "word_offset"),
                                    _cls_ref(classes) if msgs else None, int(seed) & 0xFFFFFFFFFFFFFFFF, int(epoch),
                                    int(stream_id), int(node_base), _dev32(codes, "codes") if msgs else None,
-                                   _dev(meta, torch.float32, "meta") if msgs else None, ws_ptr, ws_bytes,
+                                   _dev(meta, torch.float32, "meta") if msgs else None,
+                                   None if rs is None else C.byref(rs), ws_ptr, ws_bytes,
                                    _stream(stream)), "qha_aggregate_bwd_quantize")
 
 

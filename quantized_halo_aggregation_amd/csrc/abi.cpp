@@ -494,7 +494,8 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
                                int32_t d, int64_t n_stored, int32_t beta, float* grad_in, int64_t ldi,
                                const uint8_t* bits, const uint32_t* word_offset, const qha_width_classes* classes,
                                uint64_t seed, uint32_t epoch, uint32_t stream_id, uint32_t node_base, uint32_t* codes,
-                               float* meta, void* workspace, size_t workspace_bytes, void* stream) {
+                               float* meta, const qha_received* received, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   if (n_rows < 0 || n_rows > kMaxIndex || n_grad_rows < 0 || n_grad_rows > kMaxIndex || n_stored < 0 ||
       n_stored > n_rows)
     return fail(QHA_ERR_INVALID_ARG, "bad sizes");
@@ -519,6 +520,20 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
     if (static_cast<uint64_t>(node_base) + static_cast<uint64_t>(n_msg) - 1 > 0xFFFFFFFFull)
       return fail(QHA_ERR_INVALID_ARG, "node ids node_base + r overflow 32 bits");
   }
+  const bool recv = received != nullptr && n_stored > 0;
+  if (recv) {
+    const qha_received& r = *received;
+    if (r.n_rows < 0 || r.n_rows > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "received: bad row count");
+    if (!r.copy_ptr || !r.copy_idx) return fail(QHA_ERR_INVALID_ARG, "received: copy_ptr/copy_idx is NULL");
+    if (r.n_rows > 0) {
+      if (!r.codes || !r.meta || (!r.classes && (!r.bits || !r.word_offset)))
+        return fail(QHA_ERR_INVALID_ARG, "received: NULL pointer");
+      if (!aligned4(r.codes) || !aligned8(r.meta) || (r.word_offset && !aligned4(r.word_offset)))
+        return fail(QHA_ERR_INVALID_ARG, "received: misaligned array");
+      if (n_msg > 0 && (r.codes == codes || r.meta == meta))
+        return fail(QHA_ERR_INVALID_ARG, "received: the buffer is the one this call writes");
+    }
+  }
   st = check_plan(plan, n_rows, beta, d, workspace, workspace_bytes);
   if (st) return st;
   if (plan && plan->skip_empty) return fail(QHA_ERR_INVALID_ARG, "every row is written or coded: the plan may not skip empty rows");
@@ -527,6 +542,19 @@ int qha_aggregate_bwd_quantize(int64_t n_rows, const int32_t* colptr, const int3
   if (n_msg > 0) {
     st = take_classes(classes, n_msg, d, &g.q.cls);
     if (st) return st;
+  }
+  if (recv) {
+    const qha_received& r = *received;
+    if (r.n_rows > 0) {
+      st = take_classes(r.classes, r.n_rows, d, &g.r.cls);
+      if (st) return st;
+    }
+    g.r.ptr = r.copy_ptr;
+    g.r.idx = r.copy_idx;
+    g.r.codes = r.codes;
+    g.r.meta = r.meta;
+    g.r.bits = r.bits;
+    g.r.word_offset = r.word_offset;
   }
   g.n_rows = n_rows;
   g.rowptr = colptr;

@@ -182,10 +182,10 @@ __device__ __forceinline__ uint32_t group_or(uint32_t w, uint32_t share) {
   return w;
 }
 
-// Width and first code word of message row k, from the width classes (scalar compares) or the
-// per-row arrays.
-template <int D>
-__device__ __forceinline__ void message_row_layout(const QuantOut& q, int64_t k, uint32_t& b, uint32_t& off) {
+// Width and first code word of message row k (of a buffer the gather writes, or of a received one),
+// from the width classes (scalar compares) or the per-row arrays.
+template <int D, typename M>
+__device__ __forceinline__ void message_row_layout(const M& q, int64_t k, uint32_t& b, uint32_t& off) {
   if (q.cls.n > 0) {
     int32_t st = q.cls.start[0];
     uint32_t base = q.cls.base[0];
@@ -206,12 +206,14 @@ __device__ __forceinline__ void message_row_layout(const QuantOut& q, int64_t k,
   }
 }
 
-// The width classes held one per lane (class c in lane c), for kernels that look rows up inside a
-// loop: a lookup then costs a few lane reads instead of scalar registers kept live through it.
+// The width classes held one per lane (class c in lane lane0 + c), for kernels that look rows up
+// inside a loop: a lookup then costs a few lane reads instead of scalar registers kept live through
+// it.  Two tables can share the registers (the second in lanes 8 ..), each seen through its own view.
 struct LaneClasses {
   int32_t start = 0x7FFFFFFF, bits = 0;
   uint32_t base = 0;
   int n = 0;
+  int lane0 = 0;
 };
 
 __device__ __forceinline__ LaneClasses lane_classes(const Classes& cls, int lane) {
@@ -228,19 +230,37 @@ __device__ __forceinline__ LaneClasses lane_classes(const Classes& cls, int lane
   return c;
 }
 
-template <int D>
-__device__ __forceinline__ void message_row_layout(const QuantOut& q, const LaneClasses& lc, int64_t k, uint32_t& b,
+// Table `second` put in lanes kMaxClasses .. of the registers holding `first` (lane_classes(first));
+// the result is the view of the second table.
+__device__ __forceinline__ LaneClasses lane_classes_beside(const LaneClasses& first, const Classes& second,
+                                                          int lane) {
+  LaneClasses c = first;
+  c.n = second.n;
+  c.lane0 = kMaxClasses;
+#pragma unroll
+  for (int i = 0; i < kMaxClasses; ++i) {
+    if (lane == kMaxClasses + i && i < second.n) {
+      c.start = second.start[i];
+      c.bits = second.bits[i];
+      c.base = second.base[i];
+    }
+  }
+  return c;
+}
+
+template <int D, typename M>
+__device__ __forceinline__ void message_row_layout(const M& q, const LaneClasses& lc, int64_t k, uint32_t& b,
                                                    uint32_t& off) {
   if (lc.n > 0) {
-    int32_t st = rdlane(lc.start, 0);
-    int32_t bb = rdlane(lc.bits, 0);
-    uint32_t base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), 0));
+    int32_t st = rdlane(lc.start, lc.lane0);
+    int32_t bb = rdlane(lc.bits, lc.lane0);
+    uint32_t base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), lc.lane0));
     for (int c = 1; c < lc.n; ++c) {
-      const int32_t sc = rdlane(lc.start, c);
+      const int32_t sc = rdlane(lc.start, lc.lane0 + c);
       if (k >= sc) {                                   // k and the class starts are uniform
         st = sc;
-        bb = rdlane(lc.bits, c);
-        base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), c));
+        bb = rdlane(lc.bits, lc.lane0 + c);
+        base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), lc.lane0 + c));
       }
     }
     b = static_cast<uint32_t>(bb);
@@ -345,8 +365,111 @@ __device__ __forceinline__ void draws_of_row(const QuantOut& q, DrawCache& dc, i
   for (int i = 0; i < 4; ++i) w[i] = static_cast<uint32_t>(__shfl(static_cast<int>(dc.w[i]), src));
 }
 
-template <int D, bool HALO, bool BETA, bool QUANT>
+// ---- received messages added to stored rows (the receiver's "dequantise and continue backward",
+// guide section 11, folded into the gather that stores the rows) ----
+
+// Width and first code word of message row k held per lane (k < 0: no row, b = 0), with the
+// classes held one per lane: the received rows of a work item's stored rows, looked up once when
+// the item starts.
+template <int D, typename M>
+__device__ __forceinline__ void lane_row_layout(const M& q, const LaneClasses& lc, int32_t k, uint32_t& b,
+                                                uint32_t& off) {
+  b = 0u;
+  off = 0u;
+  if (lc.n > 0) {
+    int32_t st = rdlane(lc.start, lc.lane0);
+    int32_t bb = rdlane(lc.bits, lc.lane0);
+    uint32_t base = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), lc.lane0));
+    for (int c = 1; c < lc.n; ++c) {
+      const int32_t sc = rdlane(lc.start, lc.lane0 + c);
+      const int32_t bc = rdlane(lc.bits, lc.lane0 + c);
+      const uint32_t basec = static_cast<uint32_t>(rdlane(static_cast<int>(lc.base), lc.lane0 + c));
+      if (k >= sc) {                                   // per lane
+        st = sc;
+        bb = bc;
+        base = basec;
+      }
+    }
+    if (k >= 0) {
+      b = static_cast<uint32_t>(bb);
+      const uint32_t words = (b == 32u) ? static_cast<uint32_t>(D) : (b * static_cast<uint32_t>(D) + 31u) >> 5;
+      off = base + static_cast<uint32_t>(k - st) * words;
+    }
+  } else if (k >= 0) {
+    b = q.bits[k];
+    off = q.word_offset[k];
+  }
+}
+
+// The lane's code words of message row (b, off), both wavefront-uniform: its VEC raw floats for
+// b = 32, else the one or two words holding its VEC codes.
+template <int VEC>
+__device__ __forceinline__ void fetch_codes(const uint32_t* codes, uint32_t b, uint32_t off, int j0,
+                                            uint32_t (&wd)[VEC]) {
+  const uint32_t* row = codes + off;
+  if (b == 32u) {
+    float t[VEC];
+    load_row_unaligned<VEC>(reinterpret_cast<const float*>(row + j0), t);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) wd[v] = __float_as_uint(t[v]);
+  } else if (width_valid(b)) {
+    const uint32_t pos = static_cast<uint32_t>(j0) * b;
+    wd[0] = row[pos >> 5];
+    if constexpr (VEC * 8 > 32) wd[1] = (b * VEC > 32u) ? row[(pos >> 5) + 1] : 0u;
+  }
+}
+
+// The lane's VEC features of a message row from its code words: scale * q + min (the raw float for
+// b = 32; 0 for a width outside {1, 2, 4, 8, 32}).
+template <int VEC>
+__device__ __forceinline__ void dequant_lane(uint32_t b, float zp, float sc, int j0, const uint32_t (&wd)[VEC],
+                                             float (&q)[VEC]) {
+  if (b == 32u) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) q[v] = __uint_as_float(wd[v]);
+  } else if (width_valid(b)) {
+    const uint32_t mask = (1u << b) - 1u;
+    const uint32_t sh = (static_cast<uint32_t>(j0) * b) & 31u;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const uint32_t bit = sh + static_cast<uint32_t>(v) * b;
+      uint32_t word = wd[0] >> (bit & 31u);
+      if constexpr (VEC * 8 > 32) {
+        if (bit >= 32u) word = wd[1] >> (bit - 32u);
+      }
+      q[v] = dequant(sc, word & mask, zp);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) q[v] = 0.0f;
+  }
+}
+
+// racc += the lane's features of the dequantised received rows idx[p0 .. p1), in list order, each
+// added in float64 as the neighbour gather adds a halo row of weight 1 (the list is
+// wavefront-uniform; rows are looked up as they come).
+template <int D>
+__device__ __forceinline__ void add_received_rows(const RecvAdd& r, const LaneClasses& lr, int32_t p0, int32_t p1,
+                                                  int j0, double (&racc)[vec_of(D)]) {
+  constexpr int VEC = vec_of(D);
+  for (int32_t i = p0; i < p1; ++i) {
+    const int32_t k = cst(r.idx)[i];
+    uint32_t b, off;
+    message_row_layout<D>(r, lr, k, b, off);
+    cptr<float> m = cst(r.meta) + 2 * static_cast<int64_t>(k);
+    const float zp = m[0], sc = m[1];
+    uint32_t wd[VEC];
+    fetch_codes<VEC>(r.codes, b, off, j0, wd);
+    float q[VEC];
+    dequant_lane<VEC>(b, zp, sc, j0, wd, q);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) racc[v] = fma(1.0, static_cast<double>(q[v]), racc[v]);
+  }
+}
+
+template <int D, bool HALO, bool BETA, bool QUANT, bool RECV = false>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  static_assert(!RECV || QUANT, "received rows are added by the quantising gathers");
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;           // lanes that own features
   constexpr int B = batch_of(D, HALO);
@@ -385,6 +508,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   int cur = 0;                                  // row of the group being summed
   int32_t cur_end = rdlane(v_end, 0);
 
+  const LaneClasses lr = RECV ? lane_classes(a.r.cls, lane) : LaneClasses();
   auto flush = [&]() {                          // write row `cur` and start the next one
     const int64_t orow = rdlane(v_out, cur);
     if (QUANT && orow >= a.q.first) {
@@ -392,19 +516,34 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
       quantize_out_row<D>(a.q, orow - a.q.first, res, lane, j0, owner);
-    } else if (owner) {
-      float* dst = a.out + orow * a.ldo + j0;
-      float res[VEC];
-      if constexpr (BETA) {
-        float old[VEC];
-        load_row<VEC>(dst, old);
+    } else {
+      double racc[VEC];
+      bool recv = false;
+      if constexpr (RECV) {
+        const int32_t p0 = cst(a.r.ptr)[orow], p1 = cst(a.r.ptr)[orow + 1];
+        recv = p1 > p0;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+        for (int v = 0; v < VEC; ++v) racc[v] = 0.0;
+        add_received_rows<D>(a.r, lr, p0, p1, j0, racc);
       }
-      store_row<VEC>(dst, res);
+      if (owner) {
+        float* dst = a.out + orow * a.ldo + j0;
+        float res[VEC];
+        if constexpr (BETA) {
+          float old[VEC];
+          load_row<VEC>(dst, old);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+        }
+        if (recv) {                               // the row as stored, then its received rows added
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(res[v]) + racc[v]);
+        }
+        store_row<VEC>(dst, res);
+      }
     }
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
@@ -548,8 +687,9 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit buffer, range-che
 #ifndef QHA_QUANT_ROWS_BATCH
 #define QHA_QUANT_ROWS_BATCH 8    // edges per batch when the gather also codes message rows (its epilogue is inlined per edge)
 #endif
-template <int D, bool BETA, bool QUANT>
+template <int D, bool BETA, bool QUANT, bool RECV = false>
 __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
+  static_assert(!RECV || QUANT, "received rows are added by the quantising gathers");
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;
   constexpr int B = QUANT ? (rows_batch_of(D) * QHA_QUANT_ROWS_BATCH / QHA_ROWS_BATCH) : rows_batch_of(D);
@@ -593,7 +733,49 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
   int cur = 0;
   int32_t cur_end = rdlane(v_end, 0);
   DrawCache dc;
-  const LaneClasses lc = QUANT ? lane_classes(a.q.cls, lane) : LaneClasses();
+  LaneClasses lc = QUANT ? lane_classes(a.q.cls, lane) : LaneClasses();
+
+  // Received rows of the item's stored rows, one row per lane: the first received row of each (-1:
+  // none), its width (with bit 8 set when the list holds more rows), first code word and (min,
+  // scale).  The code words of the next row that takes one are loaded when the row before it closes
+  // (those of the first row here), so adding them waits for nothing; further rows of a list (a node
+  // with several copies) are looked up and loaded as the row closes.
+  const LaneClasses lr = RECV ? lane_classes_beside(lc, a.r.cls, lane) : LaneClasses();
+  if constexpr (RECV) {          // both tables in one set of registers
+    lc.start = lr.start;
+    lc.bits = lr.bits;
+    lc.base = lr.base;
+  }
+  int32_t v_rk = -1;
+  uint32_t v_rb = 0u, v_roff = 0u;
+  float v_rzp = 0.0f, v_rsc = 0.0f;
+  uint32_t pre[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) pre[v] = 0u;
+  auto prefetch = [&](int row) {                // row < nrows
+    if (rdlane(v_rk, row) >= 0)
+      fetch_codes<VEC>(a.r.codes, static_cast<uint32_t>(rdlane(static_cast<int>(v_rb), row)) & 0xFFu,
+                       static_cast<uint32_t>(rdlane(static_cast<int>(v_roff), row)), j0, pre);
+  };
+  if constexpr (RECV) {
+    if (!split) {
+      bool more = false;
+      if (v_out < a.q.first) {
+        const int32_t p0 = a.r.ptr[v_out], p1 = a.r.ptr[v_out + 1];
+        if (p1 > p0) v_rk = a.r.idx[p0];
+        more = p1 - p0 > 1;
+      }
+      lane_row_layout<D>(a.r, lr, v_rk, v_rb, v_roff);
+      if (more) v_rb |= 0x100u;
+      if (v_rk >= 0) {
+        const float2 m = *reinterpret_cast<const float2*>(a.r.meta + 2 * static_cast<int64_t>(v_rk));
+        v_rzp = m.x;
+        v_rsc = m.y;
+      }
+      prefetch(0);
+    }
+  }
+
   auto flush = [&]() {
     const int64_t orow = rdlane(v_out, cur);
     if (QUANT && orow >= a.q.first) {
@@ -606,19 +788,40 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs a) {
       draws_of_row<D>(a.q, dc, k, lane, j0, w);
       message_row_layout<D>(a.q, lc, k, b, off);
       quantize_row_with_draws<D>(a.q, k, b, off, res, lane, j0, owner, w);
-    } else if (owner) {
-      float* dst = a.out + orow * a.ldo + j0;
-      float res[VEC];
-      if constexpr (BETA) {
-        float old[VEC];
-        load_row<VEC>(dst, old);
+    } else {
+      double racc[VEC];
+      bool recv = false;
+      if constexpr (RECV) {
+        if (rdlane(v_rk, cur) >= 0) {
+          recv = true;
+          const uint32_t info = static_cast<uint32_t>(rdlane(static_cast<int>(v_rb), cur));
+          float q[VEC];
+          dequant_lane<VEC>(info & 0xFFu, rdlanef(v_rzp, cur), rdlanef(v_rsc, cur), j0, pre, q);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+          for (int v = 0; v < VEC; ++v) racc[v] = fma(1.0, static_cast<double>(q[v]), 0.0);
+          if (info & 0x100u)
+            add_received_rows<D>(a.r, lr, cst(a.r.ptr)[orow] + 1, cst(a.r.ptr)[orow + 1], j0, racc);
+        }
+        if (cur + 1 < nrows) prefetch(cur + 1);
       }
-      store_row<VEC>(dst, res);
+      if (owner) {
+        float* dst = a.out + orow * a.ldo + j0;
+        float res[VEC];
+        if constexpr (BETA) {
+          float old[VEC];
+          load_row<VEC>(dst, old);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(old[v]) + acc[v]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
+        }
+        if (recv) {                               // the row as stored, then its received rows added
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(static_cast<double>(res[v]) + racc[v]);
+        }
+        store_row<VEC>(dst, res);
+      }
     }
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
@@ -943,8 +1146,9 @@ __global__ __launch_bounds__(256) void gather_grouped_kernel(GatherArgs a) {
 }
 
 // Adds the partial sums of every split row in chunk order and writes (or quantises) the row.
-template <int D, bool QUANT>
+template <int D, bool QUANT, bool RECV = false>
 __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
+  static_assert(!RECV || QUANT, "received rows are added by the quantising gathers");
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;
   const int lane = threadIdx.x & 63;
@@ -969,11 +1173,26 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) res[v] = static_cast<float>(acc[v]);
     quantize_out_row<D>(a.q, orow - a.q.first, res, lane, j0, owner);
-  } else if (owner) {
-    float* dst = a.out + orow * a.ldo + j0;
+  } else {
+    double racc[VEC];
+    bool recv = false;
+    if constexpr (RECV) {
+      const LaneClasses lr = lane_classes(a.r.cls, lane);
+      const int32_t p0 = cst(a.r.ptr)[orow], p1 = cst(a.r.ptr)[orow + 1];
+      recv = p1 > p0;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v)
-      dst[v] = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
+      for (int v = 0; v < VEC; ++v) racc[v] = 0.0;
+      add_received_rows<D>(a.r, lr, p0, p1, j0, racc);
+    }
+    if (owner) {
+      float* dst = a.out + orow * a.ldo + j0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        float res = static_cast<float>(a.beta ? static_cast<double>(dst[v]) + acc[v] : acc[v]);
+        if (recv) res = static_cast<float>(static_cast<double>(res) + racc[v]);
+        dst[v] = res;
+      }
+    }
   }
 }
 
@@ -992,6 +1211,9 @@ __global__ __launch_bounds__(256) void edge_weights_kernel(int64_t n_rows, const
 
 template <int D>
 hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_out, hipStream_t s) {
+  // received rows are added to the stored rows of quantising gathers only
+  if (a.r.ptr != nullptr && !quantize_out) return hipErrorInvalidValue;
+  const bool recv = a.r.ptr != nullptr;
   // the plain-row kernel addresses x with 32-bit byte offsets
   const int64_t x_bytes = a.n_inner > 0 ? ((a.n_inner - 1) * a.ldx + D) * 4 : 0;
   const bool rows_ok = x_bytes <= static_cast<int64_t>(0xFFFFFFFFu) && QHA_ROWS_KERNEL;
@@ -1025,11 +1247,21 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_ou
     if (quantize_out && rows_ok) {
       GatherArgs r = a;
       r.x_bytes = static_cast<uint32_t>(x_bytes);
-      if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true, true>), grid, dim3(256), 0, s, r);
-      else hipLaunchKernelGGL((gather_rows_kernel<D, false, true>), grid, dim3(256), 0, s, r);
+      if (recv) {
+        if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true, true, true>), grid, dim3(256), 0, s, r);
+        else hipLaunchKernelGGL((gather_rows_kernel<D, false, true, true>), grid, dim3(256), 0, s, r);
+      } else {
+        if (a.beta) hipLaunchKernelGGL((gather_rows_kernel<D, true, true>), grid, dim3(256), 0, s, r);
+        else hipLaunchKernelGGL((gather_rows_kernel<D, false, true>), grid, dim3(256), 0, s, r);
+      }
     } else if (quantize_out) {
-      if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gather_kernel<D, false, false, true>), grid, dim3(256), 0, s, a);
+      if (recv) {
+        if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true, true, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gather_kernel<D, false, false, true, true>), grid, dim3(256), 0, s, a);
+      } else {
+        if (a.beta) hipLaunchKernelGGL((gather_kernel<D, false, true, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gather_kernel<D, false, false, true>), grid, dim3(256), 0, s, a);
+      }
     } else if (with_halo && grouped_ok) {
       GatherArgs r = a;
       if (single_base) {
@@ -1062,7 +1294,9 @@ hipError_t launch_gather_d(const GatherArgs& a, bool with_halo, bool quantize_ou
   }
   if (a.n_split_rows > 0) {
     const int64_t blocks = (a.n_split_rows + 3) / 4;
-    if (quantize_out)
+    if (recv)
+      hipLaunchKernelGGL((combine_split_kernel<D, true, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    else if (quantize_out)
       hipLaunchKernelGGL((combine_split_kernel<D, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((combine_split_kernel<D, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);

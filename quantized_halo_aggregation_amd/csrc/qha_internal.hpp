@@ -48,6 +48,19 @@ struct QuantOut {
   uint32_t seed_lo, seed_hi, epoch, stream_id, node_base;
 };
 
+// Received messages added to the stored rows of a quantising gather (ptr == nullptr: none).  Stored
+// row r gets, after its own rounding, the float64 sum of the dequantised message rows
+// idx[ptr[r] .. ptr[r + 1]) in that order, rounded to float32 once more.
+struct RecvAdd {
+  const int32_t* ptr;
+  const int32_t* idx;
+  const uint32_t* codes;
+  const float* meta;
+  const uint8_t* bits;
+  const uint32_t* word_offset;
+  Classes cls;
+};
+
 // One gather over a CSR: out[row_ids[i]] (+)= sum_e w[e] * value(col_e).  value() is a float32
 // row of x for col < n_inner and a dequantised halo message for col >= n_inner.
 struct GatherArgs {
@@ -85,6 +98,7 @@ struct GatherArgs {
   int64_t ldo;
   double* partial;            // [n_split_items, d] float64 partial sums of split rows
   QuantOut q;                 // with launch_gather(..., quantize_out = true)
+  RecvAdd r;                  // with quantize_out: messages added to the stored rows
 };
 
 struct GemmArgs {

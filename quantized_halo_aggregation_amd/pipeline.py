@@ -86,6 +86,9 @@ class GpuPartition:
         self.mirror = dev(part.mirror)
         self.m_ptr, self.m_idx, self.m_rows = dev(mc_ptr), dev(m_idx), dev(targets)
         self.h_m_ptr = mc_ptr
+        # the same lists over every inner node (empty for nodes without copies): the received
+        # messages the one-launch transposed gather adds as it stores the inner rows
+        self.c_ptr = dev(m_ptr)
 
         self.set_bits(part.bits if bits is None else bits)
 
@@ -265,14 +268,22 @@ class GpuPartition:
                                  workspace=self.agg_ws if workspace is None else workspace)
 
     def aggregate_bwd_all_quantize(self, grad_out, dx_inner, msg: Messages, epoch, stream_id, beta,
-                                   seed=QUANT_SEED):
+                                   seed=QUANT_SEED, received: Messages = None):
         """a6 over every column + a7 in one launch: the inner columns' gradients into dx_inner (added
         to it when beta = 1), the halo columns' gradients quantised into msg as quantize_send would
-        code them, without storing them."""
+        code them, without storing them.  With received (messages that arrived before the call, in
+        their own layout), a8 too: each inner row gets its copies' dequantised messages added as it
+        is stored, exactly as add_received would add them afterwards."""
         lay = self._stamp(msg)
+        rcv = None
+        if received is not None:
+            rl = received.layout or self.layout
+            rcv = (self.c_ptr, self.m_idx, self.n_h, received.codes, received.meta, rl.bits, rl.word_offset,
+                   rl.classes)
         B.aggregate_bwd_quantize(self.colptr, self.rowidx, self.w_bwd, self.plan_bwd_all, grad_out, self.n_in, self.d,
                                  lay.bits, lay.word_offset, lay.classes, seed, epoch, stream_id, self.n_in, msg.codes,
-                                 msg.meta, workspace=self.agg_ws, grad_in=dx_inner, n_stored=self.n_in, beta=beta)
+                                 msg.meta, workspace=self.agg_ws, grad_in=dx_inner, n_stored=self.n_in, beta=beta,
+                                 received=rcv)
 
     def aggregate_bwd_inner(self, grad_out, dx_inner, beta):
         """a6 (inner range): gradients of the inner columns (beta = 1 adds to dx_inner)."""
@@ -309,10 +320,13 @@ class LayerStack:
 
     def __init__(self, gp: GpuPartition, weights, x, grad_top, seed=QUANT_SEED, fused_halo_bwd: bool = False,
                  pipelined: bool = False, max_bits: int = 0, fold_received: bool = False,
-                 split_interior: bool = False):
+                 split_interior: bool = False, recv_in_gather: bool = True):
         self.gp = gp
         self.seed = seed
         self.fused_halo_bwd = fused_halo_bwd
+        # asynchronous epochs of the one-launch backward: the previous epoch's received messages are
+        # added by that launch as it stores the inner rows (no separate received add)
+        self.recv_in_gather = recv_in_gather
         self.fold_received = fold_received
         self.split_interior = split_interior
         if split_interior:
@@ -439,9 +453,15 @@ class LayerStack:
         if self.one_fused:
             # one launch over every column: the inner columns' gradients into dX (added to the self
             # half for SAGE), the halo columns' gradients coded into this epoch's message (it stays on
-            # the compute stream in an asynchronous epoch too: its inner rows are needed next)
-            gp.aggregate_bwd_all_quantize(g, self.dX[l], msg, epoch, stream_id, beta, self.seed)
-            if hook: hook("aggregate_bwd_quantize", l)
+            # the compute stream in an asynchronous epoch too: its inner rows are needed next).  In an
+            # asynchronous epoch the messages received are the previous epoch's, there before the
+            # launch, so the launch adds them to the inner rows as it stores them.
+            fold = not sync and self.recv_in_gather
+            gp.aggregate_bwd_all_quantize(g, self.dX[l], msg, epoch, stream_id, beta, self.seed,
+                                          received=self.msg_b[l][1 - slot] if fold else None)
+            if hook: hook("aggregate_bwd_quantize_received" if fold else "aggregate_bwd_quantize", l)
+            if fold:
+                return
         elif self.fused_halo_bwd:
             send = lambda: gp.aggregate_bwd_halo_quantize(g, msg, epoch, stream_id, self.seed,
                                                           workspace=None if sync else self.comm_ws)

@@ -24,7 +24,7 @@ def test_header_symbols_are_exported():
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} declared in qha.h but not exported"
     assert declared == set(B.EXPORTED)
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
 
 
 def test_status_strings():
@@ -241,3 +241,33 @@ def test_noalloc_aggregation_rejects_before_any_hip_call():
     assert call(d=128, ldx=128, ldo=96) == B.QHA_ERR_INVALID_ARG
     assert call(d=100) == B.QHA_ERR_UNSUPPORTED
     assert call(n_rows=0) == B.QHA_OK
+
+
+def test_received_messages_rejected_before_any_hip_call():
+    """The received messages of the one-launch transposed gather are checked on the host: null lists,
+    a buffer that is the call's own output, misaligned arrays, classes that do not cover the rows."""
+    f = B._aggregate_bwd_quantize
+    out_codes, out_meta = FAKE, FAKE + 4096
+    rs = B.ReceivedStruct(FAKE, FAKE, 5, FAKE + 8192, FAKE + 12288, FAKE, FAKE, None)
+    args = dict(n_rows=10, colptr=FAKE, rowidx=FAKE, w=None, plan=None, g=FAKE, ldg=128, n_grad=10, d=128,
+                n_stored=5, beta=0, gi=FAKE, ldi=128, bits=FAKE, wo=FAKE, classes=None, seed=1, epoch=0, sid=0,
+                base=0, codes=out_codes, meta=out_meta, rcv=C.byref(rs), ws=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    def with_rs(**fields):
+        r = B.ReceivedStruct(*[fields.get(n, getattr(rs, n)) for n, _ in B.ReceivedStruct._fields_])
+        return call(rcv=C.byref(r))
+    assert with_rs(copy_ptr=None) == B.QHA_ERR_INVALID_ARG
+    assert with_rs(copy_idx=None) == B.QHA_ERR_INVALID_ARG
+    assert with_rs(codes=None) == B.QHA_ERR_INVALID_ARG
+    assert with_rs(n_rows=-1) == B.QHA_ERR_INVALID_ARG
+    assert with_rs(codes=out_codes) == B.QHA_ERR_INVALID_ARG
+    assert "writes" in B._last_error().decode()
+    assert with_rs(meta=out_meta) == B.QHA_ERR_INVALID_ARG
+    assert with_rs(meta=FAKE + 12292) == B.QHA_ERR_INVALID_ARG          # (min, scale) pairs misaligned
+    assert with_rs(bits=None) == B.QHA_ERR_INVALID_ARG                  # no widths at all
+    cl = B.pack_classes(np.array([4] * 4, np.uint8), 128)               # classes of 4 rows, buffer of 5
+    assert with_rs(bits=None, word_offset=None, classes=C.pointer(cl)) == B.QHA_ERR_INVALID_ARG

@@ -199,6 +199,60 @@ def test_one_launch_gradients_and_halo_messages(case, grouped, beta):
     H.assert_bits_equal(H.host(fused.meta), H.host(two.meta), "(min, scale)")
 
 
+# widths of an earlier epoch's messages: each class moved to another width, so that the received
+# buffer's layout differs from the one the call writes
+_EARLIER = {1: 2, 2: 4, 4: 8, 8: 32, 32: 1}
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("layouts", [(True, True), (False, True), (True, False)],
+                         ids=["classes", "offset-table-out", "offset-table-received"])
+@pytest.mark.parametrize("beta", [0, 1])
+def test_one_launch_adds_received_messages(case, layouts, beta):
+    """qha_aggregate_bwd_quantize with messages received earlier (at other widths, in their own
+    layout): every inner row equals, bit for bit, the launch without them followed by the received
+    add (qha_dequant_aggregate_fwd over the copy lists); the messages it codes are unchanged; and
+    the inner rows match the oracle's transposed aggregate plus its received add.  n_h > n_in cases
+    give inner nodes several copies; heavy columns split into chunks go through the combine."""
+    H.require_gpu()
+    import torch
+    part, gp = _setup(case)
+    grouped_out, grouped_rcv = layouts
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    rng = np.random.default_rng(13)
+    g = rng.standard_normal((n_in, d)).astype(np.float32)
+    old = rng.standard_normal((n_in, d)).astype(np.float32)
+    earlier = np.array([_EARLIER[int(b)] for b in part.bits], np.uint8)
+    gp.set_bits(earlier, grouped=grouped_rcv)
+    rows = rng.standard_normal((n_h, d)).astype(np.float32)
+    msg = H.oracle_messages(rows, earlier, SEED, 2, 9, n_in)
+    rcv = H.upload_messages(gp, msg)
+    rcv.layout = gp.layout
+    gp.set_bits(part.bits, grouped=grouped_out)
+    g_dev = H.dev(g)
+    H.note(f"one-launch with received messages {_case_id(case)} layouts={layouts} beta={beta}")
+
+    start = lambda: H.dev(old) if beta else torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+    two_in, two_msg = start(), gp.new_messages()
+    gp.aggregate_bwd_all_quantize(g_dev, two_in, two_msg, 4, 7, beta)
+    gp.add_received(rcv, two_in)
+    one_in, one_msg = start(), gp.new_messages()
+    one_msg.codes.fill_(-559038737)
+    gp.aggregate_bwd_all_quantize(g_dev, one_in, one_msg, 4, 7, beta, received=rcv)
+    H.assert_bits_equal(H.host(one_in), H.host(two_in), "inner rows with received messages")
+    H.assert_bits_equal(H.host(one_msg.codes).view(np.uint32)[:gp.total_words],
+                        H.host(two_msg.codes).view(np.uint32)[:gp.total_words], "codes")
+    H.assert_bits_equal(H.host(one_msg.meta), H.host(two_msg.meta), "(min, scale)")
+
+    if part.wl.model == "gcn":
+        t = OA.gcn_aggregate_t(part.nbr_ptr, part.nbr_idx, part.deg, g)[:n_in]
+    else:
+        t = OA.mean_aggregate_t(part.nbr_ptr, part.nbr_idx, g, n_in + n_h)[:n_in]
+    stored = (old.astype(np.float64) + t) if beta else t
+    H.assert_close(H.host(one_in), OA.add_received(stored, part.mirror, msg["received"]),
+                   what="inner rows vs the oracle")
+
+
 def test_deterministic_repeats():
     H.require_gpu()
     import torch

@@ -189,3 +189,29 @@ def test_interior_split_gives_the_unsplit_result(d):
                 assert np.all(part.nbr_idx[part.nbr_ptr[r]:part.nbr_ptr[r + 1]] < n_in)
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("model", ["gcn", "sage"])
+def test_async_received_add_in_the_gather_changes_nothing(model):
+    """In an asynchronous epoch the one-launch transposed gather adds the previous epoch's received
+    messages as it stores the inner rows; the epoch's every output (H, dX, dW and the messages it
+    codes, forward and backward) equals, bit for bit, the same epoch with the separate received add."""
+    H.require_gpu()
+    from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
+    part = synth.make_partition(synth.Workload(96, f"async-fold-{model}", 1200, 700, 16000, 128, 2, model,
+                                               ("top", 4, 8, 0.1)))
+    outs = []
+    for fold in (True, False):
+        gp = GpuPartition(part, chunk=64)
+        st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=True, pipelined=True,
+                        recv_in_gather=fold)
+        H.note(f"async received add in the gather={fold} ({model})")
+        seen = []
+        st.step(epoch=0)
+        st.step(epoch=1, sync=False, hook=lambda name, l: seen.append(name))
+        assert ("aggregate_bwd_quantize_received" in seen) == fold and ("add_received" in seen) != fold
+        outs.append([H.host(t).copy() for l in range(st.L)
+                     for t in (st.H[l], st.dX[l], st.dW[l], st.msg_f[l][1].codes, st.msg_f[l][1].meta,
+                               st.msg_b[l][1].codes, st.msg_b[l][1].meta)])
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"output {i} differs"
