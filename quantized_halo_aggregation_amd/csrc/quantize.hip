@@ -68,10 +68,30 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
       v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
     }
   }
+  // The rounding draws depend only on the row's node id and the lane's groups, not on its values:
+  // the two Philox calls (features 16 gl + 8 h .. + 7 are group 2 gl + h) run while the row's loads
+  // are in flight.
+  uint32_t w[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t c0 = a.node_base + static_cast<uint32_t>(r);
+    uint32_t c1 = static_cast<uint32_t>(2 * gl + h);
+    uint32_t c2 = a.epoch;
+    uint32_t c3 = a.stream_id;
+    philox4x32_10(c0, c1, c2, c3, a.seed_lo, a.seed_hi);
+    // an empty statement that takes the four words as register operands: it keeps their computation
+    // here, beside the row's loads, where the compiler would otherwise sink it past the branches below
+    asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+    w[h][0] = c0;
+    w[h][1] = c1;
+    w[h][2] = c2;
+    w[h][3] = c3;
+  }
   uint32_t b, row_off;
   if (a.cls.n > 0) {
-    // width-grouped buffer (fewer than 2^31 rows): the class of the wave's first row from scalar
-    // compares; a wave whose rows cross into the next class looks its rows up one by one
+    // width-grouped buffer (fewer than 2^31 rows): the class of the wave's first row by selects over
+    // the whole table (no branch waits on a table entry); a wave whose rows cross into the next
+    // class looks its rows up one by one
     const int32_t w0 = static_cast<int32_t>(r0);
     const int32_t wl = w0 + (RPW - 1);
     int32_t st = a.cls.start[0];
@@ -80,25 +100,22 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
     bool straddle = false;
 #pragma unroll
     for (int c = 1; c < kMaxClasses; ++c) {
-      if (c < a.cls.n) {
-        if (w0 >= a.cls.start[c]) {
-          st = a.cls.start[c];
-          base = a.cls.base[c];
-          bb = a.cls.bits[c];
-        } else if (wl >= a.cls.start[c]) {
-          straddle = true;
-        }
-      }
+      const bool in = c < a.cls.n;
+      const int32_t sc = a.cls.start[c];
+      const bool ge = in && w0 >= sc;
+      st = ge ? sc : st;
+      base = ge ? a.cls.base[c] : base;
+      bb = ge ? a.cls.bits[c] : bb;
+      straddle = straddle || (in && !ge && wl >= sc);
     }
     const int32_t r32 = static_cast<int32_t>(rc);
     if (straddle) {
 #pragma unroll
       for (int c = 1; c < kMaxClasses; ++c) {
-        if (c < a.cls.n && r32 >= a.cls.start[c]) {
-          st = a.cls.start[c];
-          base = a.cls.base[c];
-          bb = a.cls.bits[c];
-        }
+        const bool ge = c < a.cls.n && r32 >= a.cls.start[c];
+        st = ge ? a.cls.start[c] : st;
+        base = ge ? a.cls.base[c] : base;
+        bb = ge ? a.cls.bits[c] : bb;
       }
     }
     b = static_cast<uint32_t>(bb);
@@ -120,27 +137,23 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(QuantArgs a) {
 
   const bool active = valid && width_valid(b);
   const bool raw = b == 32u;
-  // the lane's 16 codes in four groups: code 4k + i at bit i b of acc[k]
+  const bool coded = active && !raw;
+  // The lane's 16 codes in four groups: code 4k + i at bit i b of acc[k].  Every lane forms them
+  // (rows that are raw or not written use width 1 and keep nothing), so that the draws, which every
+  // lane uses, stay where they are computed: ahead of the wait for the row.
+  const uint32_t bq = coded ? b : 1u;
+  const RowScale rs = row_scale(mn, mx, bq);
+  const float zp = coded ? rs.zp : 0.0f;
+  const float sc = coded ? rs.sc : 0.0f;
   uint32_t acc[4] = {0u, 0u, 0u, 0u};
-  float sc = 0.0f, zp = 0.0f;
-  if (active && !raw) {
-    const RowScale rs = row_scale(mn, mx, b);
-    zp = rs.zp;
-    sc = rs.sc;
-    const uint32_t sh[4] = {0u, b, 2u * b, 3u * b};
+  {
+    const uint32_t sh[4] = {0u, bq, 2u * bq, 3u * bq};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      // features 16 gl + 8 h .. +7 are group 2 gl + h
-      uint32_t c0 = a.node_base + static_cast<uint32_t>(r);
-      uint32_t c1 = static_cast<uint32_t>(2 * gl + h);
-      uint32_t c2 = a.epoch;
-      uint32_t c3 = a.stream_id;
-      philox4x32_10(c0, c1, c2, c3, a.seed_lo, a.seed_hi);
-      const uint32_t w[4] = {c0, c1, c2, c3};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = 8 * h + i;
-        const uint32_t q = code_of(v[j], mn, rs, draw16_c(w, i));
+        const uint32_t q = code_of(v[j], mn, rs, draw16_c(w[h], i));
         acc[j >> 2] |= q << sh[j & 3];
       }
     }
