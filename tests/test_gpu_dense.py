@@ -247,14 +247,16 @@ def test_general_width_error_is_float32_class(m, d_in, d_out):
     assert e_dw.max() <= 16 * 2.0 ** -24, f"dW: {e_dw.max() * 2**24:.2f} units of 2^-24"
 
 
-@pytest.mark.parametrize("m,n,k,tb,mask", [(20000, 256, 512, 1, False), (20000, 512, 256, 0, True),
-                                           (16384, 516, 64, 1, False), (17001, 52, 132, 0, True),
-                                           (16383, 256, 512, 1, False)])
-def test_b_split_once_gives_the_same_bits(m, n, k, tb, mask):
+@pytest.mark.parametrize("m,n,k,tb,mask,beta", [(20000, 256, 512, 1, False, 0), (20000, 512, 256, 0, True, 0),
+                                                (16384, 516, 64, 1, False, 0), (17001, 52, 132, 0, True, 0),
+                                                (16383, 256, 512, 1, False, 0), (16385, 300, 100, 0, True, 1),
+                                                (20001, 256, 96, 1, False, 1), (16400, 768, 32, 1, True, 0)])
+def test_b_split_once_gives_the_same_bits(m, n, k, tb, mask, beta):
     """With a workspace of qha_dense_project_workspace bytes, a product over at least 16384 rows of
     A splits B into its bf16 parts once per call instead of per tile; the bits must not change
-    (same parts, same products, same order): ragged n and k, both storage orders of B, the ReLU
-    mask, and a row count just below the threshold (no split, same bits trivially)."""
+    (same parts, same products, same order): ragged m, n and k, odd and single k-step counts, both
+    storage orders of B, the ReLU mask, beta = 1, and a row count just below the threshold (no
+    split, same bits trivially)."""
     H.require_gpu()
     import torch
     from quantized_halo_aggregation_amd import binding as B
@@ -269,16 +271,18 @@ def test_b_split_once_gives_the_same_bits(m, n, k, tb, mask):
     ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
     a_d, b_d = H.dev(a), H.dev(b)
     aux_d = H.dev(aux) if mask else None
+    c0 = rng.standard_normal((m, n)).astype(np.float32)
     outs = []
     for w in (ws, None):
-        H.note(f"b split once m={m} n={n} k={k} tb={tb} mask={mask} ws={w is not None}")
-        c = torch.full((m, n), np.nan, dtype=torch.float32, device="cuda")
-        B.dense_project(0, tb, a_d, b_d, 0, c, prologue=pro, aux=aux_d, workspace=w)
+        H.note(f"b split once m={m} n={n} k={k} tb={tb} mask={mask} beta={beta} ws={w is not None}")
+        c = H.dev(c0) if beta else torch.full((m, n), np.nan, dtype=torch.float32, device="cuda")
+        B.dense_project(0, tb, a_d, b_d, beta, c, prologue=pro, aux=aux_d, workspace=w)
         outs.append(H.host(c))
     H.assert_bits_equal(outs[0], outs[1], "B split once against B split per tile")
     a64 = np.where(aux > 0, a, 0.0) if mask else a.astype(np.float64)
     b64 = b.astype(np.float64)
-    H.assert_close(outs[0], a64 @ (b64.T if tb else b64), what="op(A) op(B)")
+    ref = a64 @ (b64.T if tb else b64) + (c0.astype(np.float64) if beta else 0.0)
+    H.assert_close(outs[0], ref, what="op(A) op(B)")
 
 
 def test_backward_b_split_once_matches_dense_project():
