@@ -253,6 +253,43 @@ def test_one_launch_adds_received_messages(case, layouts, beta):
                    what="inner rows vs the oracle")
 
 
+def test_one_launch_over_rows_beyond_4gib_matches_the_rows_kernel():
+    """Gradient rows spanning more than 4 GiB (rows 4.4 MB apart) take the general kernel, with 64-bit
+    addresses, instead of the plain-row kernel's 32-bit buffer offsets.  The one launch stores the
+    inner rows (beta = 0 and 1), codes the halo rows with per-row draws, adds earlier messages to the
+    stored rows, and combines the split heavy columns.  Every output equals, bit for bit, the same
+    call on compact rows, which takes the plain-row kernel."""
+    H.require_gpu()
+    import torch
+    part, gp = _setup(CASES[3])
+    n_in, n_h, d = part.n_in, part.n_h, part.d
+    ld = 1_100_000
+    assert (n_in - 1) * ld * 4 > 0xFFFFFFFF
+    rng = np.random.default_rng(17)
+    g = rng.standard_normal((n_in, d)).astype(np.float32)
+    old = rng.standard_normal((n_in, d)).astype(np.float32)
+    earlier = np.array([_EARLIER[int(b)] for b in part.bits], np.uint8)
+    gp.set_bits(earlier)
+    rcv = H.upload_messages(gp, H.oracle_messages(rng.standard_normal((n_h, d)).astype(np.float32), earlier, SEED,
+                                                  2, 9, n_in))
+    rcv.layout = gp.layout
+    gp.set_bits(part.bits)
+    H.note(f"one launch over gradient rows {ld * 4} bytes apart (general kernel)")
+    big = torch.empty((n_in, ld), dtype=torch.float32, device="cuda")
+    big[:, :d] = H.dev(g)
+    outs = []
+    for src in (big[:, :d], H.dev(g)):
+        for beta in (0, 1):
+            dxi = H.dev(old) if beta else torch.full((n_in, d), np.nan, dtype=torch.float32, device="cuda")
+            msg = gp.new_messages()
+            gp.aggregate_bwd_all_quantize(src, dxi, msg, 4, 7, beta, received=rcv)
+            outs.append((H.host(dxi), H.host(msg.codes).view(np.uint32)[:gp.total_words], H.host(msg.meta)))
+    del big
+    for beta in (0, 1):
+        for what, a, b in zip(("inner rows", "codes", "(min, scale)"), outs[beta], outs[2 + beta]):
+            H.assert_bits_equal(a, b, f"{what}, beta = {beta}: rows beyond 4 GiB against compact rows")
+
+
 def test_deterministic_repeats():
     H.require_gpu()
     import torch
