@@ -103,6 +103,8 @@ def main():
                     help="instead of the step line: one line with the step, quantise and aggregate times and "
                          "message bytes for every halo width in {1, 2, 4, 8, 32} on the chosen partition")
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--chunk-bwd", type=int, default=None)
+    ap.add_argument("--group-edges", type=int, default=None)
     ap.add_argument("--unfused-halo-bwd", action="store_true",
                     help="gather the halo columns' gradients into a buffer and quantise that, instead of coding "
                          "them inside the one-launch transposed gather (the default)")
@@ -136,7 +138,7 @@ def main():
     from quantized_halo_aggregation_amd.pipeline import GpuPartition, LayerStack
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    gp = GpuPartition(part, chunk=args.chunk or B.DEFAULT_CHUNK)
+    gp = GpuPartition(part, chunk=args.chunk, chunk_bwd=args.chunk_bwd, group_edges=args.group_edges)
     st = LayerStack(gp, part.weights, part.x, part.grad_top, fused_halo_bwd=fused,
                     split_interior=args.split_interior)
     torch.cuda.synchronize()

@@ -284,6 +284,16 @@ def csr_transpose(rowptr, colidx, n_cols: int):
     return colptr, rowidx
 
 
+def plan_items(rowptr, chunk: int = DEFAULT_CHUNK, group_edges: int = DEFAULT_GROUP_EDGES,
+               skip_empty: bool = False) -> int:
+    """The number of work items qha_agg_plan_size gives for this CSR (host only)."""
+    rowptr, pr = _host(rowptr, np.int32, "rowptr")
+    st = AggPlanStruct()
+    _check(_plan_size(rowptr.size - 1, pr, int(chunk), int(group_edges), int(skip_empty), C.byref(st)),
+           "qha_agg_plan_size")
+    return int(st.n_items)
+
+
 class AggPlan:
     """A work plan for one CSR (host arrays built by the library, kept on the device)."""
 

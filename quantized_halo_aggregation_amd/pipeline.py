@@ -24,6 +24,20 @@ from . import synth
 
 QUANT_SEED = synth.QUANT_SEED
 
+# Shape of the aggregation work plans, a scheduling choice that the results do not depend on beyond
+# the order in which float64 partials of a split row are added (measured on the five synthetic
+# partitions): heavy rows are cut into chunks of 256 edges in the forward plans and 512 in the
+# transposed ones, and short rows are grouped into items of at most 128 edges when items of 256 would
+# leave fewer than four per wavefront slot of the chip (8 per SIMD, 1024 SIMDs), else 256.
+PLAN_CHUNK_FWD = 256
+PLAN_CHUNK_BWD = 512
+PLAN_MIN_ITEMS = 4 * 8 * 1024
+
+
+def plan_group_edges(rowptr, chunk: int) -> int:
+    """The item edge budget of a plan over rowptr with the given chunk (see PLAN_MIN_ITEMS)."""
+    return 128 if B.plan_items(rowptr, chunk, 256) < PLAN_MIN_ITEMS else 256
+
 
 @dataclasses.dataclass
 class Layout:
@@ -58,8 +72,8 @@ class Messages:
 class GpuPartition:
     """Device-resident CSR / CSC / norms / widths / plans of one partition (set-up, untimed)."""
 
-    def __init__(self, part: synth.Partition, device: str = "cuda", chunk: int = B.DEFAULT_CHUNK,
-                 group_edges: int = B.DEFAULT_GROUP_EDGES, bits=None):
+    def __init__(self, part: synth.Partition, device: str = "cuda", chunk: int = None, group_edges: int = None,
+                 bits=None, chunk_bwd: int = None):
         self.part = part
         self.device = device
         n_in, n_h, d = part.n_in, part.n_h, part.d
@@ -125,13 +139,23 @@ class GpuPartition:
         if pos_t.size:
             self.w_recv[torch.from_numpy(pos_t).to(device)] = self.w_bwd[:pos_t.size]
 
-        self.chunk, self.group_edges = chunk, group_edges
+        # heavy rows are cut into chunks of `chunk` edges in the forward plans and `chunk_bwd` in the
+        # transposed ones (by default PLAN_CHUNK_FWD / PLAN_CHUNK_BWD; an explicit chunk alone sets
+        # both); items hold at most group_edges edges (by default plan_group_edges, per plan)
+        if chunk_bwd is None:
+            chunk_bwd = PLAN_CHUNK_BWD if chunk is None else chunk
+        if chunk is None:
+            chunk = PLAN_CHUNK_FWD
+        self.chunk, self.chunk_bwd, self.group_edges = chunk, chunk_bwd, group_edges
         self.int_rows = None
-        mk = lambda rp: B.AggPlan(rp, chunk, group_edges, device=device)
+
+        def mk(rp, c=chunk):
+            g = plan_group_edges(rp, c) if group_edges is None else group_edges
+            return B.AggPlan(rp, c, g, device=device)
         self.plan_fwd = mk(ptr)
-        self.plan_bwd_halo = mk(colptr[n_in:])
-        self.plan_bwd_inner = mk(colptr[:n_in + 1])
-        self.plan_bwd_all = mk(colptr)
+        self.plan_bwd_halo = mk(colptr[n_in:], chunk_bwd)
+        self.plan_bwd_inner = mk(colptr[:n_in + 1], chunk_bwd)
+        self.plan_bwd_all = mk(colptr, chunk_bwd)
         self.plan_mirror = mk(mc_ptr)
         self.plan_recv = mk(self.h_r_ptr)
         ws = max(p.workspace_bytes(d) for p in (self.plan_fwd, self.plan_bwd_halo, self.plan_bwd_inner,
@@ -162,7 +186,8 @@ class GpuPartition:
             c = self.norm if self.model == "gcn" else None
             w = torch.empty(max(sidx.size, 1), dtype=torch.float32, device=self.device)
             B.edge_weights(sptr_d, sidx_d, r.contiguous(), c, w)
-            return rows_d, sptr_d, sidx_d, w, B.AggPlan(sptr, self.chunk, self.group_edges, device=self.device)
+            g = plan_group_edges(sptr, self.chunk) if self.group_edges is None else self.group_edges
+            return rows_d, sptr_d, sidx_d, w, B.AggPlan(sptr, self.chunk, g, device=self.device)
 
         self.int_rows, self.int_ptr, self.int_idx, self.int_w, self.plan_int = sub(np.flatnonzero(interior))
         self.bnd_rows, self.bnd_ptr, self.bnd_idx, self.bnd_w, self.plan_bnd = sub(np.flatnonzero(~interior))
