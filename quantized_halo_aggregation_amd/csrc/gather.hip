@@ -1160,12 +1160,31 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   const int64_t row = cst(a.split_row)[m];
   const int32_t i0 = cst(a.split_ptr)[m];
   const int32_t i1 = cst(a.split_ptr)[m + 1];
+  // the partials are added one by one in chunk order; the loads of U chunks (8, or 4 at d = 512)
+  // are issued together, so a row of many chunks waits for memory once per U instead of once per
+  // chunk
+  constexpr int U = VEC >= 8 ? 4 : 8;
+  const double* pp = a.partial + j0;
   double acc[VEC];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) acc[v] = a.partial[static_cast<int64_t>(i0) * D + j0 + v];
-  for (int32_t i = i0 + 1; i < i1; ++i) {
+  for (int v = 0; v < VEC; ++v) acc[v] = pp[static_cast<int64_t>(i0) * D + v];
+  int32_t i = i0 + 1;
+  for (; i + U <= i1; i += U) {
+    double t[U][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + a.partial[static_cast<int64_t>(i) * D + j0 + v];
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) t[u][v] = pp[static_cast<int64_t>(i + u) * D + v];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + t[u][v];
+    }
+  }
+  for (; i < i1; ++i) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + pp[static_cast<int64_t>(i) * D + v];
   }
   const int64_t orow = a.row_ids ? a.row_ids[row] : row;
   if (QUANT && orow >= a.q.first) {
