@@ -127,7 +127,10 @@ int qha_csr_transpose(int64_t n_rows, int64_t n_cols, const int32_t* rowptr, con
  * with no edges is an item of its own, or, if skip_empty is set, belongs to no item and is left
  * as it is (valid only with beta = 1).
  * qha_agg_plan_size fills the counts; the caller allocates the device arrays, calls
- * qha_agg_plan_fill with host staging buffers of the same sizes, and copies them to the device. */
+ * qha_agg_plan_fill with host staging buffers of the same sizes (items: 4 * n_items int32,
+ * split_row: n_split_rows, split_ptr: n_split_rows + 1), and copies them to the device.
+ * qha_agg_plan_fill returns INVALID_ARG when rowptr does not give the plan's counts, and writes
+ * nothing past those sizes even then. */
 #define QHA_GROUP_ROWS 15
 #define QHA_DEFAULT_GROUP_EDGES 256
 

@@ -128,16 +128,20 @@ int take_classes(const qha_width_classes* cls, int64_t n_rows, int32_t d, qha::C
   return QHA_OK;
 }
 
-// Walks the rows once and either counts (out == nullptr) or writes the plan's arrays.
+// Walks the rows once and either counts (cap == nullptr) or writes the plan's arrays, which hold
+// cap->items items and cap->split_rows split rows: a walk that would write more (a rowptr other than
+// the one the plan was sized for) stops writing and fails.
 struct PlanWalk {
   int64_t items = 0, split_items = 0, split_rows = 0;
 };
 
 int walk_plan(const int32_t* rowptr, int64_t n_rows, int32_t chunk, int32_t group_edges, int32_t skip_empty,
-              PlanWalk* cnt, int32_t* items, int32_t* split_row, int32_t* split_ptr) {
+              PlanWalk* cnt, const PlanWalk* cap, int32_t* items, int32_t* split_row, int32_t* split_ptr) {
   PlanWalk w;
+  bool over = false;
   auto emit = [&](int64_t r0, int64_t nr, int64_t e0, int64_t e1) {
-    if (items) {
+    if (cap && w.items >= cap->items) over = true;
+    if (items && !over) {
       int32_t* it = items + 4 * w.items;
       it[0] = static_cast<int32_t>(r0);
       it[1] = static_cast<int32_t>(nr);
@@ -153,10 +157,12 @@ int walk_plan(const int32_t* rowptr, int64_t n_rows, int32_t chunk, int32_t grou
     if (e < b) return fail(QHA_ERR_INVALID_ARG, "rowptr decreases at row %lld", (long long)r);
     if (e - b > chunk) {
       for (int64_t c = b; c < e; c += chunk) emit(r, 1, c, c + chunk < e ? c + chunk : e);
-      if (split_row) split_row[w.split_rows] = static_cast<int32_t>(r);
+      if (cap && w.split_rows >= cap->split_rows) over = true;
+      if (split_row && !over) split_row[w.split_rows] = static_cast<int32_t>(r);
       ++w.split_rows;
-      if (split_ptr) split_ptr[w.split_rows] = static_cast<int32_t>(w.items);
+      if (split_ptr && !over) split_ptr[w.split_rows] = static_cast<int32_t>(w.items);
     }
+    if (over) return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr (more split rows or items)");
   }
   w.split_items = w.items;
   // groups of consecutive rows
@@ -184,6 +190,7 @@ int walk_plan(const int32_t* rowptr, int64_t n_rows, int32_t chunk, int32_t grou
     ge += len;
   }
   close();
+  if (over) return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr (more work items)");
   if (w.items > kMaxIndex) return fail(QHA_ERR_INVALID_ARG, "too many work items");
   *cnt = w;
   return QHA_OK;
@@ -298,7 +305,7 @@ int qha_agg_plan_size(int64_t n_rows, const int32_t* rowptr, int32_t chunk, int3
   if (!rowptr || !plan) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
   if (chunk <= 0 || group_edges <= 0) return fail(QHA_ERR_INVALID_ARG, "chunk and group_edges must be positive");
   PlanWalk w;
-  int st = walk_plan(rowptr, n_rows, chunk, group_edges, skip_empty, &w, nullptr, nullptr, nullptr);
+  int st = walk_plan(rowptr, n_rows, chunk, group_edges, skip_empty, &w, nullptr, nullptr, nullptr, nullptr);
   if (st) return st;
   std::memset(plan, 0, sizeof(*plan));
   plan->n_rows = n_rows;
@@ -316,9 +323,14 @@ int qha_agg_plan_fill(const int32_t* rowptr, const qha_agg_plan* plan, int32_t* 
   if (!rowptr || !plan) return fail(QHA_ERR_INVALID_ARG, "NULL pointer");
   if ((plan->n_items > 0 && !items) || !split_ptr || (plan->n_split_rows > 0 && !split_row))
     return fail(QHA_ERR_INVALID_ARG, "NULL output array");
-  PlanWalk w;
-  int st = walk_plan(rowptr, plan->n_rows, plan->chunk, plan->group_edges, plan->skip_empty, &w, items, split_row,
-                     split_ptr);
+  if (plan->n_rows < 0 || plan->n_rows > kMaxIndex || plan->chunk <= 0 || plan->group_edges <= 0 ||
+      plan->n_items < 0 || plan->n_split_rows < 0)
+    return fail(QHA_ERR_INVALID_ARG, "malformed plan");
+  PlanWalk w, cap;
+  cap.items = plan->n_items;
+  cap.split_rows = plan->n_split_rows;
+  int st = walk_plan(rowptr, plan->n_rows, plan->chunk, plan->group_edges, plan->skip_empty, &w, &cap, items,
+                     split_row, split_ptr);
   if (st) return st;
   if (w.items != plan->n_items || w.split_items != plan->n_split_items || w.split_rows != plan->n_split_rows)
     return fail(QHA_ERR_INVALID_ARG, "plan does not match rowptr");

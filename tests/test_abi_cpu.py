@@ -128,6 +128,34 @@ def test_agg_plan_covers_every_edge_and_row_once(skip_empty, group_edges):
     assert B._plan_ws(C.byref(st), 128) == st.n_split_items * 128 * 8
 
 
+@pytest.mark.parametrize("longer", ["split rows", "items"])
+def test_agg_plan_fill_with_another_rowptr_fails_inside_its_arrays(longer):
+    """A plan filled from a rowptr other than the one it was sized for is rejected, and nothing is
+    written past the arrays of the sizes the plan gives (guard words after each stay intact)."""
+    lens = np.array([3, 700, 1, 2, 600, 4], np.int32)
+    ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    st = B.AggPlanStruct()
+    B._check(B._plan_size(ptr.size - 1, ptr.ctypes.data, 512, 256, 0, C.byref(st)), "size")
+    more = lens.copy()
+    if longer == "split rows":
+        more[0] = 900                   # a third split row
+    else:
+        more[:] = [3, 2500, 0, 2, 0, 4]  # 10 items against 7, one split row against 2
+    other = np.concatenate([[0], np.cumsum(more)]).astype(np.int32)
+    guard = -7
+    items = np.full(4 * st.n_items + 8, guard, np.int32)
+    split_row = np.full(st.n_split_rows + 8, guard, np.int32)
+    sp = np.full(st.n_split_rows + 1 + 8, guard, np.int32)
+    rc = B._plan_fill(other.ctypes.data, C.byref(st), items.ctypes.data, split_row.ctypes.data, sp.ctypes.data)
+    assert rc == B.QHA_ERR_INVALID_ARG
+    assert (items[4 * st.n_items:] == guard).all()
+    assert (split_row[st.n_split_rows:] == guard).all()
+    assert (sp[st.n_split_rows + 1:] == guard).all()
+    # the rowptr the plan was sized for still fills it
+    assert B._plan_fill(ptr.ctypes.data, C.byref(st), items.ctypes.data, split_row.ctypes.data,
+                        sp.ctypes.data) == B.QHA_OK
+
+
 def test_device_calls_reject_bad_arguments_before_any_hip_call():
     q = B._quantize_pack
     # unsupported width
