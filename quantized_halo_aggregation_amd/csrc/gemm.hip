@@ -398,8 +398,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t mn = p.m * p.n;
   if (idx >= mn) return;
+  // the splits' partials are added one by one in split order; the loads of eight splits are issued
+  // together, so the sum waits for memory once per eight splits instead of once per split
+  const double* src = p.ws + idx;
   double s = 0.0;
-  for (int z = 0; z < p.splits; ++z) s += p.ws[z * mn + idx];
+  int z = 0;
+  for (; z + 8 <= p.splits; z += 8) {
+    double t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[static_cast<int64_t>(z + u) * mn];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += t[u];
+  }
+  for (; z < p.splits; ++z) s += src[static_cast<int64_t>(z) * mn];
   const int64_t i = idx / p.n, j = idx % p.n;
   float* dst = p.c + i * p.ldc + j;
   float v = static_cast<float>(p.beta ? static_cast<double>(*dst) + s : s);
