@@ -1161,8 +1161,9 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
   const int32_t i0 = cst(a.split_ptr)[m];
   const int32_t i1 = cst(a.split_ptr)[m + 1];
   // the partials are added one by one in chunk order; the loads of U chunks (8, or 4 at d = 512)
-  // are issued together, so a row of many chunks waits for memory once per U instead of once per
-  // chunk
+  // are issued together, so a row waits for memory once per U chunks instead of once per chunk.
+  // The last, partial batch reloads the row's last chunk in place of the chunks past it and adds
+  // nothing from them.
   constexpr int U = VEC >= 8 ? 4 : 8;
   const double* pp = a.partial + j0;
   double acc[VEC];
@@ -1182,9 +1183,21 @@ __global__ __launch_bounds__(256) void combine_split_kernel(GatherArgs a) {
       for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + t[u][v];
     }
   }
-  for (; i < i1; ++i) {
+  if (i < i1) {
+    double t[U][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + pp[static_cast<int64_t>(i) * D + v];
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = i + u < i1 ? i + u : i1 - 1;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) t[u][v] = pp[c * D + v];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i + u < i1) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = acc[v] + t[u][v];
+      }
+    }
   }
   const int64_t orow = a.row_ids ? a.row_ids[row] : row;
   if (QUANT && orow >= a.q.first) {
