@@ -350,10 +350,12 @@ size_t qha_dense_project_workspace(int32_t trans_a, int32_t trans_b, int64_t m, 
  * once: 32-row panels stream through on-chip memory, dZ is formed once and used for both
  * products, both products run on the bf16 matrix cores with the three-way split of
  * qha_dense_project's width-128 forward (W's parts held on chip), and per-block dW partials
- * (workspace) are added in a fixed order.  Other widths run as the two qha_dense_project
- * products (dA's W split once into the workspace when it has room, before dW's partials use
- * it).  dA sums are chains of 32 products accumulated in float32 and added in float64; dW
- * adds float32 sums over each block's rows in float64.  workspace: device, 16-byte aligned,
+ * (workspace) are added in a fixed order.  At other widths dA runs as qha_dense_project's product
+ * (W split once into the workspace when it has room); dW runs by row panels when n is a multiple
+ * of 128 and k of 256 (blocks of 128 x 256 outputs, each summing one range of at most about 4096
+ * rows, per-range partials in the workspace), else as qha_dense_project's split product.  The
+ * workspace is reused by dW after dA has read it.  dA sums are chains of 32 products accumulated
+ * in float32 and added in float64; dW adds float32 sums over each block's rows in float64.  workspace: device, 16-byte aligned,
  * qha_dense_backward_workspace bytes (less only where the partials still fit).  Results are
  * deterministic.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */

@@ -680,6 +680,7 @@ int qha_dense_project(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, in
 static size_t dense_bwd_required_bytes(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
   if (qha::panel_fits(n, k)) return qha::panel_bwd_workspace(m);
+  if (qha::dw_panel_fits(m, n, k)) return qha::dw_panel_workspace(m, n, k);
   return gemm_required_bytes(n, k, m);
 }
 
@@ -745,6 +746,25 @@ int qha_dense_backward(int64_t m, int64_t n, int64_t k, const float* dh, int64_t
                    ? static_cast<uint32_t*>(workspace) : nullptr;
     const int st = hip_status(qha::launch_gemm(g, s), "dense_backward");
     if (st) return st;
+  }
+  if (qha::dw_panel_fits(m, n, k)) {
+    // dW by row panels (dA has read W's parts from the workspace by now: same stream)
+    qha::DwArgs d;
+    std::memset(&d, 0, sizeof(d));
+    d.m = m;
+    d.n = static_cast<int32_t>(n);
+    d.k = static_cast<int32_t>(k);
+    d.dh = dh;
+    d.lddh = ldg;
+    d.h = h;
+    d.ldh = ldh;
+    d.a = a;
+    d.lda = lda;
+    d.ws = static_cast<float*>(workspace);
+    d.ranges = qha::dw_panel_ranges(m, n, k);
+    d.groups_z = static_cast<int32_t>(n / 128);
+    d.groups_a = static_cast<int32_t>(k / 256);
+    return hip_status(qha::launch_dw_panel(d, dw, lddw, s), "dense_backward");
   }
   g.bsplit = nullptr;
   g.ta = 1; g.tb = 0; g.m = n; g.n = k; g.k = m;

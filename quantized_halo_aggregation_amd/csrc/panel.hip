@@ -460,6 +460,176 @@ __global__ __launch_bounds__(256) void panel_dw_reduce_kernel(const float* ws, i
   }
 }
 
+// ---- weight gradient of the general widths: dW = dZ^T A, dZ = dH * [H > 0] ----
+// One 512-thread block per (row range, 128 dZ columns, 256 A columns), persistent over the range's
+// 32-row panels (panels rr, rr + R, rr + 2R, ...).  As in the width-128 backward's dW role, each
+// panel is staged as float32 rows in double-buffered LDS (row strides 132 and 260 floats: the
+// column reads of the two lane halves, 8 rows apart, hit distinct banks), one barrier per panel,
+// the next panel loaded into registers during the products; every wavefront forms a 64 x 64 block
+// of four 32 x 32 tiles, reading its operands down the staged columns and splitting them as it
+// reads (six part products, smallest first, the four tiles interleaved).  The tiles accumulate in
+// float32 over the block's range and each block writes its range's partial once; a second kernel
+// adds the R partials of every output in float64 in range order.  The blocks that
+// share a row range take the same block index modulo 8, so they run on one XCD and its L2 serves
+// their common rows.  A block sums at most about DW_RANGE_ROWS rows in float32 (as the width-128
+// backward's blocks sum theirs), so the number of ranges grows with m.
+constexpr int DW_PR = 32;
+constexpr int DW_ZC = 128;
+constexpr int DW_AC = 256;
+constexpr int DW_ZLS = 132;
+constexpr int DW_ALS = 260;
+constexpr int DW_RANGE_ROWS = 4096;
+constexpr int DW_SZ = DW_PR * DW_ZC / 4 / 512;   // float4 of dH (and of H) per thread per panel
+constexpr int DW_SA = DW_PR * DW_AC / 4 / 512;   // float4 of A per thread per panel
+
+__global__ __launch_bounds__(512) void dw_panel_kernel(DwArgs p) {
+  __shared__ __attribute__((aligned(16))) float Zs[2][DW_PR * DW_ZLS];
+  __shared__ __attribute__((aligned(16))) float As[2][DW_PR * DW_ALS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l = lane & 31;
+  const int g = p.groups_z * p.groups_a;
+  const int b = static_cast<int>(blockIdx.x);
+  const int j = (b >> 3) % g;
+  const int64_t rr = 8 * static_cast<int64_t>((b >> 3) / g) + (b & 7);
+  const int zc0 = DW_ZC * (j % p.groups_z);
+  const int ac0 = DW_AC * (j / p.groups_z);
+  const int ob0 = 2 * (wid & 1);      // o-blocks (32 dZ columns each) ob0, ob0 + 1 of 4
+  const int ib0 = 2 * (wid >> 1);     // i-blocks (32 A columns each) ib0, ib0 + 1 of 8
+  const int64_t n_panels = (p.m + DW_PR - 1) / DW_PR;
+  const int64_t stride = p.ranges;
+
+  floatx16 wacc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) zero<16>(wacc[t]);
+
+  // thread tid's share of a panel: dZ float4 f = tid + 512 s at (row f / 32, column 4 (f % 32)),
+  // A float4 f at (row f / 64, column 4 (f % 64)); rows at or past m are read from row m - 1 (no
+  // branches around the loads) and staged as zero
+  float4 gz[DW_SZ], gh[DW_SZ], ga[DW_SA];
+  auto load = [&](int64_t pn) {
+#pragma unroll
+    for (int s = 0; s < DW_SZ; ++s) {
+      const int f = tid + 512 * s;
+      int64_t r = pn * DW_PR + (f >> 5);
+      r = r < p.m ? r : p.m - 1;
+      gz[s] = *reinterpret_cast<const float4*>(p.dh + r * p.lddh + zc0 + 4 * (f & 31));
+      gh[s] = *reinterpret_cast<const float4*>(p.h + r * p.ldh + zc0 + 4 * (f & 31));
+    }
+#pragma unroll
+    for (int s = 0; s < DW_SA; ++s) {
+      const int f = tid + 512 * s;
+      int64_t r = pn * DW_PR + (f >> 6);
+      r = r < p.m ? r : p.m - 1;
+      ga[s] = *reinterpret_cast<const float4*>(p.a + r * p.lda + ac0 + 4 * (f & 63));
+    }
+  };
+  auto stage = [&](int buf, int64_t pn) {
+#pragma unroll
+    for (int s = 0; s < DW_SZ; ++s) {
+      const int f = tid + 512 * s;
+      const bool in = pn * DW_PR + (f >> 5) < p.m;
+      float4 z;
+      z.x = in && gh[s].x > 0.0f ? gz[s].x : 0.0f;
+      z.y = in && gh[s].y > 0.0f ? gz[s].y : 0.0f;
+      z.z = in && gh[s].z > 0.0f ? gz[s].z : 0.0f;
+      z.w = in && gh[s].w > 0.0f ? gz[s].w : 0.0f;
+      *reinterpret_cast<float4*>(&Zs[buf][(f >> 5) * DW_ZLS + 4 * (f & 31)]) = z;
+    }
+#pragma unroll
+    for (int s = 0; s < DW_SA; ++s) {
+      const int f = tid + 512 * s;
+      const bool in = pn * DW_PR + (f >> 6) < p.m;
+      float4 x;
+      x.x = in ? ga[s].x : 0.0f;
+      x.y = in ? ga[s].y : 0.0f;
+      x.z = in ? ga[s].z : 0.0f;
+      x.w = in ? ga[s].w : 0.0f;
+      *reinterpret_cast<float4*>(&As[buf][(f >> 6) * DW_ALS + 4 * (f & 63)]) = x;
+    }
+  };
+
+  int64_t panel = rr;
+  if (panel < n_panels) {
+    load(panel);
+    stage(0, panel);
+    if (panel + stride < n_panels) load(panel + stride);
+  }
+  int buf = 0;
+  for (; panel < n_panels; panel += stride) {
+    __syncthreads();
+    const int64_t nxt = panel + stride;
+    if (nxt < n_panels) {
+      stage(buf ^ 1, nxt);
+      if (nxt + stride < n_panels) load(nxt + stride);
+    }
+    const float* zb = Zs[buf];
+    const float* ab = As[buf];
+#pragma unroll
+    for (int ks = 0; ks < DW_PR / 16; ++ks) {
+      // lane half h takes the panel rows 16 ks + 8 h .. + 7
+      bf16x8 zh[2], zm[2], zl[2], ah[2], am[2], al[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float xz[8], xa[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int row = 16 * ks + 8 * h + q;
+          xz[q] = zb[row * DW_ZLS + 32 * (ob0 + u) + l];
+          xa[q] = ab[row * DW_ALS + 32 * (ib0 + u) + l];
+        }
+        split8(xz, zh[u], zm[u], zl[u]);
+        split8(xa, ah[u], am[u], al[u]);
+      }
+#define QHA_DW_STEP(ZA, AB)                                                         \
+  _Pragma("unroll") for (int ot = 0; ot < 2; ++ot)                                  \
+  _Pragma("unroll") for (int it = 0; it < 2; ++it)                                  \
+      wacc[2 * ot + it] = mfma32b(ZA[ot], AB[it], wacc[2 * ot + it]);
+      QHA_DW_STEP(zm, am)
+      QHA_DW_STEP(zl, ah)
+      QHA_DW_STEP(zh, al)
+      QHA_DW_STEP(zm, ah)
+      QHA_DW_STEP(zh, am)
+      QHA_DW_STEP(zh, ah)
+#undef QHA_DW_STEP
+    }
+    buf ^= 1;
+  }
+  // this range's partial for the block's outputs (zero if the range holds no panel)
+  float* part = p.ws + rr * static_cast<int64_t>(p.n) * p.k;
+#pragma unroll
+  for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t o = zc0 + 32 * (ob0 + ot) + 8 * (r >> 2) + 4 * h + (r & 3);
+        part[o * p.k + ac0 + 32 * (ib0 + it) + l] = wacc[2 * ot + it][r];
+      }
+}
+
+// dW[o][i] = the float64 sum of the R ranges' partials in range order; eight ranges' loads are
+// issued together.  One thread per output.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* ws, int32_t ranges, int64_t nk, int32_t k,
+                                                        float* dw, int64_t lddw) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= nk) return;
+  const float* src = ws + idx;
+  double s = 0.0;
+  int z = 0;
+  for (; z + 8 <= ranges; z += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[static_cast<int64_t>(z + u) * nk];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += static_cast<double>(t[u]);
+  }
+  for (; z < ranges; ++z) s += static_cast<double>(src[static_cast<int64_t>(z) * nk]);
+  dw[(idx / k) * lddw + idx % k] = static_cast<float>(s);
+}
+
 int32_t panel_grid(int64_t m) {
   const int64_t n_panels = (m + PR - 1) / PR;
   return static_cast<int32_t>(n_panels < kPanelBlocks ? n_panels : kPanelBlocks);
@@ -491,6 +661,38 @@ hipError_t launch_panel_bwd(const PanelArgs& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(panel_dw_reduce_kernel, dim3(PD * PD / 64), dim3(256), 0, s, static_cast<const float*>(p.ws),
                      grid, p.dw, p.lddw);
+  return hipGetLastError();
+}
+
+
+bool dw_panel_fits(int64_t m, int64_t n, int64_t k) {
+  return m > 0 && n > 0 && k > 0 && n % DW_ZC == 0 && k % DW_AC == 0;
+}
+
+int32_t dw_panel_ranges(int64_t m, int64_t n, int64_t k) {
+  // enough blocks for every compute unit, and at most about DW_RANGE_ROWS rows per range
+  // (a whole number of rounds of kPanelBlocks blocks when the ranges outnumber one round)
+  const int64_t g = (n / DW_ZC) * (k / DW_AC);
+  int64_t fill = kPanelBlocks / g;
+  fill = fill < 8 ? 8 : fill / 8 * 8;
+  const int64_t len = (m + DW_RANGE_ROWS - 1) / DW_RANGE_ROWS;
+  return static_cast<int32_t>((len + fill - 1) / fill * fill);
+}
+
+size_t dw_panel_workspace(int64_t m, int64_t n, int64_t k) {
+  return static_cast<size_t>(dw_panel_ranges(m, n, k)) * static_cast<size_t>(n) * static_cast<size_t>(k) *
+         sizeof(float);
+}
+
+hipError_t launch_dw_panel(const DwArgs& a, float* dw, int64_t lddw, hipStream_t s) {
+  const int64_t g = static_cast<int64_t>(a.groups_z) * a.groups_a;
+  const int64_t blocks = static_cast<int64_t>(a.ranges) * g;
+  hipLaunchKernelGGL(dw_panel_kernel, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nk = static_cast<int64_t>(a.n) * a.k;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3(static_cast<unsigned>((nk + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const float*>(a.ws), a.ranges, nk, a.k, dw, lddw);
   return hipGetLastError();
 }
 

@@ -145,6 +145,27 @@ struct PanelArgs {
   float* ws;           // backward: per-block dW partials [blocks][128][128]
 };
 bool panel_fits(int64_t n, int64_t k);
+
+// Weight gradient of the general widths: dW [n x k] = dZ^T A over m rows, dZ = dH * [H > 0], for n a
+// multiple of 128 and k a multiple of 256 (row-panel blocks, one float32 partial per row range).
+struct DwArgs {
+  int64_t m;
+  int32_t n, k;
+  const float* dh;
+  int64_t lddh;
+  const float* h;
+  int64_t ldh;
+  const float* a;
+  int64_t lda;
+  float* ws;           // [ranges][n][k] partials
+  int32_t ranges;      // row ranges R (a multiple of 8)
+  int32_t groups_z;    // n / 128
+  int32_t groups_a;    // k / 256
+};
+bool dw_panel_fits(int64_t m, int64_t n, int64_t k);
+int32_t dw_panel_ranges(int64_t m, int64_t n, int64_t k);
+size_t dw_panel_workspace(int64_t m, int64_t n, int64_t k);
+hipError_t launch_dw_panel(const DwArgs& a, float* dw, int64_t lddw, hipStream_t s);
 size_t panel_bwd_workspace(int64_t m);
 hipError_t launch_panel_fwd(const PanelArgs& p, hipStream_t s);
 hipError_t launch_panel_bwd(const PanelArgs& p, hipStream_t s);

@@ -98,11 +98,14 @@ def test_strided_operands_and_empty_reduction():
 
 
 @pytest.mark.parametrize("m,d_in,d_out", [(1, 128, 128), (63, 128, 128), (65, 128, 128), (3001, 128, 128),
-                                          (70001, 128, 128), (1001, 16, 16), (2000, 256, 256), (4099, 512, 256)])
+                                          (70001, 128, 128), (1001, 16, 16), (2000, 256, 256), (4099, 512, 256),
+                                          (5000, 256, 128), (3000, 512, 512), (140001, 512, 256), (5, 256, 256)])
 def test_fused_dense_backward(m, d_in, d_out):
     """qha_dense_backward: dA and dW in one call.  Width 128 runs the fused row-panel kernel (ragged
     panels, several panels per block at m = 70001, strided dH / H rows); other widths the general
-    products.  Bitwise repeatable."""
+    products, with dW by row panels where d_out is a multiple of 128 and d_in of 256 (at m = 140001
+    with more row ranges than blocks fill the chip, at m = 5 with ranges that hold no rows).
+    Bitwise repeatable."""
     H.require_gpu()
     import torch
     from quantized_halo_aggregation_amd import binding as B
@@ -215,7 +218,7 @@ def test_backward_error_is_float32_class(dist):
     assert e_dw.max() <= 16 * 2.0 ** -24, f"dW: max error {e_dw.max() * 2**24:.2f} units of 2^-24"
 
 
-@pytest.mark.parametrize("m,d_in,d_out", [(3001, 256, 256), (2000, 512, 256), (1001, 16, 16)])
+@pytest.mark.parametrize("m,d_in,d_out", [(3001, 256, 256), (2000, 512, 256), (1001, 16, 16), (140001, 512, 256)])
 def test_general_width_error_is_float32_class(m, d_in, d_out):
     """The tiled products at widths other than 128 (split parts on the bf16 matrix cores, 32-k
     chains folded into float64): the forward and dA within 8 units of 2^-24 of the sum of |terms|
