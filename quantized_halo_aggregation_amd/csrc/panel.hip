@@ -1,5 +1,6 @@
-// Row-panel dense products for width 128 layers: the forward projection H = ReLU(A W^T) and the
-// fused backward dZ = dH * [H > 0], dA = dZ W, dW = dZ^T A.
+// Row-panel dense products: for width 128 layers the forward projection H = ReLU(A W^T) and the
+// fused backward dZ = dH * [H > 0], dA = dZ W, dW = dZ^T A; for wider layers the weight gradient
+// dW alone (dw_panel_kernel, below).
 //
 // Method: SYLVIE guide, section 2 (z_v = W a_v, h_v = sigma(z_v)) and section 7 (the weight
 // gradient sums (dL/dh_v * sigma'(z_v)) a_v^T over the rows).
@@ -14,10 +15,12 @@
 // Backward (panel_bwd_x3_kernel): dZ and A are staged per 32-row panel; four wavefronts form dA
 // (W's parts in registers, as in the forward) while four form the block's dW partial, so dH, H
 // and A are each read once and dZ is formed once.
+// Weight gradient at wider layers (dw_panel_kernel): blocks of 128 x 256 outputs over row ranges,
+// the width-128 backward's dW role on its own.
 // Precision: for the forward and dA each MFMA chain adds 32 k-steps in float32 and those partial
 // sums are added in float64.  A block's dW tiles are float32 matrix-core sums over its panels' rows
-// (about m/256 rows); a second kernel adds the blocks' partials in float64 in a fixed order, so
-// results are deterministic.
+// (about m/256 rows at width 128, at most about 4096 rows at wider layers); a second kernel adds
+// the blocks' partials in float64 in a fixed order, so results are deterministic.
 #include "qha_internal.hpp"
 
 namespace qha {
