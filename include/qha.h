@@ -241,7 +241,7 @@ int qha_dequant_aggregate_fwd(int64_t n_rows, const int32_t* rowptr, const int32
  * Errors: those of qha_dequant_aggregate_fwd; WORKSPACE when the plan's partials
  * (qha_agg_workspace_bytes) exceed QHA_NOALLOC_SCRATCH_BYTES, reported before any HIP call; HIP
  * when the scratch's device address cannot be found. */
-#define QHA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define QHA_NOALLOC_SCRATCH_BYTES (128u << 20)
 int qha_dequant_aggregate_fwd_noalloc(int64_t n_rows, const int32_t* rowptr, const int32_t* colidx,
                                       const float* w, const int32_t* row_ids, const qha_agg_plan* plan,
                                       const float* x_inner, int64_t ldx, int64_t n_inner,

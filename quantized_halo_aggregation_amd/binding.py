@@ -406,7 +406,7 @@ def dequant_aggregate_fwd(rowptr, colidx, w, plan, x_inner, n_inner: int, codes,
     _check(_dequant_aggregate_fwd(*args, ws_ptr, ws_bytes, _stream(stream)), "qha_dequant_aggregate_fwd")
 
 
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def dequant_aggregate_fwd_noalloc(rowptr, colidx, w, plan, x_inner, n_inner: int, codes, word_offset, bits, classes,

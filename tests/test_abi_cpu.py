@@ -250,7 +250,7 @@ def test_noalloc_aggregation_rejects_before_any_hip_call():
     """The allocation-free aggregation refuses a plan whose split-row partials exceed its scratch, and
     bad arguments, before it looks anything up on the device."""
     f = B._dequant_aggregate_fwd_noalloc
-    lens = np.full(100, 4000, np.int32)                    # 100 rows split into 250 chunks of 16 each
+    lens = np.full(100, 8000, np.int32)                    # 100 rows split into 500 chunks of 16 each
     ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     st, *_ = _plan_host(ptr, 16, False)
     st.items = st.split_row = st.split_ptr = FAKE
