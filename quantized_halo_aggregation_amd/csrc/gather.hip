@@ -1099,12 +1099,21 @@ __global__ __launch_bounds__(256) void gather_grouped_kernel(GatherArgs a) {
           const uint32_t lgb = pk[i] >> 16;
           const uint32_t bit0 = (static_cast<uint32_t>(j0) << lgb) & 31u;
           float qv[VEC];
+          if constexpr (CW == 1) {
+            // a lane's VEC * b <= 32 bits of codes start at a multiple of VEC * b in one word:
+            // shifted down once, code v is the field at bit v * b (a scalar offset)
+            const uint32_t w0 = cwd[i][0] >> bit0;
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            const uint32_t vb_ = static_cast<uint32_t>(v) * b;
-            const uint32_t word = (CW == 2 && vb_ >= 32u) ? cwd[i][CW - 1] : cwd[i][0];
-            const uint32_t code = __builtin_amdgcn_ubfe(word, (bit0 + vb_) & 31u, b);
-            qv[v] = dequant(sc, code, mn);
+            for (int v = 0; v < VEC; ++v)
+              qv[v] = dequant(sc, __builtin_amdgcn_ubfe(w0, static_cast<uint32_t>(v) * b, b), mn);
+          } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const uint32_t vb_ = static_cast<uint32_t>(v) * b;
+              const uint32_t word = vb_ >= 32u ? cwd[i][CW - 1] : cwd[i][0];
+              const uint32_t code = __builtin_amdgcn_ubfe(word, (bit0 + vb_) & 31u, b);
+              qv[v] = dequant(sc, code, mn);
+            }
           }
 #pragma unroll
           for (int v = 0; v < VEC; ++v) acc[v] = fma(wt, static_cast<double>(qv[v]), acc[v]);
