@@ -60,6 +60,9 @@ constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
 #ifndef QHA_HALO_BATCH
 #define QHA_HALO_BATCH 8    // edges per batch when halo rows are dequantised too
 #endif
+#ifndef QHA_HALO_BATCH_128
+#define QHA_HALO_BATCH_128 16   // the grouped gather's at d = 128, whose one load form keeps 16 edges in 70 VGPRs
+#endif
 #ifndef QHA_SINGLE_BASE
 #define QHA_SINGLE_BASE 1
 #endif
@@ -74,6 +77,8 @@ constexpr int vec_of(int D) { return D >= 64 ? D / 64 : 1; }
 #endif
 constexpr int rows_batch_of(int D) { return D >= 512 ? QHA_ROWS_BATCH / 4 : (D >= 256 ? QHA_ROWS_BATCH / 2 : QHA_ROWS_BATCH); }
 constexpr int batch_of(int D, bool halo) { return D >= 512 ? 8 : (halo ? QHA_HALO_BATCH : QHA_BATCH); }
+// the width-grouped halo gather's batch
+constexpr int grouped_batch_of(int D) { return D == 128 ? QHA_HALO_BATCH_128 : batch_of(D, true); }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 
 __device__ __forceinline__ int rdlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -913,7 +918,7 @@ template <int D, bool BETA, bool SB>
 __global__ __launch_bounds__(256) void gather_grouped_kernel(GatherArgs a) {
   constexpr int VEC = vec_of(D);
   constexpr int G = D / VEC;
-  constexpr int B = batch_of(D, true);
+  constexpr int B = grouped_batch_of(D);
   constexpr int CW = (VEC * 8 > 32) ? 2 : 1;
   constexpr int LGD = log2i(D);
   constexpr uint32_t LGV = static_cast<uint32_t>(log2i(VEC));
