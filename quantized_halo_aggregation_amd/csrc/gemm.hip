@@ -16,8 +16,10 @@
 // read four k at a time with coalesced 4-byte loads, which transposes them on the way in (range-
 // checked buffer loads at 32-bit offsets when they span under 2 GiB, else 64-bit addresses).
 // When A has many rows and the caller's workspace has room, B (the weights) is split once per call
-// by split_b_kernel into three k-contiguous bf16 planes, and its tiles are then copied into LDS
-// with 16-byte loads instead of being split again by every block (the same parts, so the same bits).
+// by split_b_kernel, in the order of the MFMA fragments, and gemm_bsplit_kernel runs the products:
+// 64 x 128 block tiles whose wavefronts own 64 rows x 32 columns each and read their B fragments
+// straight from the split parts (L2-resident, 1 KB per wavefront load), so LDS carries only A
+// (the same parts and the same part products per accumulator, so the same bits).
 // The next tile's global loads are issued before the current tile is consumed.  Each 32-wide k
 // step accumulates into fresh fp32 MFMA accumulators that are then added into float64 running
 // sums, so a long dot product is rounded in float32 only over 32 terms at a time (for K = 512 this
@@ -203,9 +205,10 @@ __device__ __forceinline__ void store_tiles(__bf16* As, __bf16* Bs, int tid, con
   }
 }
 
-// B's parts split once per call: plane q holds part q (hi, mid, lo) of B's column j at
-// [q][j][kk] as bf16, rows padded to the column tile and k to BK with zeros, so the tiles need no
-// range checks.  The split is split_pair's, so the staged parts equal those of the per-tile split.
+// B's parts split once per call (hi, mid, lo of every value, by split_pair, so the same parts as the
+// per-tile split), written in the order in which gemm_bsplit_kernel's wavefronts read them as MFMA
+// fragments; columns padded to the 128-wide tile and k to BK with zeros, so no load needs a range
+// check.
 __global__ __launch_bounds__(256) void split_b_kernel(const float* b, int64_t ldb, int32_t tb, int64_t n, int64_t k,
                                                       uint32_t* planes, int64_t n_pad, int64_t k_pad) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // a pair (j, 2 kq .. + 1)
@@ -220,68 +223,18 @@ __global__ __launch_bounds__(256) void split_b_kernel(const float* b, int64_t ld
   }
   uint32_t h, m, l;
   split_pair(v[0], v[1], h, m, l);
-  planes[i] = h;
-  planes[pairs + i] = m;
-  planes[2 * pairs + i] = l;
+  // fragment order: for each 32-column tile and 16-k step, the three planes' fragments in lane
+  // order (lane (hf, c) holds column 32 t + c, k = 16 s + 8 hf .. + 7, as 16 bytes), so that a
+  // wavefront reads one fragment of one plane as 1 KB of consecutive memory
+  const int64_t nks = k_pad / 16;
+  const int64_t chunk = (((j / 32) * nks + kk / 16) * 3) * 64 + ((kk / 8) % 2) * 32 + j % 32;
+  const int64_t w = (kk % 8) / 2;
+  planes[(chunk + 0 * 64) * 4 + w] = h;
+  planes[(chunk + 1 * 64) * 4 + w] = m;
+  planes[(chunk + 2 * 64) * 4 + w] = l;
 }
 
-// 16-byte chunks of B's split parts per thread and k step: 3 planes x BN columns x BK bf16
-template <int BN>
-constexpr int kBChunks = 3 * BN * BK / 8 / Tile<BN>::NT;
-
-template <int BN>
-__device__ __forceinline__ void load_bsplit(const GemmArgs& p, int tid, int64_t n0, int64_t k0, u32x4 (&rq)[kBChunks<BN>]) {
-  const int64_t kc = (p.k + BK - 1) / BK * (BK / 8);              // 16-byte chunks per padded column
-  const int64_t plane = (p.n + BN - 1) / BN * BN * kc;
-  const u32x4* src = reinterpret_cast<const u32x4*>(p.bsplit);
-#pragma unroll
-  for (int s = 0; s < kBChunks<BN>; ++s) {
-    const int c = tid + Tile<BN>::NT * s;
-    const int q = c / (BN * BK / 8), r = c % (BN * BK / 8);
-    rq[s] = src[q * plane + (n0 + r / (BK / 8)) * kc + k0 / 8 + r % (BK / 8)];
-  }
-}
-
-template <int BN>
-__device__ __forceinline__ void store_bsplit(__bf16* Bs, int tid, const u32x4 (&rq)[kBChunks<BN>]) {
-#pragma unroll
-  for (int s = 0; s < kBChunks<BN>; ++s) {
-    const int c = tid + Tile<BN>::NT * s;
-    const int q = c / (BN * BK / 8), r = c % (BN * BK / 8);
-    *reinterpret_cast<u32x4*>(Bs + q * BN * KS + (r / (BK / 8)) * KS + 8 * (r % (BK / 8))) = rq[s];
-  }
-}
-
-// One k step's global loads and its staging: with PB, B's tiles are copied from its parts split
-// once per call (p.bsplit) instead of being split here.
-template <int BN, bool TA, bool TB, bool MASK, bool PB, int NB, int NQ>
-__device__ __forceinline__ void load_step(const GemmArgs& p, int tid, int64_t m0, int64_t n0, int64_t k0, int64_t kend,
-                                          float4 (&ra)[Tile<BN>::A_LOADS], float4 (&rb)[NB], u32x4 (&rq)[NQ]) {
-  if constexpr (PB) {
-    load_k4<TA, BM, Tile<BN>::A_LOADS, Tile<BN>::NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0, kend, tid, ra);
-    load_bsplit<BN>(p, tid, n0, k0, rq);
-  } else {
-    load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, k0, kend, ra, rb);
-  }
-}
-
-template <int BN, bool TA, bool TB, bool PB, int NB, int NQ>
-__device__ __forceinline__ void stage_step(__bf16* As, __bf16* Bs, int tid, const float4 (&ra)[Tile<BN>::A_LOADS],
-                                           const float4 (&rb)[NB], const u32x4 (&rq)[NQ]) {
-  if constexpr (PB) {
-#pragma unroll
-    for (int s = 0; s < Tile<BN>::A_LOADS; ++s) {
-      const int f = tid + Tile<BN>::NT * s;
-      if (!TA) stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), ra[s]);
-      else stage_k4<BM>(As, f % BM, 4 * (f / BM), ra[s]);
-    }
-    store_bsplit<BN>(Bs, tid, rq);
-  } else {
-    store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
-  }
-}
-
-template <int BN, bool TA, bool TB, bool MASK, bool SPLIT, bool PB>
+template <int BN, bool TA, bool TB, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) __bf16 As[3 * BM * KS];
   __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * BN * KS];
@@ -330,17 +283,16 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum[j][r] = 0.0;
 
-  float4 ra[Tile<BN>::A_LOADS], rb[PB ? 1 : Tile<BN>::B_LOADS];
-  u32x4 rq[PB ? kBChunks<BN> : 1];
+  float4 ra[Tile<BN>::A_LOADS], rb[Tile<BN>::B_LOADS];
 
   if (kbeg < kend) {
-    load_step<BN, TA, TB, MASK, PB>(p, tid, m0, n0, kbeg, kend, ra, rb, rq);
-    stage_step<BN, TA, TB, PB>(As, Bs, tid, ra, rb, rq);
+    load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, kbeg, kend, ra, rb);
+    store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
     __syncthreads();
   }
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
-    if (more) load_step<BN, TA, TB, MASK, PB>(p, tid, m0, n0, k0 + BK, kend, ra, rb, rq);
+    if (more) load_tiles<BN, TA, TB, MASK>(p, tid, m0, n0, k0 + BK, kend, ra, rb);
     floatx16 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -368,7 +320,7 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) sum[ni][r] += static_cast<double>(acc[ni][r]);
     __syncthreads();
     if (more) {
-      stage_step<BN, TA, TB, PB>(As, Bs, tid, ra, rb, rq);
+      store_tiles<BN, TA, TB>(As, Bs, tid, ra, rb);
       __syncthreads();
     }
   }
@@ -390,6 +342,133 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
           if (p.epi == 1) v = v > 0.0f ? v : 0.0f;
           *dst = v;
         }
+      }
+    }
+}
+
+// The products with B split once per call (A not transposed, k not split): the same part products
+// as gemm_kernel in the same order per accumulator (so the same bits), with a different division of
+// the block tile: each wavefront owns all BM = 64 rows and 32 columns, and reads its B fragments --
+// 16 bytes of one plane for one column and 8 consecutive k, a contiguous piece of the split planes --
+// straight from global memory (the planes stay in L2), one k step ahead, instead of through LDS.
+// Only A's tile is staged, so LDS carries A's fragments (read by every wavefront) and no B tile:
+// about half the LDS bytes per MFMA of the 32 x 64 wavefront tiles, which were bound by them.
+template <int BN, bool TA, bool MASK>
+__global__ __launch_bounds__(Tile<BN>::NT) void gemm_bsplit_kernel(GemmArgs p) {
+  static_assert(!TA, "B split once is used with A not transposed");
+  __shared__ __attribute__((aligned(16))) __bf16 As[3 * BM * KS];
+  constexpr int NT = Tile<BN>::NT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);   // 32-column slice of the block tile
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  int64_t mbk = blockIdx.x, nbk = blockIdx.y;
+  if constexpr (QHA_GEMM_ORDER > 0) {
+    // the unsplit kernels' order: the column tiles of a row tile are consecutive blocks (of one XCD)
+    const int64_t nb = (p.n + BN - 1) / BN, b = blockIdx.x;
+    if constexpr (QHA_GEMM_ORDER == 1) {
+      nbk = b % nb;
+      mbk = b / nb;
+    } else {
+      const int64_t sl = b / kXcds;
+      nbk = sl % nb;
+      mbk = sl / nb * kXcds + b % kXcds;
+      if (mbk * BM >= p.m) return;
+    }
+  }
+  const int64_t m0 = mbk * BM;
+  const int64_t n0 = nbk * BN;
+  const int64_t kend = p.k;
+
+  double sum[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum[j][r] = 0.0;
+
+  // B's split parts in fragment order (split_b_kernel), padded with zeros to whole column tiles
+  // and k steps: this wavefront's fragment of plane q at 16-k step s is 64 consecutive u32x4
+  const int64_t nks = (p.k + BK - 1) / BK * (BK / 16);
+  const u32x4* bsrc = reinterpret_cast<const u32x4*>(p.bsplit) + ((n0 / 32 + wn) * nks) * 3 * 64 + lane;
+  auto load_b = [&](int64_t k0, u32x4 (&dst)[2][3]) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) dst[ks][q] = bsrc[((k0 / 16 + ks) * 3 + q) * 64];
+  };
+  auto stage_a = [&](const float4 (&ra)[Tile<BN>::A_LOADS]) {
+#pragma unroll
+    for (int s = 0; s < Tile<BN>::A_LOADS; ++s) {
+      const int f = tid + NT * s;
+      stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), ra[s]);
+    }
+  };
+
+  float4 ra[Tile<BN>::A_LOADS];
+  u32x4 bq[2][3], bn[2][3];
+  if (kend > 0) {
+    load_k4<false, BM, Tile<BN>::A_LOADS, NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, 0, kend, tid, ra);
+    load_b(0, bq);
+    stage_a(ra);
+    __syncthreads();
+  }
+  // one k step: the next step's A rows and B fragments are loaded (into nxt) while this step's
+  // products run from cur; two steps per loop trip, so the fragment sets alternate without copies
+  auto kstep = [&](int64_t k0, const u32x4 (&cur)[2][3], u32x4 (&nxt)[2][3]) {
+    const bool more = k0 + BK < kend;
+    if (more) {
+      load_k4<false, BM, Tile<BN>::A_LOADS, NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0 + BK, kend, tid, ra);
+      load_b(k0 + BK, nxt);
+    }
+    floatx16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const bf16x8 yh = __builtin_bit_cast(bf16x8, cur[ks][0]);
+      const bf16x8 ym = __builtin_bit_cast(bf16x8, cur[ks][1]);
+      const bf16x8 yl = __builtin_bit_cast(bf16x8, cur[ks][2]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        // lane (h, l32) takes k = 16 ks + 8 h .. + 7 of row 32 mi + l32
+        const __bf16* ap = As + (32 * mi + l32) * KS + 16 * ks + 8 * h;
+        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(ap);
+        const bf16x8 xm = *reinterpret_cast<const bf16x8*>(ap + BM * KS);
+        const bf16x8 xl = *reinterpret_cast<const bf16x8*>(ap + 2 * BM * KS);
+        acc[mi] = mfma6(xh, xm, xl, yh, ym, yl, acc[mi]);
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum[mi][r] += static_cast<double>(acc[mi][r]);
+    __syncthreads();
+    if (more) {
+      stage_a(ra);
+      __syncthreads();
+    }
+  };
+  for (int64_t k0 = 0; k0 < kend; k0 += 2 * BK) {
+    kstep(k0, bq, bn);
+    if (k0 + BK < kend) kstep(k0 + BK, bn, bq);
+  }
+
+  // accumulator element r of lane (h, l32) is C[8*(r/4) + 4*h + r%4][l32] of the 32x32 block
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t grow = m0 + 32 * mi + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t gcol = n0 + 32 * wn + l32;
+      if (grow < p.m && gcol < p.n) {
+        const double s = sum[mi][r];
+        float* dst = p.c + grow * p.ldc + gcol;
+        float v = static_cast<float>(p.beta ? static_cast<double>(*dst) + s : s);
+        if (p.epi == 1) v = v > 0.0f ? v : 0.0f;
+        *dst = v;
       }
     }
 }
@@ -436,14 +515,14 @@ hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
                          p.ldb, p.tb, p.n, p.k, p.bsplit, n_pad, k_pad);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, true>), gridu, dim3(Tile<BN>::NT), 0, s, p);
+      hipLaunchKernelGGL((gemm_bsplit_kernel<BN, TA, MASK>), gridu, dim3(Tile<BN>::NT), 0, s, p);
       return hipGetLastError();
     }
   }
   if (p.splits > 1)
-    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true, false>), grids, dim3(Tile<BN>::NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, true>), grids, dim3(Tile<BN>::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false, false>), gridu, dim3(Tile<BN>::NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<BN, TA, TB, MASK, false>), gridu, dim3(Tile<BN>::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;
   const int64_t mn = p.m * p.n;
@@ -453,6 +532,9 @@ hipError_t launch_tiled(const GemmArgs& p, hipStream_t s) {
 
 template <bool TA, bool TB, bool MASK>
 hipError_t launch_variant(const GemmArgs& p, hipStream_t s) {
+  // with B split once every width takes 128-wide tiles: the products whose wavefronts read B's
+  // fragments from memory ran faster with four wavefronts per block than with eight sharing A's tile
+  if (!TA && p.bsplit != nullptr && p.splits == 1) return launch_tiled<128, TA, TB, MASK>(p, s);
   return tile_n(p.n) == 256 ? launch_tiled<256, TA, TB, MASK>(p, s) : launch_tiled<128, TA, TB, MASK>(p, s);
 }
 
@@ -482,7 +564,7 @@ size_t gemm_bsplit_bytes(int32_t ta, int64_t m, int64_t n, int64_t k) {
   int64_t kps;
   gemm_split_rule(m, n, k, &splits, &kps);
   if (ta || splits != 1 || m < kBSplitMinRows || n <= 0 || k <= 0) return 0;
-  const int64_t bn = tile_n(n);
+  const int64_t bn = 128;   // the tile width of the products that read B split once
   return static_cast<size_t>(3 * ((n + bn - 1) / bn * bn) * ((k + BK - 1) / BK * BK) * 2);
 }
 
