@@ -36,9 +36,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libqha")
 
 
+# per-source code generation options: the tiled products keep their MFMA accumulators in ordinary
+# VGPRs (gfx950 has one register file), so the float64 folds read them without accumulator moves
+SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool, defines=(), build_dir: str = BUILD_DIR) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -356,7 +356,7 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_kernel(GemmArgs p) {
 template <int BN, bool TA, bool MASK>
 __global__ __launch_bounds__(Tile<BN>::NT) void gemm_bsplit_kernel(GemmArgs p) {
   static_assert(!TA, "B split once is used with A not transposed");
-  __shared__ __attribute__((aligned(16))) __bf16 As[3 * BM * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 Asb[2][3 * BM * KS];   // double-buffered A tile
   constexpr int NT = Tile<BN>::NT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -397,28 +397,61 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_bsplit_kernel(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 3; ++q) dst[ks][q] = bsrc[((k0 / 16 + ks) * 3 + q) * 64];
   };
-  auto stage_a = [&](const float4 (&ra)[Tile<BN>::A_LOADS]) {
+  // A's rows for the k step at k0: raw float4s (and the ReLU mask's beside them), with nothing
+  // computed from them here, so that the loads stay in flight through the current step's products;
+  // the range check and the mask are applied as the tile is staged
+  constexpr int AL = Tile<BN>::A_LOADS;
+  auto a_ok = [&](int s, int64_t k0, int64_t& off, int64_t& offm) {
+    const int f = tid + NT * s;
+    const int64_t gr = m0 + f / (BK / 4), gk = k0 + 4 * (f % (BK / 4));
+    const bool ok = gr < p.m && gk < kend;
+    off = ok ? gr * p.lda + gk : 0;
+    offm = ok ? gr * p.ld_aux + gk : 0;
+    return ok;
+  };
+  auto load_a = [&](int64_t k0, float4 (&ra)[AL], float4 (&rm)[MASK ? AL : 1]) {
 #pragma unroll
-    for (int s = 0; s < Tile<BN>::A_LOADS; ++s) {
+    for (int s = 0; s < AL; ++s) {
+      int64_t off, offm;
+      a_ok(s, k0, off, offm);
+      ra[s] = *reinterpret_cast<const float4*>(p.a + off);
+      if constexpr (MASK) rm[s] = *reinterpret_cast<const float4*>(p.aux + offm);
+    }
+  };
+  auto stage_a = [&](__bf16* As, int64_t k0, const float4 (&ra)[AL], const float4 (&rm)[MASK ? AL : 1]) {
+#pragma unroll
+    for (int s = 0; s < AL; ++s) {
+      int64_t off, offm;
+      const bool ok = a_ok(s, k0, off, offm);
+      float4 v = ra[s];
+      if constexpr (MASK) {
+        v.x = rm[s].x > 0.0f ? v.x : 0.0f;
+        v.y = rm[s].y > 0.0f ? v.y : 0.0f;
+        v.z = rm[s].z > 0.0f ? v.z : 0.0f;
+        v.w = rm[s].w > 0.0f ? v.w : 0.0f;
+      }
+      v = ok ? v : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       const int f = tid + NT * s;
-      stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), ra[s]);
+      stage_k4<BM>(As, f / (BK / 4), 4 * (f % (BK / 4)), v);
     }
   };
 
-  float4 ra[Tile<BN>::A_LOADS];
+  float4 ra[AL], rm[MASK ? AL : 1];
   u32x4 bq[2][3], bn[2][3];
   if (kend > 0) {
-    load_k4<false, BM, Tile<BN>::A_LOADS, NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, 0, kend, tid, ra);
+    load_a(0, ra, rm);
     load_b(0, bq);
-    stage_a(ra);
+    stage_a(Asb[0], 0, ra, rm);
     __syncthreads();
   }
   // one k step: the next step's A rows and B fragments are loaded (into nxt) while this step's
-  // products run from cur; two steps per loop trip, so the fragment sets alternate without copies
-  auto kstep = [&](int64_t k0, const u32x4 (&cur)[2][3], u32x4 (&nxt)[2][3]) {
+  // products run from cur and A's tile in As; two steps per loop trip, so the fragment sets
+  // alternate without copies.  The next A tile is staged into the other buffer An after this
+  // step's products, so one barrier per step orders both the reads and the writes.
+  auto kstep = [&](int64_t k0, const __bf16* As, __bf16* An, const u32x4 (&cur)[2][3], u32x4 (&nxt)[2][3]) {
     const bool more = k0 + BK < kend;
     if (more) {
-      load_k4<false, BM, Tile<BN>::A_LOADS, NT>(p.a, p.lda, p.aux, p.ld_aux, MASK, m0, p.m, k0 + BK, kend, tid, ra);
+      load_a(k0 + BK, ra, rm);
       load_b(k0 + BK, nxt);
     }
     floatx16 acc[2];
@@ -445,15 +478,14 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_bsplit_kernel(GemmArgs p) {
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sum[mi][r] += static_cast<double>(acc[mi][r]);
-    __syncthreads();
     if (more) {
-      stage_a(ra);
+      stage_a(An, k0 + BK, ra, rm);
       __syncthreads();
     }
   };
   for (int64_t k0 = 0; k0 < kend; k0 += 2 * BK) {
-    kstep(k0, bq, bn);
-    if (k0 + BK < kend) kstep(k0 + BK, bn, bq);
+    kstep(k0, Asb[0], Asb[1], bq, bn);
+    if (k0 + BK < kend) kstep(k0 + BK, Asb[1], Asb[0], bn, bq);
   }
 
   // accumulator element r of lane (h, l32) is C[8*(r/4) + 4*h + r%4][l32] of the 32x32 block
