@@ -450,10 +450,10 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_bsplit_kernel(GemmArgs p) {
   // step's products, so one barrier per step orders both the reads and the writes.
   auto kstep = [&](int64_t k0, const __bf16* As, __bf16* An, const u32x4 (&cur)[2][3], u32x4 (&nxt)[2][3]) {
     const bool more = k0 + BK < kend;
-    if (more) {
-      load_a(k0 + BK, ra, rm);
-      load_b(k0 + BK, nxt);
-    }
+    // the loads are issued whether or not a next step exists (past the last step A's rows read the
+    // operand's first element and B's fragments this step's again, all unused): with no branch
+    // around them the compiler waits for exactly the loads each use needs, and keeps them here
+    load_a(k0 + BK, ra, rm);
     floatx16 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -474,14 +474,18 @@ __global__ __launch_bounds__(Tile<BN>::NT) void gemm_bsplit_kernel(GemmArgs p) {
         acc[mi] = mfma6(xh, xm, xl, yh, ym, yl, acc[mi]);
       }
     }
+    // the next step's B fragments are requested once this step's products have taken theirs (they
+    // come from L2); requested before them, they would sit behind this step's A rows in the load
+    // queue, and the compiler's wait for the fragments in use would also wait for those rows
+    load_b(more ? k0 + BK : k0, nxt);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sum[mi][r] += static_cast<double>(acc[mi][r]);
-    if (more) {
-      stage_a(An, k0 + BK, ra, rm);
-      __syncthreads();
-    }
+    // staged whether or not a next step exists (past the last step the buffer is not read again):
+    // a branch here would let the compiler sink the loads above into it, next to their use
+    stage_a(An, k0 + BK, ra, rm);
+    __syncthreads();
   };
   for (int64_t k0 = 0; k0 < kend; k0 += 2 * BK) {
     kstep(k0, Asb[0], Asb[1], bq, bn);
